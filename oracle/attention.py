@@ -1,0 +1,247 @@
+"""Plain float64 softmax attention: the definition written out, S and P materialised.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  numpy only; no blocking,
+fusion or reordering beyond what each docstring states.
+
+Notation (all pages): Q [B, Hq, N, d], K and V [B, Hkv, N, d], scale a positive
+number, S = scale * Q K^T, P = softmax(S) over keys, O = P V.  With grouped
+heads, query head h reads key/value head h // (Hq // Hkv) ([FA-LLM], entry
+"Grouped-Query Attention": query heads are divided into groups that share one
+key/value head; groups are contiguous runs of query heads).  Causal: key j is
+visible to query i iff j <= i ([Digest], "Limits", which lists causal masks;
+queries and keys have the same length, so there is no alignment choice).
+
+The log-sum-exp statistic is LSE_i = m_i + ln(l_i) in natural-log units of
+the scaled scores ([FA-legal], paragraph on the backward pass: only the
+softmax normalisation statistics (m, l) are kept; [FA-LLM], third paragraph:
+the log-sum-exp trick).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ROW_BLOCK = 256   # rows materialised at once; each block still holds full rows of S and P
+
+
+def _visible(rows: np.ndarray, n_keys: int, causal: bool) -> np.ndarray | None:
+    """Boolean mask [len(rows), n_keys] of visible keys, or None when all are."""
+    if not causal:
+        return None
+    return np.arange(n_keys)[None, :] <= rows[:, None]
+
+
+def probabilities(qh, kg, scale, causal, rows=None):
+    """Rows of S and P = softmax(S), plus the row max m and row sum l.
+
+    [IO-aware], "The Memory Bandwidth Bottleneck", steps 1-2: S = Q K^T, then
+    P = softmax(S).  The softmax is the two-pass form that [FA-legal] (online
+    softmax paragraph) contrasts with the online one: first the row maximum,
+    then exponentials of S - m and their sum.  Masked scores are -inf and
+    contribute exp(-inf) = 0.
+    """
+    qh = np.asarray(qh, dtype=np.float64)
+    kg = np.asarray(kg, dtype=np.float64)
+    n = kg.shape[0]
+    rows = np.arange(qh.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    S = scale * (qh[rows] @ kg.T)
+    vis = _visible(rows, n, causal)
+    if vis is not None:
+        S = np.where(vis, S, -np.inf)
+    m = S.max(axis=1)
+    E = np.exp(S - m[:, None])
+    l = E.sum(axis=1)
+    P = E / l[:, None]
+    return S, P, m, l
+
+
+def head_rows_forward(qh, kg, vg, rows, causal, scale):
+    """O and LSE for the given query rows of one head, in row blocks.
+
+    [IO-aware], "The Memory Bandwidth Bottleneck", step 3: O = P V.
+    LSE_i = m_i + ln l_i.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    vg = np.asarray(vg, dtype=np.float64)
+    O = np.empty((rows.size, vg.shape[1]))
+    L = np.empty(rows.size)
+    for s in range(0, rows.size, ROW_BLOCK):
+        r = rows[s:s + ROW_BLOCK]
+        _, P, m, l = probabilities(qh, kg, scale, causal, r)
+        O[s:s + r.size] = P @ vg
+        L[s:s + r.size] = m + np.log(l)
+    return O, L
+
+
+def forward(q, k, v, causal, scale):
+    """Full forward over [B, Hq, N, d]: returns O [B, Hq, N, d] and LSE [B, Hq, N]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, N, d = q.shape
+    G = Hq // k.shape[1]
+    O = np.empty((B, Hq, N, v.shape[3]))
+    L = np.empty((B, Hq, N))
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            O[b, h], L[b, h] = head_rows_forward(q[b, h], k[b, g], v[b, g], rows, causal, scale)
+    return O, L
+
+
+def forward_online(q, k, v, causal, scale, block_sizes):
+    """Forward by the tiled online softmax, key blocks taken in order.
+
+    [IO-aware], "Flash Attention Algorithm" and "Online Softmax"; [FA-legal],
+    online softmax paragraph and glossary entry "Online softmax": keep a
+    running maximum m and running sum l per query row; for each key block,
+    take the new maximum m' = max(m, rowmax(S_blk)), rescale what was
+    accumulated so far by exp(m - m'), add the block's exp(S_blk - m') to the
+    sum and exp(S_blk - m') V_blk to the output accumulator; at the end divide
+    the accumulator by l.  Rows with no visible key yet have m = -inf and no
+    accumulated mass (their rescale factor is taken as 0 and their exponent
+    base as 0 so that -inf - -inf never occurs).
+
+    ``block_sizes`` lists the key-block lengths; they must sum to N.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, N, d = q.shape
+    assert sum(block_sizes) == N
+    G = Hq // k.shape[1]
+    O = np.empty((B, Hq, N, v.shape[3]))
+    L = np.empty((B, Hq, N))
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            m = np.full(N, -np.inf)
+            l = np.zeros(N)
+            acc = np.zeros((N, v.shape[3]))
+            j0 = 0
+            for bs in block_sizes:
+                cols = np.arange(j0, j0 + bs)
+                S = scale * (q[b, h] @ k[b, g, j0:j0 + bs].T)
+                if causal:
+                    S = np.where(cols[None, :] <= rows[:, None], S, -np.inf)
+                m_new = np.maximum(m, S.max(axis=1))
+                base = np.where(np.isneginf(m_new), 0.0, m_new)
+                alpha = np.where(np.isneginf(m), 0.0, np.exp(m - base))
+                Pt = np.exp(S - base[:, None])
+                l = alpha * l + Pt.sum(axis=1)
+                acc = alpha[:, None] * acc + Pt @ v[b, g, j0:j0 + bs]
+                m = m_new
+                j0 += bs
+            O[b, h] = acc / l[:, None]
+            L[b, h] = m + np.log(l)
+    return O, L
+
+
+def backward(q, k, v, do, causal, scale):
+    """Gradients of O = softmax(scale Q K^T [+mask]) V for a loss with dL/dO = dO.
+
+    The pages do not print the backward; [FA-legal] (backward paragraph and
+    entry "Recomputation") and [Digest] ("Method", item 4) say only that P is
+    recomputed from Q, K and the stored statistics.  This is the chain rule of
+    the forward definition, P materialised:
+      dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic (= sum_j P_ij dP_ij),
+      dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q,
+    and, with grouped heads, dK and dV of a key/value head are the sums over
+    the query heads of its group.  Returns dq, dk, dv and D [B, Hq, N].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, N, d = q.shape
+    G = Hq // k.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    Dall = np.empty((B, Hq, N))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            _, P, _, _ = probabilities(q[b, h], k[b, g], scale, causal)
+            O = P @ v[b, g]
+            dv[b, g] += P.T @ do[b, h]
+            dP = do[b, h] @ v[b, g].T
+            D = (do[b, h] * O).sum(axis=1)
+            dS = P * (dP - D[:, None])
+            dq[b, h] = scale * (dS @ k[b, g])
+            dk[b, g] += scale * (dS.T @ q[b, h])
+            Dall[b, h] = D
+    return dq, dk, dv, Dall
+
+
+def head_rows_backward_dq(qh, kg, vg, doh, rows, causal, scale):
+    """dQ rows of one head (and their O, LSE, D), from full rows of P.
+
+    Same chain rule as ``backward`` restricted to the given query rows: D of
+    those rows uses this oracle's own O of those rows.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    kg = np.asarray(kg, dtype=np.float64)
+    vg = np.asarray(vg, dtype=np.float64)
+    doh = np.asarray(doh, dtype=np.float64)
+    dQ = np.empty((rows.size, kg.shape[1]))
+    O = np.empty((rows.size, vg.shape[1]))
+    L = np.empty(rows.size)
+    Dr = np.empty(rows.size)
+    for s in range(0, rows.size, ROW_BLOCK):
+        r = rows[s:s + ROW_BLOCK]
+        _, P, m, l = probabilities(qh, kg, scale, causal, r)
+        Or = P @ vg
+        dP = doh[r] @ vg.T
+        D = (doh[r] * Or).sum(axis=1)
+        dS = P * (dP - D[:, None])
+        dQ[s:s + r.size] = scale * (dS @ kg)
+        O[s:s + r.size] = Or
+        L[s:s + r.size] = m + np.log(l)
+        Dr[s:s + r.size] = D
+    return dQ, O, L, Dr
+
+
+def head_full_stats(qh, kg, vg, doh, causal, scale):
+    """LSE and D for every row of one head (row blocks, full rows of P)."""
+    n = np.asarray(qh).shape[0]
+    _, _, L, D = head_rows_backward_dq(qh, kg, vg, doh, np.arange(n), causal, scale)
+    return L, D
+
+
+def head_cols_backward_dkdv(q_heads, kg, vg, do_heads, stats, cols, causal, scale):
+    """dK and dV rows (key positions ``cols``) of one key/value head.
+
+    For each query head h of the group, with its full-row LSE and D
+    (``stats[h] = (LSE, D)``): P[:, j] = exp(S[:, j] - LSE), dP[:, j] =
+    dO v_j, dS[:, j] = P[:, j] (dP[:, j] - D); dV_j = sum_i P_ij dO_i and
+    dK_j = scale sum_i dS_ij Q_i, summed over the group's query heads.
+    P from LSE is the recomputation of [FA-legal] entry "Recomputation".
+    """
+    cols = np.asarray(cols, dtype=np.int64)
+    kg = np.asarray(kg, dtype=np.float64)
+    vg = np.asarray(vg, dtype=np.float64)
+    n = kg.shape[0]
+    rows = np.arange(n)
+    dK = np.zeros((cols.size, kg.shape[1]))
+    dV = np.zeros((cols.size, vg.shape[1]))
+    for qh, doh, (L, D) in zip(q_heads, do_heads, stats):
+        qh = np.asarray(qh, dtype=np.float64)
+        doh = np.asarray(doh, dtype=np.float64)
+        S = scale * (qh @ kg[cols].T)                      # [n, |cols|]
+        if causal:
+            S = np.where(cols[None, :] <= rows[:, None], S, -np.inf)
+        P = np.exp(S - np.asarray(L)[:, None])
+        dP = doh @ vg[cols].T
+        dS = P * (dP - np.asarray(D)[:, None])
+        dV += P.T @ doh
+        dK += scale * (dS.T @ qh)
+    return dK, dV
+
+
+def attention_matrix_bytes(n: int, bytes_per_element: int) -> int:
+    """Bytes of one head's N x N score matrix that standard attention writes.
+
+    [IO-aware], "The Memory Bandwidth Bottleneck": standard attention writes
+    S and P (N x N) to HBM; this is the size of one such matrix.
+    """
+    return int(n) * int(n) * int(bytes_per_element)

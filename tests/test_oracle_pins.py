@@ -1,0 +1,300 @@
+"""Pins of the CPU float64 oracle against what the pages and the mathematics fix.
+
+Each test names the fact it checks.  None re-types the oracle's formula: the
+checks are closed forms, invariants, central finite differences, torch's own
+CPU float64 scaled_dot_product_attention (a separate library routine), and the
+pages' printed memory arithmetic (tests/golden/memory_arithmetic.txt).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(seed, shape, sigma=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * sigma
+
+
+# ---------------------------------------------------------------- V1: softmax rows
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    q, k = rnd(1, (37, 16)), rnd(2, (37, 16))
+    _, P, _, _ = oracle.probabilities(q, k, 0.25, causal)
+    assert np.all(P >= 0)
+    assert np.max(np.abs(P.sum(axis=1) - 1.0)) <= 1e-12
+    if causal:
+        assert np.all(np.triu(P, 1) == 0.0)
+
+
+# ---------------------------------------------------------------- V2: single key
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_key_returns_v(causal):
+    q, k, v = rnd(3, (1, 1, 1, 8)), rnd(4, (1, 1, 1, 8)), rnd(5, (1, 1, 1, 8))
+    O, L = oracle.forward(q, k, v, causal, 0.7)
+    assert np.array_equal(O, v)
+    assert abs(L[0, 0, 0] - 0.7 * float(q[0, 0, 0] @ k[0, 0, 0])) <= 1e-14
+
+
+# ---------------------------------------------------------------- V3: identical keys
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_v(causal):
+    N, d, scale = 50, 8, 0.3
+    q = rnd(6, (1, 1, N, d))
+    krow = rnd(7, (d,))
+    k = np.broadcast_to(krow, (1, 1, N, d)).copy()
+    v = rnd(8, (1, 1, N, d))
+    O, L = oracle.forward(q, k, v, causal, scale)
+    qk = scale * (q[0, 0] @ krow)
+    if causal:
+        counts = np.arange(1, N + 1)
+        expect_o = np.cumsum(v[0, 0], axis=0) / counts[:, None]
+        expect_l = qk + np.log(counts)
+    else:
+        expect_o = np.broadcast_to(v[0, 0].mean(axis=0), (N, d))
+        expect_l = qk + np.log(N)
+    assert np.max(np.abs(O[0, 0] - expect_o)) <= 1e-12
+    assert np.max(np.abs(L[0, 0] - expect_l)) <= 1e-12
+
+
+# ---------------------------------------------------------------- V4: causal row 0
+
+def test_causal_row_zero_returns_v0():
+    q, k, v = rnd(9, (2, 3, 20, 8)), rnd(10, (2, 3, 20, 8)), rnd(11, (2, 3, 20, 8))
+    O, L = oracle.forward(q, k, v, True, 0.5)
+    assert np.array_equal(O[:, :, 0], v[:, :, 0])
+    expect = 0.5 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0])
+    assert np.max(np.abs(L[:, :, 0] - expect)) <= 1e-14
+
+
+# ---------------------------------------------------------------- V5: online == two-pass
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_online_softmax_matches_two_pass(causal, seed):
+    N = 41
+    q, k, v = rnd(20 + seed, (1, 2, N, 8), 3.0), rnd(30 + seed, (1, 2, N, 8), 3.0), rnd(40 + seed, (1, 2, N, 8))
+    rng = np.random.default_rng(seed)
+    sizes, left = [], N
+    while left:
+        s = int(rng.integers(1, left + 1))
+        sizes.append(s)
+        left -= s
+    O1, L1 = oracle.forward(q, k, v, causal, 0.4)
+    for blocks in (sizes, [1] * N, [N]):
+        O2, L2 = oracle.forward_online(q, k, v, causal, 0.4, blocks)
+        assert np.max(np.abs(O2 - O1)) <= 1e-12 * max(1.0, np.max(np.abs(O1)))
+        assert np.max(np.abs(L2 - L1) / np.maximum(1.0, np.abs(L1))) <= 1e-12
+
+
+# ---------------------------------------------------------------- V6: finite differences
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_central_differences(causal):
+    B, Hq, Hkv, N, d, scale = 1, 4, 2, 7, 4, 0.6
+    q, k, v = rnd(50, (B, Hq, N, d)), rnd(51, (B, Hkv, N, d)), rnd(52, (B, Hkv, N, d))
+    do = rnd(53, (B, Hq, N, d))
+
+    def loss(q_, k_, v_):
+        O, _ = oracle.forward(q_, k_, v_, causal, scale)
+        return float(np.sum(do * O))
+
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, causal, scale)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        rel = np.linalg.norm(num - g) / np.linalg.norm(g)
+        assert rel <= 1e-6, (name, rel)
+
+
+# ---------------------------------------------------------------- V7: D identity
+
+def test_delta_identity():
+    q, k, v, do = rnd(60, (1, 2, 33, 8)), rnd(61, (1, 2, 33, 8)), rnd(62, (1, 2, 33, 8)), rnd(63, (1, 2, 33, 8))
+    _, _, _, D = oracle.backward(q, k, v, do, True, 0.3)
+    for h in range(2):
+        _, P, _, _ = oracle.probabilities(q[0, h], k[0, h], 0.3, True)
+        dP = do[0, h] @ v[0, h].T
+        assert np.max(np.abs(D[0, h] - (P * dP).sum(axis=1))) <= 1e-12
+
+
+# ---------------------------------------------------------------- V8: torch CPU SDPA
+
+def _torch_reference(q, k, v, do, causal, scale):
+    F = torch.nn.functional
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale,
+                                       enable_gqa=tq.shape[1] != tk.shape[1])
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    G = tq.shape[1] // tk.shape[1]
+    kr = tk.detach().repeat_interleave(G, dim=1)
+    s = scale * (tq.detach() @ kr.transpose(-1, -2))
+    if causal:
+        n = s.shape[-1]
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return (o.detach().numpy(), lse.numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy())
+
+
+@pytest.mark.parametrize("shape,causal", [
+    ((1, 2, 2, 256, 64), False),     # the tiny fp32 workload's shape
+    ((2, 4, 2, 19, 8), True),
+    ((1, 6, 3, 33, 16), False),
+    ((1, 8, 1, 12, 4), True),
+])
+def test_matches_torch_cpu_float64_sdpa(shape, causal):
+    B, Hq, Hkv, N, d = shape
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, do = (rnd(70 + i, (B, H, N, d)) for i, H in enumerate((Hq, Hkv, Hkv, Hq)))
+    O, L = oracle.forward(q, k, v, causal, scale)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, causal, scale)
+    to, tl, tdq, tdk, tdv = _torch_reference(q, k, v, do, causal, scale)
+    for a, b in ((O, to), (L, tl), (dq, tdq), (dk, tdk), (dv, tdv)):
+        assert np.max(np.abs(a - b)) <= 1e-12 * max(1.0, np.max(np.abs(b)))
+
+
+# ---------------------------------------------------------------- V9: shift invariance
+
+def test_key_shift_invariance_large_offset():
+    N, d, scale = 24, 8, 0.5
+    q, k, v = rnd(80, (1, 1, N, d)), rnd(81, (1, 1, N, d)), rnd(82, (1, 1, N, d))
+    w = rnd(83, (d,)) * 50.0
+    O1, L1 = oracle.forward(q, k, v, False, scale)
+    O2, L2 = oracle.forward(q, k + w, v, False, scale)
+    assert np.max(np.abs(O2 - O1)) <= 1e-9
+    shift = scale * (q[0, 0] @ w)
+    assert np.max(np.abs(L2[0, 0] - (L1[0, 0] + shift))) <= 1e-9 * np.max(np.abs(shift))
+
+
+# ---------------------------------------------------------------- V10: permutations
+
+def test_permutation_equivariance():
+    N, d, scale = 30, 8, 0.35
+    q, k, v = rnd(90, (1, 1, N, d)), rnd(91, (1, 1, N, d)), rnd(92, (1, 1, N, d))
+    pk = np.random.default_rng(93).permutation(N)
+    pq = np.random.default_rng(94).permutation(N)
+    O1, L1 = oracle.forward(q, k, v, False, scale)
+    O2, L2 = oracle.forward(q, k[:, :, pk], v[:, :, pk], False, scale)
+    assert np.max(np.abs(O2 - O1)) <= 1e-13 and np.max(np.abs(L2 - L1)) <= 1e-13
+    O3, L3 = oracle.forward(q[:, :, pq], k, v, False, scale)
+    assert np.max(np.abs(O3 - O1[:, :, pq])) <= 1e-13 and np.max(np.abs(L3 - L1[:, :, pq])) <= 1e-13
+
+
+# ---------------------------------------------------------------- V11: grouped heads
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_repeated_mha(causal):
+    B, Hq, Hkv, N, d, scale = 2, 6, 2, 15, 8, 0.3
+    G = Hq // Hkv
+    q, k, v, do = rnd(100, (B, Hq, N, d)), rnd(101, (B, Hkv, N, d)), rnd(102, (B, Hkv, N, d)), rnd(103, (B, Hq, N, d))
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    O1, L1 = oracle.forward(q, k, v, causal, scale)
+    O2, L2 = oracle.forward(q, kr, vr, causal, scale)
+    assert np.max(np.abs(O1 - O2)) <= 1e-14 and np.max(np.abs(L1 - L2)) <= 1e-14
+    dq1, dk1, dv1, _ = oracle.backward(q, k, v, do, causal, scale)
+    dq2, dk2, dv2, _ = oracle.backward(q, kr, vr, do, causal, scale)
+    assert np.max(np.abs(dq1 - dq2)) <= 1e-13
+    assert np.max(np.abs(dk1 - dk2.reshape(B, Hkv, G, N, d).sum(axis=2))) <= 1e-12
+    assert np.max(np.abs(dv1 - dv2.reshape(B, Hkv, G, N, d).sum(axis=2))) <= 1e-12
+
+
+# ---------------------------------------------------------------- sampled forms == full forms
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_and_columns_match_full(causal):
+    B, Hq, Hkv, N, d, scale = 1, 4, 2, 300, 16, 0.25
+    G = Hq // Hkv
+    q, k, v, do = rnd(110, (B, Hq, N, d)), rnd(111, (B, Hkv, N, d)), rnd(112, (B, Hkv, N, d)), rnd(113, (B, Hq, N, d))
+    O, L = oracle.forward(q, k, v, causal, scale)
+    dq, dk, dv, D = oracle.backward(q, k, v, do, causal, scale)
+    rows = np.array([0, 1, 5, 128, 255, 256, 299])
+    for h in range(Hq):
+        g = h // G
+        Or, Lr = oracle.head_rows_forward(q[0, h], k[0, g], v[0, g], rows, causal, scale)
+        assert np.max(np.abs(Or - O[0, h, rows])) <= 1e-13
+        assert np.max(np.abs(Lr - L[0, h, rows])) <= 1e-13
+        dQr, _, _, Dr = oracle.head_rows_backward_dq(q[0, h], k[0, g], v[0, g], do[0, h], rows, causal, scale)
+        assert np.max(np.abs(dQr - dq[0, h, rows])) <= 1e-12
+        assert np.max(np.abs(Dr - D[0, h, rows])) <= 1e-12
+    for g in range(Hkv):
+        hs = range(g * G, (g + 1) * G)
+        stats = [oracle.head_full_stats(q[0, h], k[0, g], v[0, g], do[0, h], causal, scale) for h in hs]
+        dKc, dVc = oracle.head_cols_backward_dkdv([q[0, h] for h in hs], k[0, g], v[0, g],
+                                                  [do[0, h] for h in hs], stats, rows, causal, scale)
+        assert np.max(np.abs(dKc - dk[0, g, rows])) <= 1e-12
+        assert np.max(np.abs(dVc - dv[0, g, rows])) <= 1e-12
+
+
+# ---------------------------------------------------------------- V12: printed memory arithmetic
+
+def test_pages_memory_arithmetic():
+    lines = [ln.split("--")[0].split() for ln in open(os.path.join(GOLDEN, "memory_arithmetic.txt"))
+             if ln.strip() and not ln.startswith("#")]
+    assert len(lines) == 3
+    for f in lines:
+        if f[0] == "ratio":
+            n1, n2, ratio = int(f[1]), int(f[2]), int(f[3])
+            assert oracle.attention_matrix_bytes(n1, 2) == ratio * oracle.attention_matrix_bytes(n2, 2)
+        else:
+            n, e, rel, val = int(f[0]), int(f[1]), f[2], int(f[3])
+            got = oracle.attention_matrix_bytes(n, e)
+            assert (got == val) if rel == "==" else (got >= val)
+
+
+# ---------------------------------------------------------------- fp8 (OCP E4M3)
+
+def test_e4m3_decode_matches_format_definition_and_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    d = oracle.e4m3_decode(codes)
+    # format facts: largest finite 448, smallest subnormal 2^-9, smallest normal 2^-6, NaN codes
+    assert np.nanmax(d) == 448.0 and d[0x7E] == 448.0
+    assert d[0x01] == 2.0 ** -9 and d[0x08] == 2.0 ** -6 and d[0x38] == 1.0
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF]) and np.sum(np.isnan(d)) == 2
+    t = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    ok = ~np.isnan(d)
+    assert np.array_equal(d[ok], t[ok])
+
+
+def test_e4m3_encode_round_trip_ties_and_saturation():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    assert np.array_equal(oracle.e4m3_encode_rne_sat(vals), codes)
+    # ties go to the even mantissa: 1 + 1/16 lies halfway between 1 and 1.125
+    assert oracle.e4m3_encode_rne_sat(np.array([1.0625, 1.1875]))[0] == 0x38
+    assert oracle.e4m3_encode_rne_sat(np.array([1.1875]))[0] == 0x3A
+    # half the smallest subnormal rounds to (signed) zero; beyond 448 saturates
+    assert list(oracle.e4m3_encode_rne_sat(np.array([2.0 ** -10, -2.0 ** -10]))) == [0x00, 0x80]
+    assert list(oracle.e4m3_encode_rne_sat(np.array([460.0, 1e9, -1e9]))) == [0x7E, 0x7E, 0xFE]
+    x = np.random.default_rng(5).standard_normal(200000).astype(np.float32) * 60
+    x = x[np.abs(x) < 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode_rne_sat(x), ref)
+
+
+def test_quantize_per_tensor_scale_and_range():
+    x = (np.random.default_rng(6).standard_normal(4096) * 3).astype(np.float32)
+    codes, s = oracle.quantize_per_tensor(x)
+    assert s.dtype == np.float32 and s == np.float32(np.max(np.abs(x))) / np.float32(448.0)
+    back = oracle.e4m3_decode(codes) * np.float64(s)
+    # E4M3 keeps 3 mantissa bits: normal values carry relative error at most 2^-4
+    big = np.abs(x) > 2.0 ** -6 * s
+    assert np.max(np.abs(back[big] - x[big]) / np.abs(x[big])) <= 2.0 ** -4 + 1e-7
+    assert np.max(np.abs(oracle.e4m3_decode(codes))) == 448.0
+    z, sz = oracle.quantize_per_tensor(np.zeros(8, np.float32))
+    assert sz == np.float32(2.0 ** -120) / np.float32(448.0) and not z.any()
