@@ -1,0 +1,108 @@
+// C entry points declared in include/fa.h: argument validation (host only,
+// before any HIP call), then dispatch to the kernel launchers.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Common shape checks.  Returns FA_OK and sets *empty for an empty problem.
+fa_status_t check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float scale, bool* empty) {
+    if (B < 0 || Hq < 0 || Hkv < 0 || N < 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_UNSUPPORTED;
+    *empty = (B == 0 || Hq == 0 || N == 0);
+    if (*empty) return FA_OK;
+    if (Hkv == 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    // grids are one-dimensional: (query or key blocks) x heads x batch must fit
+    const int64_t blocks = ((int64_t)N + 31) / 32 * (int64_t)Hq * (int64_t)B;
+    if (blocks > INT32_MAX) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+fa_status_t launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                   int N, int d, int causal, float softmax_scale, int dtype, const float* descale_qkv,
+                   hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    const bool fp8 = dtype == FA_DTYPE_FP8_E4M3;
+    if (fp8 != (descale_qkv != nullptr)) return fp8 ? FA_ERR_NULL : FA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    if (fp8 && !aligned(descale_qkv, 4)) return FA_ERR_ALIGN;
+    if (o == q || o == k || o == v || (void*)lse == q || (void*)lse == k || (void*)lse == v || (void*)lse == o)
+        return FA_ERR_ALIAS;
+    if (fp8)
+        return launch_status(fa::launch_fwd_fp8(d, causal, q, k, v, o, lse, descale_qkv, B, Hq, Hkv, N,
+                                                softmax_scale, stream));
+    return launch_status(fa::launch_fwd(dtype, d, causal, q, k, v, o, lse, B, Hq, Hkv, N, softmax_scale, stream));
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, float* delta_ws, int B, int Hq, int Hkv, int N, int d,
+                   int causal, float softmax_scale, int dtype, hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !delta_ws) return FA_ERR_NULL;
+    const void* in[6] = {q, k, v, o, dO, lse};
+    const void* out[4] = {dq, dk, dv, delta_ws};
+    for (const void* p : in)
+        if (!aligned(p, p == (const void*)lse ? 4 : 16)) return FA_ERR_ALIGN;
+    for (const void* p : out)
+        if (!aligned(p, p == (const void*)delta_ws ? 4 : 16)) return FA_ERR_ALIGN;
+    for (const void* a : out)
+        for (const void* b : in)
+            if (a == b) return FA_ERR_ALIAS;
+    if (dq == dk || dq == dv || dk == dv || (void*)delta_ws == dq || (void*)delta_ws == dk ||
+        (void*)delta_ws == dv)
+        return FA_ERR_ALIAS;
+    return launch_status(fa::launch_bwd(dtype, d, causal, q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv,
+                                        N, softmax_scale, stream));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int N) {
+    if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+    return (size_t)4 * (size_t)B * (size_t)Hq * (size_t)N;
+}
+
+fa_status_t fa_quantize_fp8(const void* x_bf16, size_t n, void* x_e4m3, float* descale, hipStream_t stream) {
+    if (!descale || (n > 0 && (!x_bf16 || !x_e4m3))) return FA_ERR_NULL;
+    if (!aligned(descale, 4) || (n > 0 && !aligned(x_bf16, 2))) return FA_ERR_ALIGN;
+    if (n > 0 && ((const void*)x_e4m3 == x_bf16 || (const void*)descale == x_bf16 ||
+                  (const void*)descale == (const void*)x_e4m3))
+        return FA_ERR_ALIAS;
+    return launch_status(fa::launch_quantize_fp8(x_bf16, n, x_e4m3, descale, stream));
+}
+
+const char* fa_status_string(fa_status_t s) {
+    switch (s) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "invalid shape (negative size, Hkv == 0 or Hq % Hkv != 0, or too large)";
+        case FA_ERR_UNSUPPORTED: return "unsupported head dim, dtype, causal flag or softmax scale";
+        case FA_ERR_ALIGN: return "pointer misaligned (tensors need 16 bytes, float arrays 4)";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_ALIAS: return "an output aliases an input";
+        default: return "unknown status";
+    }
+}
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+}  // extern "C"

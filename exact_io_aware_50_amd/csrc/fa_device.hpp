@@ -1,0 +1,265 @@
+// Device-side building blocks shared by the attention kernels (gfx950 only).
+//
+// Matrix-core convention used everywhere.  One 32x32 output block comes from
+// v_mfma_f32_32x32x16_bf16 (bf16) or eight chained v_mfma_f32_32x32x2f32
+// (float32).  Lane l of a wave64 owns column n = l % 32 of the output and the
+// sixteen rows  row(r, hh) = 8*(r/4) + 4*hh + (r%4),  r = 0..15, hh = l / 32.
+// For the A operand (M x 16) lane l supplies row l % 32, for the B operand
+// (16 x N) column l % 32; in both, lane l supplies the eight contraction
+// slots 8*hh + e, e = 0..7.  Which hardware k each slot is does not matter:
+// A and B use the same slot order, and a contraction is order-free.
+//
+// "Accumulator as operand": registers r = 8t..8t+7 of an accumulator hold rows
+// 16t + 8*(e/4) + 4*hh + (e%4).  Fed back as the B operand of a product that
+// contracts over those rows, slot 8*hh + e must therefore meet row
+// 16t + swap23(8*hh + e) of the other operand, where swap23 exchanges bits 2
+// and 3 of an index.  Tiles that are read as "transposed" A operands store the
+// contraction index at position swap23(index) (within aligned groups of 16),
+// so that each lane reads eight contiguous elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite "minus infinity" for the running maximum: exp2(kNegBig - m) is 0 for
+// any finite m, and kNegBig - kNegBig = 0 never produces NaN.
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ int swap23(int p) {
+    return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of the same lane in the other half of the wave (lane l <-> l ^ 32).
+__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+    // float32 -> bfloat16, round to nearest even (inputs here are never NaN).
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ----------------------------------------------------------------------------
+// Element types.  A "raw8" holds 8 consecutive elements as opaque bits (one
+// operand fragment or one staging chunk); "raw4" holds 4.
+// ----------------------------------------------------------------------------
+struct BF16 {
+    using elem = uint16_t;
+    using raw8 = u32x4;
+    using raw4 = u32x2;
+    static constexpr int kBytes = 2;
+
+    static __device__ __forceinline__ f32x16 mma(raw8 a, raw8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    // 8 accumulator registers (floats) -> one operand fragment.
+    static __device__ __forceinline__ raw8 pack8(const f32x16& v, int base) {
+        raw8 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r[i] = bf16_bits_rne(v[base + 2 * i]) | (bf16_bits_rne(v[base + 2 * i + 1]) << 16);
+        return r;
+    }
+    static __device__ __forceinline__ raw8 pack8_scaled(const f32x16& v, int base, float s) {
+        raw8 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r[i] = bf16_bits_rne(v[base + 2 * i] * s) | (bf16_bits_rne(v[base + 2 * i + 1] * s) << 16);
+        return r;
+    }
+    static __device__ __forceinline__ raw4 pack4(float a, float b, float c, float d) {
+        raw4 r;
+        r[0] = bf16_bits_rne(a) | (bf16_bits_rne(b) << 16);
+        r[1] = bf16_bits_rne(c) | (bf16_bits_rne(d) << 16);
+        return r;
+    }
+    // element e of a raw8 as its 16 bits in the low half of a word
+    static __device__ __forceinline__ uint32_t get(const raw8& r, int e) {
+        return (e & 1) ? (r[e >> 1] >> 16) : (r[e >> 1] & 0xffffu);
+    }
+    static __device__ __forceinline__ raw4 join4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+        raw4 r;
+        r[0] = a | (b << 16);
+        r[1] = c | (d << 16);
+        return r;
+    }
+    static __device__ __forceinline__ float to_f32(const raw8& r, int e) {
+        return __uint_as_float(get(r, e) << 16);
+    }
+};
+
+struct F32 {
+    using elem = float;
+    using raw8 = u32x8;
+    using raw4 = u32x4;
+    static constexpr int kBytes = 4;
+
+    static __device__ __forceinline__ f32x16 mma(raw8 a, raw8 b, f32x16 c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[e]), __uint_as_float(b[e]), c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ raw8 pack8(const f32x16& v, int base) {
+        raw8 r;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = __float_as_uint(v[base + i]);
+        return r;
+    }
+    static __device__ __forceinline__ raw8 pack8_scaled(const f32x16& v, int base, float s) {
+        raw8 r;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = __float_as_uint(v[base + i] * s);
+        return r;
+    }
+    static __device__ __forceinline__ raw4 pack4(float a, float b, float c, float d) {
+        raw4 r;
+        r[0] = __float_as_uint(a); r[1] = __float_as_uint(b);
+        r[2] = __float_as_uint(c); r[3] = __float_as_uint(d);
+        return r;
+    }
+    static __device__ __forceinline__ uint32_t get(const raw8& r, int e) { return r[e]; }
+    static __device__ __forceinline__ raw4 join4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+        raw4 r;
+        r[0] = a; r[1] = b; r[2] = c; r[3] = d;
+        return r;
+    }
+    static __device__ __forceinline__ float to_f32(const raw8& r, int e) { return __uint_as_float(r[e]); }
+};
+
+template <class ET>
+__device__ __forceinline__ typename ET::raw8 ld8(const typename ET::elem* p) {
+    return *reinterpret_cast<const typename ET::raw8*>(p);
+}
+template <class ET>
+__device__ __forceinline__ void st8(typename ET::elem* p, const typename ET::raw8& v) {
+    *reinterpret_cast<typename ET::raw8*>(p) = v;
+}
+template <class ET>
+__device__ __forceinline__ void st4(typename ET::elem* p, const typename ET::raw4& v) {
+    *reinterpret_cast<typename ET::raw4*>(p) = v;
+}
+
+// ----------------------------------------------------------------------------
+// Global -> LDS staging of one ROWS x COLS tile (row-major in global memory,
+// COLS elements per row, rows past `rows_valid` read as zero).  Loads go to
+// registers first so that the next tile's loads overlap the current compute.
+//
+// NatTile: LDS copy keeps the layout, row stride COLS + 8 elements.
+// TrTile : LDS copy is transposed, [COLS][ROWS + 8], with the row index
+//          stored at position swap23(row) -- the "transposed A operand" form.
+// ----------------------------------------------------------------------------
+template <class ET, int ROWS, int COLS, int NT>
+struct NatTile {
+    using elem = typename ET::elem;
+    using raw8 = typename ET::raw8;
+    static constexpr int kSegs = COLS / 8;
+    static constexpr int kChunks = ROWS * kSegs;
+    static constexpr int kPer = (kChunks + NT - 1) / NT;
+    static constexpr int kStride = COLS + 8;
+    static constexpr int kElems = ROWS * kStride;
+    raw8 r[kPer];
+
+    __device__ __forceinline__ void load(const elem* src, int rows_valid, int tid) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = tid + i * NT;
+            const int row = c / kSegs, seg = c % kSegs;
+            raw8 v = {};
+            if ((kChunks % NT == 0 || c < kChunks) && row < rows_valid)
+                v = ld8<ET>(src + (int64_t)row * COLS + seg * 8);
+            r[i] = v;
+        }
+    }
+    __device__ __forceinline__ void store(elem* lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = tid + i * NT;
+            if (kChunks % NT == 0 || c < kChunks) {
+                const int row = c / kSegs, seg = c % kSegs;
+                st8<ET>(lds + row * kStride + seg * 8, r[i]);
+            }
+        }
+    }
+};
+
+template <class ET, int ROWS, int COLS, int NT>
+struct TrTile {
+    using elem = typename ET::elem;
+    using raw8 = typename ET::raw8;
+    static constexpr int kGroups = ROWS / 4;          // groups of 4 source rows
+    static constexpr int kSegs = COLS / 8;            // 8-column segments
+    static constexpr int kTasks = kGroups * kSegs;    // one 4 x 8 block per task
+    static constexpr int kPer = (kTasks + NT - 1) / NT;
+    static constexpr int kStride = ROWS + 8;
+    static constexpr int kElems = COLS * kStride;
+    static_assert(ROWS % 16 == 0, "transposed tiles hold whole groups of 16 rows");
+    raw8 r[kPer][4];
+
+    __device__ __forceinline__ void load(const elem* src, int rows_valid, int tid) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int t = tid + i * NT;
+            const int rg = t % kGroups, seg = t / kGroups;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                raw8 v = {};
+                const int row = 4 * rg + j;
+                if ((kTasks % NT == 0 || t < kTasks) && row < rows_valid)
+                    v = ld8<ET>(src + (int64_t)row * COLS + seg * 8);
+                r[i][j] = v;
+            }
+        }
+    }
+    __device__ __forceinline__ void store(elem* lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int t = tid + i * NT;
+            if (kTasks % NT == 0 || t < kTasks) {
+                const int rg = t % kGroups, seg = t / kGroups;
+                const int pos = swap23(4 * rg);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    st4<ET>(lds + (8 * seg + e) * kStride + pos,
+                            ET::join4(ET::get(r[i][0], e), ET::get(r[i][1], e),
+                                      ET::get(r[i][2], e), ET::get(r[i][3], e)));
+            }
+        }
+    }
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
+// Give every XCD one contiguous range of logical tiles, so that the tiles of a
+// head (which share K and V) run on the same XCD.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+    constexpr int kXcd = 8;
+    const int per = total / kXcd, rem = total % kXcd;
+    const int x = bid % kXcd, i = bid / kXcd;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+// Row index (within a 32-row block) held by register r of lane half hh.
+__device__ __forceinline__ constexpr int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+
+}  // namespace fa

@@ -1,0 +1,25 @@
+// Internal launchers (C++ linkage) called by the C entry points in fa_api.hip.
+// Arguments are already validated; each returns the launch's hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+// dtype: 0 = float32, 1 = bfloat16 (fp8 goes through launch_fwd_fp8)
+hipError_t launch_fwd(int dtype, int d, int causal, const void* q, const void* k, const void* v,
+                      void* o, float* lse, int B, int Hq, int Hkv, int N, float scale,
+                      hipStream_t st);
+
+hipError_t launch_fwd_fp8(int d, int causal, const void* q, const void* k, const void* v,
+                          void* o, float* lse, const float* descale, int B, int Hq, int Hkv, int N,
+                          float scale, hipStream_t st);
+
+hipError_t launch_bwd(int dtype, int d, int causal, const void* q, const void* k, const void* v,
+                      const void* o, const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                      float* delta, int B, int Hq, int Hkv, int N, float scale, hipStream_t st);
+
+hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
+
+}  // namespace fa

@@ -1,0 +1,164 @@
+"""Python binding of libfa.so (the C ABI in include/fa.h).
+
+Argument marshalling only: every step of attention runs in the HIP kernels
+behind the C entry points.  The raw entry points keep their C names
+(``fa_fwd``, ``fa_bwd``, ...) and take integer device addresses; the tensor
+helpers ``fwd``, ``bwd`` and ``quantize_fp8`` allocate outputs with torch and
+pass its current HIP stream.
+
+Importing this module fails loudly if the library has not been built
+(``python -m exact_io_aware_50_amd.build``); there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_50_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+FA_DTYPE_F32, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_LAUNCH, FA_ERR_ALIAS = range(7)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+_lib.fa_fwd.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p]
+_lib.fa_fwd.restype = _i
+_lib.fa_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
+_lib.fa_bwd.restype = _i
+_lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i]
+_lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+_lib.fa_quantize_fp8.argtypes = [_p, ctypes.c_size_t, _p, _p, _p]
+_lib.fa_quantize_fp8.restype = _i
+_lib.fa_status_string.argtypes = [_i]
+_lib.fa_status_string.restype = ctypes.c_char_p
+_lib.fa_abi_version.argtypes = []
+_lib.fa_abi_version.restype = _i
+
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_quantize_fp8", "fa_status_string",
+           "fa_abi_version")
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({fa_status_string(status)})")
+        self.status = status
+
+
+# ------------------------------------------------------------------ raw C entry points
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, softmax_scale, dtype, descale_qkv, stream) -> int:
+    return _lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(softmax_scale), dtype,
+                       descale_qkv, stream)
+
+
+def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal, softmax_scale, dtype,
+           stream) -> int:
+    return _lib.fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, int(causal),
+                       float(softmax_scale), dtype, stream)
+
+
+def fa_bwd_workspace_bytes(B, Hq, N) -> int:
+    return int(_lib.fa_bwd_workspace_bytes(B, Hq, N))
+
+
+def fa_quantize_fp8(x_bf16, n, x_e4m3, descale, stream) -> int:
+    return _lib.fa_quantize_fp8(x_bf16, n, x_e4m3, descale, stream)
+
+
+def fa_status_string(status: int) -> str:
+    return _lib.fa_status_string(status).decode()
+
+
+def fa_abi_version() -> int:
+    return int(_lib.fa_abi_version())
+
+
+# ------------------------------------------------------------------ torch tensor helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.uint8:
+        return FA_DTYPE_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != FA_OK:
+        raise FAError(status, where)
+
+
+def _shape(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    for t in (q, k):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+    B, Hq, N, d = q.shape
+    return B, Hq, k.shape[1], N, d
+
+
+def fwd(q, k, v, causal: bool, scale: float, descale=None, stream=None):
+    """(o, lse) for q [B,Hq,N,d], k, v [B,Hkv,N,d] (fp32, bf16, or E4M3 codes as uint8 + descale[3])."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    if v.shape != k.shape or not v.is_contiguous() or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("v must match k in shape and all of q, k, v in dtype")
+    code = _dtype_code(q)
+    odt = torch.bfloat16 if code == FA_DTYPE_FP8_E4M3 else q.dtype
+    o = torch.empty((B, Hq, N, d), dtype=odt, device=q.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    dptr = None if descale is None else descale.data_ptr()
+    _check(fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
+                  causal, scale, code, dptr, _stream_handle(stream)), "fa_fwd")
+    return o, lse
+
+
+def bwd(q, k, v, o, do, lse, causal: bool, scale: float, stream=None, workspace=None):
+    """(dq, dk, dv, delta) for the forward's inputs and outputs and the output gradient do."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    code = _dtype_code(q)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, d, causal,
+                  scale, code, _stream_handle(stream)), "fa_bwd")
+    return dq, dk, dv, workspace
+
+
+def quantize_fp8(x, stream=None):
+    """(codes uint8 like x, descale float32[1]) for a contiguous bf16 device tensor x."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous bf16 device tensor")
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    ds = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(fa_quantize_fp8(x.data_ptr(), x.numel(), out.data_ptr(), ds.data_ptr(), _stream_handle(stream)),
+           "fa_quantize_fp8")
+    return out, ds

@@ -1,0 +1,137 @@
+/*
+ * fa.h -- exact, tiled, fused softmax attention on AMD MI355X (gfx950).
+ *
+ * The operation (all pages; "flash attention io aware", section "The Memory
+ * Bandwidth Bottleneck", steps 1-3): for every batch b and query head h,
+ *     S = scale * Q[b,h] K[b,g]^T        (N x N, never stored)
+ *     causal: S[i,j] = -inf for j > i    ("Paper digest: FlashAttention",
+ *                                        section "Limits", names causal masks)
+ *     P = softmax(S) over keys,  O[b,h] = P V[b,g],
+ *     LSE[b,h,i] = ln sum_j exp(S[i,j])  (natural log; the log-sum-exp of the
+ *                                        FA-LLM glossary's third paragraph)
+ * where g = h / (Hq / Hkv) is the key/value head of the query head's group
+ * ("Flash Attention" self-hosted-LLM glossary, entry "Grouped-Query Attention":
+ * query heads are split into contiguous groups sharing one K/V head).
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or synchronises, keeps no mutable global
+ *    state, and enqueues all work on `stream` (NULL = the default stream).
+ *  - Layouts are contiguous, row-major, head dimension fastest:
+ *    Q, O, dO, dQ are [B, Hq, N, d]; K, V, dK, dV are [B, Hkv, N, d];
+ *    LSE and the backward workspace are [B, Hq, N] float32.
+ *  - Element types: FA_DTYPE_F32 = IEEE float32, FA_DTYPE_BF16 = bfloat16
+ *    bits, FA_DTYPE_FP8_E4M3 = OCP E4M3 ("e4m3fn") codes.  O and the
+ *    gradients take the input type, except that an FP8 forward writes bf16 O.
+ *  - Supported: d in {64, 128}; Hkv >= 1 and Hq % Hkv == 0; causal in {0, 1};
+ *    0 < softmax_scale < inf.  B == 0, Hq == 0 or N == 0 is an empty problem:
+ *    FA_OK is returned and nothing is read or written.
+ *  - Tensor base pointers must be 16-byte aligned, float pointers 4-byte.
+ *    Outputs must not alias inputs.
+ *  - Errors: every argument is validated on the host before any HIP call;
+ *    a bad argument returns a nonzero fa_status_t and enqueues nothing.  A
+ *    failed launch returns FA_ERR_LAUNCH.  Device faults surface at the
+ *    caller's next synchronisation of `stream`.
+ *  - No atomics in attention: results are bitwise reproducible run to run.
+ *  - Calls on different streams are independent and thread-safe.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+    FA_DTYPE_F32 = 0,
+    FA_DTYPE_BF16 = 1,
+    FA_DTYPE_FP8_E4M3 = 2
+} fa_dtype_t;
+
+typedef int fa_status_t;
+enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,          /* a required pointer is NULL                  */
+    FA_ERR_SHAPE = 2,         /* negative size, Hkv == 0, Hq % Hkv != 0, ... */
+    FA_ERR_UNSUPPORTED = 3,   /* d, dtype, causal flag or scale not supported */
+    FA_ERR_ALIGN = 4,         /* pointer misaligned                          */
+    FA_ERR_LAUNCH = 5,        /* the HIP launch failed                       */
+    FA_ERR_ALIAS = 6          /* an output aliases an input                  */
+};
+
+#define FA_ABI_VERSION 1
+
+/*
+ * Forward pass.  "flash attention io aware", section "Flash Attention
+ * Algorithm" (tiles of Q, K, V in on-chip memory; online softmax; write only
+ * O) and section "Online Softmax"; "FlashAttention" legal-glossary paragraph
+ * on FlashAttention-2 (parallel over the sequence).
+ *   q, k, v     : inputs, dtype `dtype` (FP8: E4M3 codes from fa_quantize_fp8)
+ *   o           : output [B,Hq,N,d]; dtype `dtype` (bf16 when dtype is FP8)
+ *   lse         : output [B,Hq,N] float32, natural-log log-sum-exp of the
+ *                 scaled scores of each query row
+ *   descale_qkv : FP8 only, device float[3] = (s_Q, s_K, s_V) with real value
+ *                 = code value * s_X; must be NULL for other dtypes
+ * Returns FA_OK once the kernel is enqueued.
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v,
+                   void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d,
+                   int causal, float softmax_scale,
+                   int dtype, const float* descale_qkv,
+                   hipStream_t stream);
+
+/*
+ * Backward pass by recomputation: "FlashAttention" legal glossary, backward
+ * paragraph and entry "Recomputation" (only the softmax statistics are kept;
+ * S and P are recomputed on chip); FlashAttention-2 paragraph (the backward
+ * is parallel over the key (column) blocks, without atomic adds).
+ * Three kernels run in order on `stream`: D = rowsum(dO * O) into `delta_ws`,
+ * then dK/dV (one workgroup per key block and K/V head, looping over the query
+ * heads of its group) and dQ (one workgroup per query block and query head).
+ *   q, k, v, o, dO, lse : as produced/consumed by fa_fwd (same dtype, F32 or
+ *                         BF16 only)
+ *   dq [B,Hq,N,d], dk, dv [B,Hkv,N,d] : outputs, overwritten (not accumulated)
+ *   delta_ws : caller-owned device workspace of fa_bwd_workspace_bytes() bytes;
+ *              holds D on return
+ */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v,
+                   const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv,
+                   float* delta_ws,
+                   int B, int Hq, int Hkv, int N, int d,
+                   int causal, float softmax_scale, int dtype,
+                   hipStream_t stream);
+
+/* Bytes of the fa_bwd workspace: 4 * B * Hq * N (0 for an empty problem). */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int N);
+
+/*
+ * Per-tensor FP8 quantisation for the FP8 forward ("FlashAttention" legal
+ * glossary, FlashAttention-3 paragraph, and "flash attention io aware",
+ * section "Flash Attention 2 and 3", name FP8 attention but give no recipe;
+ * this is the plainest one): s = max(absmax(x), 2^-120) / 448 in float32 and
+ * code_i = E4M3 round-to-nearest-even, saturating at +-448, of x_i / s.
+ *   x_bf16  : n bf16 values (device)        x_e4m3 : n output codes (device)
+ *   descale : device float[1] receiving s (it is also used as the absmax
+ *             scratch while the call runs)
+ * Four small kernels are enqueued; n == 0 writes s = 2^-120 / 448.
+ */
+fa_status_t fa_quantize_fp8(const void* x_bf16, size_t n, void* x_e4m3,
+                            float* descale, hipStream_t stream);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* fa_status_string(fa_status_t s);
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -202,9 +202,10 @@ def head_rows_backward_dq(qh, kg, vg, doh, rows, causal, scale):
 
 
 def head_full_stats(qh, kg, vg, doh, causal, scale):
-    """LSE and D for every row of one head (row blocks, full rows of P)."""
+    """LSE and D = rowsum(dO * O) for every row of one head (row blocks, full rows of P)."""
     n = np.asarray(qh).shape[0]
-    _, _, L, D = head_rows_backward_dq(qh, kg, vg, doh, np.arange(n), causal, scale)
+    O, L = head_rows_forward(qh, kg, vg, np.arange(n), causal, scale)
+    D = (np.asarray(doh, dtype=np.float64) * O).sum(axis=1)
     return L, D
 
 

@@ -26,3 +26,13 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _built_library():
+    """Build libfa.so once if it is missing (a built library is used as is)."""
+    lib = os.path.join(ROOT, "exact_io_aware_50_amd", "libfa.so")
+    if not os.path.exists(lib):
+        from exact_io_aware_50_amd import build
+        build.build(verbose=False)
+    yield

@@ -1,0 +1,115 @@
+"""Host-only checks of the C-ABI library: it loads, exports every function the
+public header declares, the header is plain C, and every validation error is
+returned before any HIP call (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_is_plain_c():
+    r = subprocess.run(["gcc", "-std=c99", "-fsyntax-only", "-Wall", "-Werror", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_library_exports_every_declared_function():
+    from exact_io_aware_50_amd import fa
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    names = header_functions()
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_quantize_fp8",
+                          "fa_status_string", "fa_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(fa.EXPORTS) == set(names)
+    assert fa.fa_abi_version() == 1
+
+
+def test_status_strings():
+    from exact_io_aware_50_amd import fa
+    seen = {fa.fa_status_string(s) for s in range(7)}
+    assert len(seen) == 7
+    assert fa.fa_status_string(99) == "unknown status"
+
+
+def test_workspace_bytes():
+    from exact_io_aware_50_amd import fa
+    assert fa.fa_bwd_workspace_bytes(4, 32, 4096) == 4 * 4 * 32 * 4096
+    assert fa.fa_bwd_workspace_bytes(0, 32, 4096) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, -5) == 0
+
+
+# Fake, well-aligned addresses: validation must reject the call before it
+# could ever be dereferenced or launched.
+A = [0x10000 * (i + 1) for i in range(12)]
+
+
+def fwd(**kw):
+    from exact_io_aware_50_amd import fa
+    args = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, Hq=2, Hkv=2, N=256, d=64, causal=0,
+                softmax_scale=0.125, dtype=fa.FA_DTYPE_BF16, descale_qkv=None, stream=None)
+    args.update(kw)
+    return fa.fa_fwd(**args)
+
+
+def bwd(**kw):
+    from exact_io_aware_50_amd import fa
+    args = dict(q=A[0], k=A[1], v=A[2], o=A[3], dO=A[4], lse=A[5], dq=A[6], dk=A[7], dv=A[8], delta_ws=A[9],
+                B=1, Hq=2, Hkv=2, N=256, d=64, causal=0, softmax_scale=0.125, dtype=1, stream=None)
+    args.update(kw)
+    return fa.fa_bwd(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(lse=None), 1), (dict(o=None), 1),
+    (dict(d=96), 3), (dict(d=0), 3), (dict(dtype=7), 3), (dict(causal=2), 3),
+    (dict(softmax_scale=0.0), 3), (dict(softmax_scale=-1.0), 3), (dict(softmax_scale=float("inf")), 3),
+    (dict(softmax_scale=float("nan")), 3),
+    (dict(B=-1), 2), (dict(N=-3), 2), (dict(Hkv=0), 2), (dict(Hq=6, Hkv=4), 2),
+    (dict(B=65536, Hq=65536, N=1 << 20), 2),
+    (dict(q=A[0] + 8), 4), (dict(v=A[2] + 2), 4), (dict(lse=A[4] + 2), 4),
+    (dict(o=A[0]), 6), (dict(lse=A[3]), 6),
+    (dict(dtype=2), 1),                       # fp8 needs descale
+    (dict(descale_qkv=A[5]), 3),              # descale only with fp8
+    (dict(dtype=2, descale_qkv=A[5] + 1), 4),
+])
+def test_fwd_validation(kw, status):
+    assert fwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0), dict(Hq=0), dict(B=0, q=None, k=None)])
+def test_fwd_empty_problem_is_ok_and_touches_nothing(kw):
+    assert fwd(**kw) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dO=None), 1), (dict(delta_ws=None), 1), (dict(dv=None), 1),
+    (dict(dtype=2), 3), (dict(d=32), 3), (dict(Hq=3, Hkv=2), 2),
+    (dict(dq=A[0] + 4), 4), (dict(delta_ws=A[9] + 1), 4),
+    (dict(dq=A[0]), 6), (dict(dk=A[6]), 6), (dict(delta_ws=A[8]), 6), (dict(dv=A[5]), 6),
+])
+def test_bwd_validation(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_bwd_empty_problem_is_ok():
+    assert bwd(N=0) == 0 and bwd(B=0, q=None) == 0
+
+
+def test_quantize_validation():
+    from exact_io_aware_50_amd import fa
+    assert fa.fa_quantize_fp8(A[0], 16, A[1], None, None) == 1
+    assert fa.fa_quantize_fp8(None, 16, A[1], A[2], None) == 1
+    assert fa.fa_quantize_fp8(A[0], 16, A[1], A[2] + 2, None) == 4
+    assert fa.fa_quantize_fp8(A[0], 16, A[0], A[2], None) == 6
