@@ -1,0 +1,285 @@
+"""Throughput of exact fused attention on one MI355X.
+
+One step = one forward (fa_fwd) plus one backward (fa_bwd_delta, fa_bwd_dkdv,
+fa_bwd_dq: the three stages fa_bwd runs) over the headline workload: bf16,
+causal, B=4, H=32, N=4096, d=128, Q, K, V, dO i.i.d. N(0, 1) from fixed seeds,
+all inputs resident in device memory before the timed region.
+
+Credited flops (the usual attention convention): forward 4 B H N^2 d, halved
+when causal; backward 2.5 x forward.  `value` is forward+backward TFLOP/s over
+the timed steps; forward-only TFLOP/s and the per-kernel figures ride along.
+
+Each kernel is bracketed by HIP events recorded on the stream it is launched
+on (torch's current stream, which the binding passes to the C ABI); the
+dominant kernel's average duration gives the roofline figure.  The CPU leg
+times the float64 oracle on a bounded sample of the same workload's heads.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd and fwd+bwd TFLOP/s and % of MI355X bf16 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def credited(w):
+    f = 4.0 * w.B * w.Hq * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    return f, 2.5 * f
+
+
+def kernel_flops(w):
+    """Algorithmic matrix-product flops each kernel must execute per launch.
+
+    Per (batch, query head), with f = 1/2 for causal: forward S = QK^T and PV
+    (4 N^2 d f); dK/dV recomputes S, forms dP = dO V^T, dV = P^T dO and
+    dK = dS^T Q (8 N^2 d f); dQ recomputes S and dP and forms dS K (6 N^2 d f).
+    """
+    u = w.B * w.Hq * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    return {"fwd": 4 * u, "bwd_dkdv": 8 * u, "bwd_dq": 6 * u}
+
+
+def delta_bytes(w):
+    e = 2 if w.dtype == "bf16" else 4
+    return 2 * w.B * w.Hq * w.N * w.d * e + 4 * w.B * w.Hq * w.N
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
+
+    The summary records the sha256 of the kernel's source file; a changed source
+    makes the stored figure stale and it is not reported.
+    """
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith(f"{kernel} {workload} "):
+            for kv in line.split()[2:]:
+                k, _, v = kv.partition("=")
+                rec[k] = v
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "exact_io_aware_50_amd", "csrc", rec.get("source", ""))
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("sha256"):
+        return None
+    return float(rec["bytes_per_launch"])
+
+
+def cpu_baseline(w, seconds):
+    """Time the float64 oracle (forward + backward, P materialised) on whole heads."""
+    import numpy as np
+    import oracle
+    from exact_io_aware_50_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    heads = 0
+    t0 = time.perf_counter()
+    while True:
+        b, h = divmod(heads, w.Hq)
+        g = h // (w.Hq // w.Hkv)
+        q = I.head_slice(w, I.Q_ID, b, h).double().numpy()[None, None]
+        k = I.head_slice(w, I.K_ID, b, g).double().numpy()[None, None]
+        v = I.head_slice(w, I.V_ID, b, g).double().numpy()[None, None]
+        do = I.head_slice(w, I.DO_ID, b, h).double().numpy()[None, None]
+        ts = time.perf_counter()
+        oracle.forward(q, k, v, w.causal, w.scale)
+        oracle.backward(q, k, v, do, w.causal, w.scale)
+        t_comp = time.perf_counter() - ts
+        heads += 1
+        if heads == 1:
+            elapsed = t_comp
+        else:
+            elapsed += t_comp
+        if elapsed >= seconds or heads >= w.B * w.Hq or time.perf_counter() - t0 > 3 * seconds:
+            break
+    fwd, bwd = credited(w)
+    per_head = (fwd + bwd) / (w.B * w.Hq)
+    return {"value": per_head * heads / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 oracle forward+backward of {heads} whole head(s) (b, h) in order of "
+                      f"{w.name.split(' ')[0]}; credited flops of those heads / compute time ({elapsed:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal_bf16_n4096")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (calibrates HBM byte counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_io_aware_50_amd import fa, inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {w.name}")
+    q, k, v, do = (I.full_tensor(w, t).to(dev) for t in range(4))
+    B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
+    code = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def check(st, name):
+        if st != fa.FA_OK:
+            raise fa.FAError(st, name)
+
+    calls = [
+        ("fwd", lambda: fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq,
+                                  Hkv, N, d, w.causal, w.scale, code, None, sh)),
+        ("bwd_delta", lambda: fa.fa_bwd_delta(o.data_ptr(), do.data_ptr(), delta.data_ptr(), B, Hq, N, d, code,
+                                              sh)),
+        ("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                                            lse.data_ptr(), delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq,
+                                            Hkv, N, d, w.causal, w.scale, code, sh)),
+        ("bwd_dq", lambda: fa.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                        delta.data_ptr(), dq.data_ptr(), B, Hq, Hkv, N, d, w.causal, w.scale,
+                                        code, sh)),
+    ]
+
+    def step(events=None):
+        for i, (name, fn) in enumerate(calls):
+            if events is not None:
+                events[i].record(stream)
+            check(fn(), name)
+        if events is not None:
+            events[len(calls)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {name: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
+           for i, (name, _) in enumerate(calls)}
+    gpu_ms = sum(evs[s][0].elapsed_time(evs[s][-1]) for s in range(args.steps)) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, {gpu_ms:.3f} ms/step on events; "
+        + ", ".join(f"{n} {t:.3f} ms" for n, t in per.items()))
+
+    fwd_fl, bwd_fl = credited(w)
+    value = (fwd_fl + bwd_fl) / (ms_per_step * 1e-3) / 1e12
+    fwd_tf = fwd_fl / (per["fwd"] * 1e-3) / 1e12
+    kfl = kernel_flops(w)
+    kern = {}
+    for n, t in per.items():
+        ent = {"ms": round(t, 4)}
+        if n in kfl:
+            tf = kfl[n] / (t * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), frac_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+        else:
+            gbs = delta_bytes(w) / (t * 1e-3) / 1e9
+            ent.update(gbs=round(gbs, 1), frac_peak=round(gbs / PEAK_HBM_GBS, 4))
+        kern[n] = ent
+    dom = max((n for n in per if n in kfl), key=lambda n: per[n])
+    ach = kfl[dom] / (per[dom] * 1e-3) / 1e12
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": stored_traffic(dom, args.workload)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
+        "config": {"workload": args.workload, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d,
+                   "causal": w.causal},
+        "fwd_bwd_tflops": round(value, 2),
+        "fwd_bwd_frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(fwd_tf, 2),
+        "fwd_frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+        "kernels": kern,
+        "roofline": roof,
+    }
+
+    if not args.no_fp8 and w.dtype == "bf16":
+        q8, sq = fa.quantize_fp8(q)
+        k8, sk = fa.quantize_fp8(k)
+        v8, sv = fa.quantize_fp8(v)
+        ds = torch.cat([sq, sk, sv])
+        o8 = torch.empty_like(q)
+        run8 = lambda: check(fa.fa_fwd(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o8.data_ptr(), lse.data_ptr(),
+                                       B, Hq, Hkv, N, d, w.causal, w.scale, fa.FA_DTYPE_FP8_E4M3, ds.data_ptr(),
+                                       sh), "fa_fwd fp8")
+        for _ in range(args.warmup):
+            run8()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            run8()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t8 = e0.elapsed_time(e1) / args.steps
+        tf8 = fwd_fl / (t8 * 1e-3) / 1e12
+        result["fp8_fwd"] = {"ms": round(t8, 4), "tflops": round(tf8, 1),
+                             "frac_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
+                             "note": "E4M3 forward of the same shape, inputs quantised per tensor outside the timing"}
+        log(f"fp8 forward {t8:.3f} ms ({tf8:.0f} TFLOP/s)")
+
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        bcopy = torch.empty_like(a)
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy of {args.copy_mib} MiB done")
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (float64 oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

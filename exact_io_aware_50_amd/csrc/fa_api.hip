@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "fa.h"
 #include "fa_launch.hpp"
 
@@ -52,6 +54,43 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
     return launch_status(fa::launch_fwd(dtype, d, causal, q, k, v, o, lse, B, Hq, Hkv, N, softmax_scale, stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Pointer checks shared by the backward entry points: non-NULL, aligned (float
+// arrays to 4 bytes, tensors to 16), and no output equal to an input or to
+// another output.
+fa_status_t check_ptrs(std::initializer_list<const void*> in, std::initializer_list<const void*> in_f32,
+                       std::initializer_list<const void*> out, std::initializer_list<const void*> out_f32) {
+    for (auto l : {in, in_f32, out, out_f32})
+        for (const void* p : l)
+            if (!p) return FA_ERR_NULL;
+    for (const void* p : in)
+        if (!aligned(p, 16)) return FA_ERR_ALIGN;
+    for (const void* p : out)
+        if (!aligned(p, 16)) return FA_ERR_ALIGN;
+    for (const void* p : in_f32)
+        if (!aligned(p, 4)) return FA_ERR_ALIGN;
+    for (const void* p : out_f32)
+        if (!aligned(p, 4)) return FA_ERR_ALIGN;
+    for (auto lo : {out, out_f32})
+        for (const void* a : lo) {
+            for (auto li : {in, in_f32})
+                for (const void* b : li)
+                    if (a == b) return FA_ERR_ALIAS;
+            int same = 0;
+            for (auto lo2 : {out, out_f32})
+                for (const void* b : lo2) same += (a == b);
+            if (same > 1) return FA_ERR_ALIAS;
+        }
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                    void* dq, void* dk, void* dv, float* delta_ws, int B, int Hq, int Hkv, int N, int d,
                    int causal, float softmax_scale, int dtype, hipStream_t stream) {
@@ -59,21 +98,53 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
     if (s != FA_OK || empty) return s;
-    if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !delta_ws) return FA_ERR_NULL;
-    const void* in[6] = {q, k, v, o, dO, lse};
-    const void* out[4] = {dq, dk, dv, delta_ws};
-    for (const void* p : in)
-        if (!aligned(p, p == (const void*)lse ? 4 : 16)) return FA_ERR_ALIGN;
-    for (const void* p : out)
-        if (!aligned(p, p == (const void*)delta_ws ? 4 : 16)) return FA_ERR_ALIGN;
-    for (const void* a : out)
-        for (const void* b : in)
-            if (a == b) return FA_ERR_ALIAS;
-    if (dq == dk || dq == dv || dk == dv || (void*)delta_ws == dq || (void*)delta_ws == dk ||
-        (void*)delta_ws == dv)
-        return FA_ERR_ALIAS;
-    return launch_status(fa::launch_bwd(dtype, d, causal, q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv,
-                                        N, softmax_scale, stream));
+    s = check_ptrs({q, k, v, o, dO}, {lse}, {dq, dk, dv}, {delta_ws});
+    if (s != FA_OK) return s;
+    hipError_t e = fa::launch_bwd_delta(dtype, d, o, dO, delta_ws, B, Hq, N, stream);
+    if (e == hipSuccess)
+        e = fa::launch_bwd_dkdv(dtype, d, causal, q, k, v, dO, lse, delta_ws, dk, dv, B, Hq, Hkv, N,
+                                softmax_scale, stream);
+    if (e == hipSuccess)
+        e = fa::launch_bwd_dq(dtype, d, causal, q, k, v, dO, lse, delta_ws, dq, B, Hq, Hkv, N, softmax_scale,
+                              stream);
+    return launch_status(e);
+}
+
+fa_status_t fa_bwd_delta(const void* o, const void* dO, float* delta, int B, int Hq, int N, int d, int dtype,
+                         hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, 1, N, d, 0, 1.0f, &empty);
+    if (s != FA_OK || empty) return s;
+    s = check_ptrs({o, dO}, {}, {}, {delta});
+    if (s != FA_OK) return s;
+    return launch_status(fa::launch_bwd_delta(dtype, d, o, dO, delta, B, Hq, N, stream));
+}
+
+fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                        const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal,
+                        float softmax_scale, int dtype, hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    s = check_ptrs({q, k, v, dO}, {lse, delta}, {dk, dv}, {});
+    if (s != FA_OK) return s;
+    return launch_status(fa::launch_bwd_dkdv(dtype, d, causal, q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N,
+                                             softmax_scale, stream));
+}
+
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                      const float* delta, void* dq, int B, int Hq, int Hkv, int N, int d, int causal,
+                      float softmax_scale, int dtype, hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    s = check_ptrs({q, k, v, dO}, {lse, delta}, {dq}, {});
+    if (s != FA_OK) return s;
+    return launch_status(fa::launch_bwd_dq(dtype, d, causal, q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N,
+                                           softmax_scale, stream));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N) {

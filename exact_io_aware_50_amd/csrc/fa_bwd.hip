@@ -358,49 +358,67 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     }
 }
 
-template <class ET, int D, bool CAUSAL>
-static hipError_t launch(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                         const float* lse, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
-                         int Hkv, int N, float scale, hipStream_t st) {
+template <class ET, int D>
+static hipError_t launch_delta(const void* o, const void* dO, float* delta, int B, int Hq, int N, hipStream_t st) {
     using elem = typename ET::elem;
     const int64_t rows = (int64_t)B * Hq * N;
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_delta_kernel<ET, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                       st, (const elem*)o, (const elem*)dO, delta, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
-    const float c2 = scale * kLog2e;
-    const int nkb = (N + KVCfg<ET, D>::BNK - 1) / KVCfg<ET, D>::BNK;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<ET, D, CAUSAL>), dim3((unsigned)((int64_t)nkb * Hkv * B)), dim3(256),
-                       0, st, (const elem*)q, (const elem*)k, (const elem*)v, (const elem*)dO, lse, delta,
-                       (elem*)dk, (elem*)dv, Hq, Hkv, N, c2, scale);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
-    const int nmb = (N + QCfg<ET, D>::BM - 1) / QCfg<ET, D>::BM;
-    hipLaunchKernelGGL((bwd_dq_kernel<ET, D, CAUSAL>), dim3((unsigned)((int64_t)nmb * Hq * B)), dim3(256), 0,
-                       st, (const elem*)q, (const elem*)k, (const elem*)v, (const elem*)dO, lse, delta,
-                       (elem*)dq, Hq, Hkv, N, c2, scale);
+    hipLaunchKernelGGL((bwd_delta_kernel<ET, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
+                       (const elem*)o, (const elem*)dO, delta, rows);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd(int dtype, int d, int causal, const void* q, const void* k, const void* v,
-                      const void* o, const void* dO, const float* lse, void* dq, void* dk, void* dv,
-                      float* delta, int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
-#define FA_BWD_CASE(ET, DD)                                                                              \
-    if (d == DD)                                                                                         \
-        return causal ? launch<ET, DD, true>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, Hkv, N, scale, st) \
-                      : launch<ET, DD, false>(q, k, v, o, dO, lse, dq, dk, dv, delta, B, Hq, Hkv, N, scale, st);
-    if (dtype == 1) {
-        FA_BWD_CASE(BF16, 64)
-        FA_BWD_CASE(BF16, 128)
-    } else if (dtype == 0) {
-        FA_BWD_CASE(F32, 64)
-        FA_BWD_CASE(F32, 128)
-    }
-#undef FA_BWD_CASE
+template <class ET, int D, bool CAUSAL>
+static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                              const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale,
+                              hipStream_t st) {
+    using elem = typename ET::elem;
+    const int nkb = (N + KVCfg<ET, D>::BNK - 1) / KVCfg<ET, D>::BNK;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<ET, D, CAUSAL>), dim3((unsigned)((int64_t)nkb * Hkv * B)), dim3(256), 0,
+                       st, (const elem*)q, (const elem*)k, (const elem*)v, (const elem*)dO, lse, delta,
+                       (elem*)dk, (elem*)dv, Hq, Hkv, N, scale * kLog2e, scale);
+    return hipGetLastError();
+}
+
+template <class ET, int D, bool CAUSAL>
+static hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                            const float* delta, void* dq, int B, int Hq, int Hkv, int N, float scale,
+                            hipStream_t st) {
+    using elem = typename ET::elem;
+    const int nmb = (N + QCfg<ET, D>::BM - 1) / QCfg<ET, D>::BM;
+    hipLaunchKernelGGL((bwd_dq_kernel<ET, D, CAUSAL>), dim3((unsigned)((int64_t)nmb * Hq * B)), dim3(256), 0, st,
+                       (const elem*)q, (const elem*)k, (const elem*)v, (const elem*)dO, lse, delta, (elem*)dq,
+                       Hq, Hkv, N, scale * kLog2e, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_delta(int dtype, int d, const void* o, const void* dO, float* delta, int B, int Hq, int N,
+                            hipStream_t st) {
+    if (dtype == 1 && d == 64) return launch_delta<BF16, 64>(o, dO, delta, B, Hq, N, st);
+    if (dtype == 1 && d == 128) return launch_delta<BF16, 128>(o, dO, delta, B, Hq, N, st);
+    if (dtype == 0 && d == 64) return launch_delta<F32, 64>(o, dO, delta, B, Hq, N, st);
+    if (dtype == 0 && d == 128) return launch_delta<F32, 128>(o, dO, delta, B, Hq, N, st);
     return hipErrorInvalidValue;
 }
+
+#define FA_DISPATCH(FN, ...)                                                          \
+    if (dtype == 1 && d == 64) return causal ? FN<BF16, 64, true>(__VA_ARGS__) : FN<BF16, 64, false>(__VA_ARGS__);   \
+    if (dtype == 1 && d == 128) return causal ? FN<BF16, 128, true>(__VA_ARGS__) : FN<BF16, 128, false>(__VA_ARGS__); \
+    if (dtype == 0 && d == 64) return causal ? FN<F32, 64, true>(__VA_ARGS__) : FN<F32, 64, false>(__VA_ARGS__);     \
+    if (dtype == 0 && d == 128) return causal ? FN<F32, 128, true>(__VA_ARGS__) : FN<F32, 128, false>(__VA_ARGS__);  \
+    return hipErrorInvalidValue;
+
+hipError_t launch_bwd_dkdv(int dtype, int d, int causal, const void* q, const void* k, const void* v,
+                           const void* dO, const float* lse, const float* delta, void* dk, void* dv, int B,
+                           int Hq, int Hkv, int N, float scale, hipStream_t st) {
+    FA_DISPATCH(launch_dkdv, q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N, scale, st)
+}
+
+hipError_t launch_bwd_dq(int dtype, int d, int causal, const void* q, const void* k, const void* v,
+                         const void* dO, const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
+                         int N, float scale, hipStream_t st) {
+    FA_DISPATCH(launch_dq, q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N, scale, st)
+}
+#undef FA_DISPATCH
 
 }  // namespace fa

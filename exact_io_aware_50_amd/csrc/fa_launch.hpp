@@ -16,9 +16,16 @@ hipError_t launch_fwd_fp8(int d, int causal, const void* q, const void* k, const
                           void* o, float* lse, const float* descale, int B, int Hq, int Hkv, int N,
                           float scale, hipStream_t st);
 
-hipError_t launch_bwd(int dtype, int d, int causal, const void* q, const void* k, const void* v,
-                      const void* o, const void* dO, const float* lse, void* dq, void* dk, void* dv,
-                      float* delta, int B, int Hq, int Hkv, int N, float scale, hipStream_t st);
+hipError_t launch_bwd_delta(int dtype, int d, const void* o, const void* dO, float* delta, int B, int Hq, int N,
+                            hipStream_t st);
+
+hipError_t launch_bwd_dkdv(int dtype, int d, int causal, const void* q, const void* k, const void* v,
+                           const void* dO, const float* lse, const float* delta, void* dk, void* dv, int B,
+                           int Hq, int Hkv, int N, float scale, hipStream_t st);
+
+hipError_t launch_bwd_dq(int dtype, int d, int causal, const void* q, const void* k, const void* v,
+                         const void* dO, const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
+                         int N, float scale, hipStream_t st);
 
 hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
 

@@ -33,6 +33,12 @@ _lib.fa_fwd.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, 
 _lib.fa_fwd.restype = _i
 _lib.fa_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_bwd.restype = _i
+_lib.fa_bwd_delta.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.fa_bwd_delta.restype = _i
+_lib.fa_bwd_dkdv.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
+_lib.fa_bwd_dkdv.restype = _i
+_lib.fa_bwd_dq.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
+_lib.fa_bwd_dq.restype = _i
 _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_quantize_fp8.argtypes = [_p, ctypes.c_size_t, _p, _p, _p]
@@ -42,8 +48,8 @@ _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_abi_version.argtypes = []
 _lib.fa_abi_version.restype = _i
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_quantize_fp8", "fa_status_string",
-           "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
+           "fa_quantize_fp8", "fa_status_string", "fa_abi_version")
 
 
 class FAError(RuntimeError):
@@ -63,6 +69,20 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal, 
            stream) -> int:
     return _lib.fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, int(causal),
                        float(softmax_scale), dtype, stream)
+
+
+def fa_bwd_delta(o, dO, delta, B, Hq, N, d, dtype, stream) -> int:
+    return _lib.fa_bwd_delta(o, dO, delta, B, Hq, N, d, dtype, stream)
+
+
+def fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N, d, causal, softmax_scale, dtype, stream) -> int:
+    return _lib.fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N, d, int(causal), float(softmax_scale),
+                            dtype, stream)
+
+
+def fa_bwd_dq(q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N, d, causal, softmax_scale, dtype, stream) -> int:
+    return _lib.fa_bwd_dq(q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N, d, int(causal), float(softmax_scale),
+                          dtype, stream)
 
 
 def fa_bwd_workspace_bytes(B, Hq, N) -> int:

@@ -107,6 +107,37 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v,
                    int causal, float softmax_scale, int dtype,
                    hipStream_t stream);
 
+/*
+ * The three stages of fa_bwd as separate calls, for callers that schedule or
+ * time them one by one.  Same arguments, validation and layouts as fa_bwd;
+ * fa_bwd_dkdv and fa_bwd_dq read the D that fa_bwd_delta wrote into `delta`,
+ * and do not depend on each other.
+ *   fa_bwd_delta : D[b,h,i] = sum_c dO[b,h,i,c] * O[b,h,i,c] in float32 (the
+ *                  row term of the softmax gradient: sum_j P_ij dP_ij equals it)
+ *   fa_bwd_dkdv  : dK, dV, parallel over key blocks ("FlashAttention" legal
+ *                  glossary, FlashAttention-2 paragraph: column-parallel
+ *                  backward without atomic adds); a workgroup owns one key
+ *                  block of one K/V head and sums over its group's query heads
+ *   fa_bwd_dq    : dQ, parallel over query blocks
+ */
+fa_status_t fa_bwd_delta(const void* o, const void* dO, float* delta,
+                         int B, int Hq, int N, int d, int dtype,
+                         hipStream_t stream);
+
+fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v,
+                        const void* dO, const float* lse, const float* delta,
+                        void* dk, void* dv,
+                        int B, int Hq, int Hkv, int N, int d,
+                        int causal, float softmax_scale, int dtype,
+                        hipStream_t stream);
+
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v,
+                      const void* dO, const float* lse, const float* delta,
+                      void* dq,
+                      int B, int Hq, int Hkv, int N, int d,
+                      int causal, float softmax_scale, int dtype,
+                      hipStream_t stream);
+
 /* Bytes of the fa_bwd workspace: 4 * B * Hq * N (0 for an empty problem). */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N);
 

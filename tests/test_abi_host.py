@@ -28,8 +28,8 @@ def test_library_exports_every_declared_function():
     from exact_io_aware_50_amd import fa
     lib = ctypes.CDLL(fa.LIB_PATH)
     names = header_functions()
-    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_quantize_fp8",
-                          "fa_status_string", "fa_abi_version"}
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
+                          "fa_bwd_workspace_bytes", "fa_quantize_fp8", "fa_status_string", "fa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(fa.EXPORTS) == set(names)
@@ -113,3 +113,24 @@ def test_quantize_validation():
     assert fa.fa_quantize_fp8(None, 16, A[1], A[2], None) == 1
     assert fa.fa_quantize_fp8(A[0], 16, A[1], A[2] + 2, None) == 4
     assert fa.fa_quantize_fp8(A[0], 16, A[0], A[2], None) == 6
+
+
+def test_stage_entry_points_validation():
+    from exact_io_aware_50_amd import fa
+    # delta: o, dO, delta
+    assert fa.fa_bwd_delta(None, A[1], A[2], 1, 2, 64, 64, 1, None) == 1
+    assert fa.fa_bwd_delta(A[0], A[1], A[2] + 2, 1, 2, 64, 64, 1, None) == 4
+    assert fa.fa_bwd_delta(A[0], A[1], A[0], 1, 2, 64, 64, 1, None) == 6
+    assert fa.fa_bwd_delta(A[0], A[1], A[2], 1, 2, 64, 80, 1, None) == 3
+    assert fa.fa_bwd_delta(A[0], A[1], A[2], 1, 2, 0, 64, 1, None) == 0
+    base = dict(B=1, Hq=2, Hkv=2, N=64, d=64, causal=1, softmax_scale=0.1, dtype=1, stream=None)
+    kv = dict(q=A[0], k=A[1], v=A[2], dO=A[3], lse=A[4], delta=A[5], dk=A[6], dv=A[7])
+    assert fa.fa_bwd_dkdv(**{**kv, "delta": None}, **base) == 1
+    assert fa.fa_bwd_dkdv(**{**kv, "dk": A[7]}, **base) == 6          # dk == dv
+    assert fa.fa_bwd_dkdv(**{**kv, "dv": A[1]}, **base) == 6          # dv == k
+    assert fa.fa_bwd_dkdv(**kv, **{**base, "Hkv": 3}) == 2
+    assert fa.fa_bwd_dkdv(**kv, **{**base, "dtype": 2}) == 3
+    dq = dict(q=A[0], k=A[1], v=A[2], dO=A[3], lse=A[4], delta=A[5], dq=A[6])
+    assert fa.fa_bwd_dq(**{**dq, "dq": A[6] + 8}, **base) == 4
+    assert fa.fa_bwd_dq(**{**dq, "dq": A[5]}, **base) == 6
+    assert fa.fa_bwd_dq(**dq, **{**base, "N": 0}) == 0
