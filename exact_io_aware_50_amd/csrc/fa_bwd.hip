@@ -1,4 +1,5 @@
-// Backward pass of exact attention by recomputation.
+// Backward pass of exact attention by recomputation (generic kernels, used for
+// float32; bf16 dK/dV and dQ run the tuned kernels in fa_bwd_bf16.hip).
 //
 // The FlashAttention legal glossary (backward paragraph, entry
 // "Recomputation"): the forward keeps only the softmax statistics; the
@@ -402,8 +403,6 @@ hipError_t launch_bwd_delta(int dtype, int d, const void* o, const void* dO, flo
 }
 
 #define FA_DISPATCH(FN, ...)                                                          \
-    if (dtype == 1 && d == 64) return causal ? FN<BF16, 64, true>(__VA_ARGS__) : FN<BF16, 64, false>(__VA_ARGS__);   \
-    if (dtype == 1 && d == 128) return causal ? FN<BF16, 128, true>(__VA_ARGS__) : FN<BF16, 128, false>(__VA_ARGS__); \
     if (dtype == 0 && d == 64) return causal ? FN<F32, 64, true>(__VA_ARGS__) : FN<F32, 64, false>(__VA_ARGS__);     \
     if (dtype == 0 && d == 128) return causal ? FN<F32, 128, true>(__VA_ARGS__) : FN<F32, 128, false>(__VA_ARGS__);  \
     return hipErrorInvalidValue;
@@ -411,12 +410,15 @@ hipError_t launch_bwd_delta(int dtype, int d, const void* o, const void* dO, flo
 hipError_t launch_bwd_dkdv(int dtype, int d, int causal, const void* q, const void* k, const void* v,
                            const void* dO, const float* lse, const float* delta, void* dk, void* dv, int B,
                            int Hq, int Hkv, int N, float scale, hipStream_t st) {
+    if (dtype == 1)
+        return launch_bwd_dkdv_bf16(d, causal, q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N, scale, st);
     FA_DISPATCH(launch_dkdv, q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N, scale, st)
 }
 
 hipError_t launch_bwd_dq(int dtype, int d, int causal, const void* q, const void* k, const void* v,
                          const void* dO, const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
                          int N, float scale, hipStream_t st) {
+    if (dtype == 1) return launch_bwd_dq_bf16(d, causal, q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N, scale, st);
     FA_DISPATCH(launch_dq, q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N, scale, st)
 }
 #undef FA_DISPATCH

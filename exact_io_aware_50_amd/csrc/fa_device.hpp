@@ -262,4 +262,126 @@ __device__ __forceinline__ f32x16 zero16() {
 // Row index (within a 32-row block) held by register r of lane half hh.
 __device__ __forceinline__ constexpr int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
+
+// ----------------------------------------------------------------------------
+// bf16 tiles kept in LDS in their global (row-major) layout, filled by direct
+// global -> LDS loads and read either as rows (16-byte reads, the operand of a
+// product that contracts over the row's columns) or transposed (the operand
+// of a product that contracts over rows).
+//
+// Transposed read (ds_read_b64_tr_b16): inside each 16-lane group, output
+// lane i, element j receives element (i % 4) of what source lane 4*j + i/4
+// loaded.  Source lane t therefore reads row kbase + t/4, columns
+// n0 + 4*(t%4) .. +3, and output lane i ends up holding the column n0 + i for
+// rows kbase .. kbase+3: four consecutive contraction slots of one row of the
+// transposed operand.  Two such reads fill the eight slots of a lane.
+// ----------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+// Pack two floats into two bf16 (hardware round-to-nearest-even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ u32x4 pack_bf16x8(const f32x16& v, int base) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(v[base + 2 * i], v[base + 2 * i + 1]);
+    return r;
+}
+
+// acc + (lo + hi) of the two bf16 values packed in w, in float32.
+__device__ __forceinline__ float dot2_bf16_sum(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                           acc, false);
+}
+
+// Both halves of the wave: (x of lane l%32, x of lane l%32 + 32).
+__device__ __forceinline__ float pair_max(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Tile layout in LDS ("row groups"): rows are taken in groups of RG, where RG
+// rows hold exactly 64 chunks (1 KB, the bytes one wave moves with one direct
+// load).  Inside a group, chunk c of row r sits at 16 * (c * RG + r % RG);
+// groups are RGS = 1 KB + 64 bytes apart.  Consequences:
+//  - one wave fills one group with one global_load_lds, reading 1 KB of
+//    contiguous global memory;
+//  - a row read (16 consecutive lanes: 16 rows, one chunk) touches
+//    16 * 16 bytes spread over groups offset by 64 bytes: no bank collision;
+//  - a transposed read touches, per 16 lanes, 4 rows of 2 neighbouring chunks:
+//    128 contiguous bytes;
+//  - every fragment address is one per-lane base plus a compile-time offset.
+template <int ROWS, int COLS, int NW>
+struct LdsTile {
+    static constexpr int CPR = COLS / 8;                 // 16-byte chunks per row
+    static constexpr int RG = 64 / CPR;                  // rows per group
+    static constexpr int RGS = 1024 + 64;                // bytes between groups
+    static constexpr int kGroups = ROWS / RG;
+    static constexpr int kBytes = kGroups * RGS;
+    static constexpr int kElems = kBytes / 2;
+    static constexpr int kPerWave = kGroups / NW;
+    static_assert(CPR == 8 || CPR == 16, "64 or 128 columns");
+    static_assert(kGroups % NW == 0, "the waves cover the tile in whole groups");
+
+    // Direct global -> LDS copy of rows [0, ROWS) of `src` (row stride COLS).
+    // Rows at or past rows_valid re-read the last valid row: finite values the
+    // caller masks out.
+    static __device__ __forceinline__ void load(const uint16_t* src, int rows_valid, uint16_t* tile, int wave,
+                                                int lane) {
+        const int c = lane / RG, r = lane % RG;
+#pragma unroll
+        for (int i = 0; i < kPerWave; ++i) {
+            const int grp = i * NW + wave;
+            const int row = grp * RG + r;
+            const int grow = row < rows_valid ? row : rows_valid - 1;
+            __builtin_amdgcn_global_load_lds((gbl_void*)(src + (int64_t)grow * COLS + c * 8),
+                                             (lds_void*)((char*)tile + grp * RGS), 16, 0, 0);
+        }
+    }
+    // Byte offset of (row, chunk).
+    static __device__ __forceinline__ constexpr int off(int row, int c) {
+        return (row / RG) * RGS + (c * RG + row % RG) * 16;
+    }
+    // 8 consecutive elements (chunk c) of row r.
+    static __device__ __forceinline__ u32x4 row8(const uint16_t* tile, int r, int c) {
+        return *reinterpret_cast<const u32x4*>((const char*)tile + off(r, c));
+    }
+    // Transposed operand fragment: this lane gets column n0 + lane%32 (n0 a
+    // multiple of 32) for rows kk + swap23(8*hh + e), e = 0..7 (kk a multiple of 16).
+    static __device__ __forceinline__ u32x4 tr8(const uint16_t* tile, int kk, int n0, int lane) {
+        const int hh = lane >> 5, half = (lane >> 4) & 1, t = lane & 15;
+        const int col = n0 + 16 * half + 4 * (t & 3);
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = kk + 8 * i + 4 * hh + (t >> 2);
+            const char* a = (const char*)tile + off(row, col >> 3) + 2 * (col & 7);
+            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
+            const u32x2 w = __builtin_bit_cast(u32x2, v);
+            r[2 * i] = w[0];
+            r[2 * i + 1] = w[1];
+        }
+        return r;
+    }
+};
+
+__device__ __forceinline__ f32x16 mma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
 }  // namespace fa

@@ -1,4 +1,5 @@
-// Forward pass of exact attention: tiled, fused, online softmax.
+// Forward pass of exact attention: tiled, fused, online softmax (float32
+// instantiation; bf16 runs the tuned kernel in fa_fwd_bf16.hip).
 //
 // "flash attention io aware", section "Flash Attention Algorithm": Q, K, V are
 // cut into blocks held on chip; for each Q block the kernel walks the K/V
@@ -203,8 +204,7 @@ hipError_t launch_fwd(int dtype, int d, int causal, const void* q, const void* k
     if (d == DD) return causal ? launch<ET, DD, true>(q, k, v, o, lse, B, Hq, Hkv, N, scale, st)  \
                                : launch<ET, DD, false>(q, k, v, o, lse, B, Hq, Hkv, N, scale, st);
     if (dtype == 1) {
-        FA_FWD_CASE(BF16, 64)
-        FA_FWD_CASE(BF16, 128)
+        return launch_fwd_bf16(d, causal, q, k, v, o, lse, B, Hq, Hkv, N, scale, st);
     } else if (dtype == 0) {
         FA_FWD_CASE(F32, 64)
         FA_FWD_CASE(F32, 128)

@@ -12,6 +12,9 @@ hipError_t launch_fwd(int dtype, int d, int causal, const void* q, const void* k
                       void* o, float* lse, int B, int Hq, int Hkv, int N, float scale,
                       hipStream_t st);
 
+hipError_t launch_fwd_bf16(int d, int causal, const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Hq, int Hkv, int N, float scale, hipStream_t st);
+
 hipError_t launch_fwd_fp8(int d, int causal, const void* q, const void* k, const void* v,
                           void* o, float* lse, const float* descale, int B, int Hq, int Hkv, int N,
                           float scale, hipStream_t st);
@@ -26,6 +29,14 @@ hipError_t launch_bwd_dkdv(int dtype, int d, int causal, const void* q, const vo
 hipError_t launch_bwd_dq(int dtype, int d, int causal, const void* q, const void* k, const void* v,
                          const void* dO, const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
                          int N, float scale, hipStream_t st);
+
+hipError_t launch_bwd_dkdv_bf16(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
+                                const float* lse, const float* delta, void* dk, void* dv, int B, int Hq, int Hkv,
+                                int N, float scale, hipStream_t st);
+
+hipError_t launch_bwd_dq_bf16(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
+                              const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv, int N,
+                              float scale, hipStream_t st);
 
 hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
 
