@@ -56,15 +56,16 @@ def kernel_flops(w):
 
 
 def delta_bytes(w):
+    """Bytes the workspace pass must move: read O, dO and LSE, write D and LSE*log2(e)."""
     e = 2 if w.dtype == "bf16" else 4
-    return 2 * w.B * w.Hq * w.N * w.d * e + 4 * w.B * w.Hq * w.N
+    return 2 * w.B * w.Hq * w.N * w.d * e + 12 * w.B * w.Hq * w.N
 
 
 def stored_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
 
-    The summary records the sha256 of the kernel's source file; a changed source
-    makes the stored figure stale and it is not reported.
+    The summary records the sha256 of the kernel's source files; a changed
+    source makes the stored figure stale and it is not reported.
     """
     import hashlib
     if not os.path.exists(TRAFFIC_FILE):
@@ -77,8 +78,13 @@ def stored_traffic(kernel, workload):
                 rec[k] = v
     if not rec:
         return None
-    src = os.path.join(ROOT, "exact_io_aware_50_amd", "csrc", rec.get("source", ""))
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("sha256"):
+    h = hashlib.sha256()
+    for name in rec.get("source", "").split("+"):
+        src = os.path.join(ROOT, "exact_io_aware_50_amd", "csrc", name)
+        if not name or not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if h.hexdigest() != rec.get("sha256"):
         return None
     return float(rec["bytes_per_launch"])
 
@@ -152,7 +158,7 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, Hq, N) // 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
@@ -163,14 +169,13 @@ def main():
     calls = [
         ("fwd", lambda: fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq,
                                   Hkv, N, d, w.causal, w.scale, code, None, sh)),
-        ("bwd_delta", lambda: fa.fa_bwd_delta(o.data_ptr(), do.data_ptr(), delta.data_ptr(), B, Hq, N, d, code,
-                                              sh)),
-        ("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
-                                            lse.data_ptr(), delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq,
-                                            Hkv, N, d, w.causal, w.scale, code, sh)),
-        ("bwd_dq", lambda: fa.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                                        delta.data_ptr(), dq.data_ptr(), B, Hq, Hkv, N, d, w.causal, w.scale,
-                                        code, sh)),
+        ("bwd_delta", lambda: fa.fa_bwd_delta(o.data_ptr(), do.data_ptr(), lse.data_ptr(), ws.data_ptr(), B, Hq,
+                                              N, d, code, sh)),
+        ("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), ws.data_ptr(),
+                                            dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d, w.causal, w.scale,
+                                            code, sh)),
+        ("bwd_dq", lambda: fa.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), ws.data_ptr(),
+                                        dq.data_ptr(), B, Hq, Hkv, N, d, w.causal, w.scale, code, sh)),
     ]
 
     def step(events=None):

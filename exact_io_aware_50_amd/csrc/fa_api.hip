@@ -98,58 +98,56 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
     if (s != FA_OK || empty) return s;
-    s = check_ptrs({q, k, v, o, dO}, {lse}, {dq, dk, dv}, {delta_ws});
+    s = check_ptrs({q, k, v, o, dO, delta_ws}, {lse}, {dq, dk, dv}, {});
     if (s != FA_OK) return s;
-    hipError_t e = fa::launch_bwd_delta(dtype, d, o, dO, delta_ws, B, Hq, N, stream);
+    hipError_t e = fa::launch_bwd_delta(dtype, d, o, dO, lse, delta_ws, B, Hq, N, stream);
     if (e == hipSuccess)
-        e = fa::launch_bwd_dkdv(dtype, d, causal, q, k, v, dO, lse, delta_ws, dk, dv, B, Hq, Hkv, N,
-                                softmax_scale, stream);
+        e = fa::launch_bwd_dkdv(dtype, d, causal, q, k, v, dO, delta_ws, dk, dv, B, Hq, Hkv, N, softmax_scale,
+                                stream);
     if (e == hipSuccess)
-        e = fa::launch_bwd_dq(dtype, d, causal, q, k, v, dO, lse, delta_ws, dq, B, Hq, Hkv, N, softmax_scale,
-                              stream);
+        e = fa::launch_bwd_dq(dtype, d, causal, q, k, v, dO, delta_ws, dq, B, Hq, Hkv, N, softmax_scale, stream);
     return launch_status(e);
 }
 
-fa_status_t fa_bwd_delta(const void* o, const void* dO, float* delta, int B, int Hq, int N, int d, int dtype,
-                         hipStream_t stream) {
+fa_status_t fa_bwd_delta(const void* o, const void* dO, const float* lse, float* ws, int B, int Hq, int N, int d,
+                         int dtype, hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, 1, N, d, 0, 1.0f, &empty);
     if (s != FA_OK || empty) return s;
-    s = check_ptrs({o, dO}, {}, {}, {delta});
+    s = check_ptrs({o, dO}, {lse}, {ws}, {});
     if (s != FA_OK) return s;
-    return launch_status(fa::launch_bwd_delta(dtype, d, o, dO, delta, B, Hq, N, stream));
+    return launch_status(fa::launch_bwd_delta(dtype, d, o, dO, lse, ws, B, Hq, N, stream));
 }
 
-fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                        const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal,
-                        float softmax_scale, int dtype, hipStream_t stream) {
+fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dk,
+                        void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
+                        hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
     if (s != FA_OK || empty) return s;
-    s = check_ptrs({q, k, v, dO}, {lse, delta}, {dk, dv}, {});
+    s = check_ptrs({q, k, v, dO, ws}, {}, {dk, dv}, {});
     if (s != FA_OK) return s;
-    return launch_status(fa::launch_bwd_dkdv(dtype, d, causal, q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N,
+    return launch_status(fa::launch_bwd_dkdv(dtype, d, causal, q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N,
                                              softmax_scale, stream));
 }
 
-fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                      const float* delta, void* dq, int B, int Hq, int Hkv, int N, int d, int causal,
-                      float softmax_scale, int dtype, hipStream_t stream) {
+fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dq, int B,
+                      int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype, hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
     if (s != FA_OK || empty) return s;
-    s = check_ptrs({q, k, v, dO}, {lse, delta}, {dq}, {});
+    s = check_ptrs({q, k, v, dO, ws}, {}, {dq}, {});
     if (s != FA_OK) return s;
-    return launch_status(fa::launch_bwd_dq(dtype, d, causal, q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N,
-                                           softmax_scale, stream));
+    return launch_status(fa::launch_bwd_dq(dtype, d, causal, q, k, v, dO, ws, dq, B, Hq, Hkv, N, softmax_scale,
+                                           stream));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N) {
     if (B <= 0 || Hq <= 0 || N <= 0) return 0;
-    return (size_t)4 * (size_t)B * (size_t)Hq * (size_t)N;
+    return (size_t)8 * (size_t)B * (size_t)Hq * (size_t)fa::ws_rows(N);
 }
 
 fa_status_t fa_quantize_fp8(const void* x_bf16, size_t n, void* x_e4m3, float* descale, hipStream_t stream) {

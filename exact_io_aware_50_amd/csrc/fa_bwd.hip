@@ -18,24 +18,34 @@
 
 namespace fa {
 
-// ------------------------------------------------------------ D = rowsum(dO*O)
+// ------------------------------------------------------------ workspace: D, LSE*log2e
+// Row r of the padded [B*Hq][Np] layout: D = sum_c dO*O and LSE*log2(e) for
+// query rows < N; D = 0 and +infinity (zero probability) for padding rows.
 template <class ET, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const typename ET::elem* __restrict__ O,
                                                         const typename ET::elem* __restrict__ dO,
-                                                        float* __restrict__ Dl, int64_t rows) {
+                                                        const float* __restrict__ LSE, float* __restrict__ WSd,
+                                                        float* __restrict__ WSl, int N, int Np, int64_t rows) {
     constexpr int TPR = D / 8, RPB = 256 / TPR;
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
     const int seg = threadIdx.x % TPR;
+    const int64_t bh = row / Np;
+    const int i = (int)(row - bh * Np);
+    const bool valid = row < rows && i < N;
     float acc = 0.f;
-    if (row < rows) {
-        const auto a = ld8<ET>(O + row * D + seg * 8);
-        const auto d = ld8<ET>(dO + row * D + seg * 8);
+    if (valid) {
+        const int64_t src = (bh * N + i) * D + seg * 8;
+        const auto a = ld8<ET>(O + src);
+        const auto d = ld8<ET>(dO + src);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf(ET::to_f32(a, e), ET::to_f32(d, e), acc);
     }
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (seg == 0 && row < rows) Dl[row] = acc;
+    if (seg == 0 && row < rows) {
+        WSd[row] = acc;
+        WSl[row] = valid ? LSE[bh * N + i] * kLog2e : INFINITY;
+    }
 }
 
 // ------------------------------------------------------------ dK, dV
@@ -53,9 +63,9 @@ template <class ET, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const typename ET::elem* __restrict__ Q, const typename ET::elem* __restrict__ K,
     const typename ET::elem* __restrict__ V, const typename ET::elem* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Dl,
+    const float* __restrict__ WSd, const float* __restrict__ WSl,
     typename ET::elem* __restrict__ dK, typename ET::elem* __restrict__ dV,
-    int Hq, int Hkv, int N, float c2, float scale) {
+    int Hq, int Hkv, int N, int Np, float c2, float scale) {
     using Cfg = KVCfg<ET, D>;
     using elem = typename ET::elem;
     using raw8 = typename ET::raw8;
@@ -117,9 +127,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
         o_nat.load(dO + base * D, N - q0, tid);
         o_tr.load(dO + base * D, N - q0, tid);
         if (tid < BMQ) {
-            const bool ok = q0 + tid < N;
-            st_l = ok ? LSE[base + tid] * kLog2e : INFINITY;
-            st_d = ok ? Dl[base + tid] : 0.f;
+            // padded workspace rows (>= N) hold +inf and 0
+            const int64_t srow = ((int64_t)b * Hq + hq) * Np + q0 + tid;
+            st_l = WSl[srow];
+            st_d = WSd[srow];
         }
     };
     auto put = [&](int stage) {
@@ -230,8 +241,8 @@ template <class ET, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(
     const typename ET::elem* __restrict__ Q, const typename ET::elem* __restrict__ K,
     const typename ET::elem* __restrict__ V, const typename ET::elem* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Dl, typename ET::elem* __restrict__ dQ,
-    int Hq, int Hkv, int N, float c2, float scale) {
+    const float* __restrict__ WSd, const float* __restrict__ WSl, typename ET::elem* __restrict__ dQ,
+    int Hq, int Hkv, int N, int Np, float c2, float scale) {
     using Cfg = QCfg<ET, D>;
     using elem = typename ET::elem;
     using raw8 = typename ET::raw8;
@@ -268,8 +279,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
         qf[s] = a;
         of[s] = c;
     }
-    const float lse2 = qrow < N ? LSE[rowbase + qrow] * kLog2e : INFINITY;
-    const float dq_d = qrow < N ? Dl[rowbase + qrow] : 0.f;
+    const int64_t srow = ((int64_t)b * Hq + h) * Np + qrow;
+    const float lse2 = qrow < N ? WSl[srow] : INFINITY;
+    const float dq_d = qrow < N ? WSd[srow] : 0.f;
 
     f32x16 dqacc[D / 32];
 #pragma unroll
@@ -360,66 +372,67 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 }
 
 template <class ET, int D>
-static hipError_t launch_delta(const void* o, const void* dO, float* delta, int B, int Hq, int N, hipStream_t st) {
+static hipError_t launch_delta(const void* o, const void* dO, const float* lse, float* ws, int B, int Hq, int N,
+                               hipStream_t st) {
     using elem = typename ET::elem;
-    const int64_t rows = (int64_t)B * Hq * N;
+    const int Np = ws_rows(N);
+    const int64_t rows = (int64_t)B * Hq * Np;
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((bwd_delta_kernel<ET, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                       (const elem*)o, (const elem*)dO, delta, rows);
+                       (const elem*)o, (const elem*)dO, lse, ws, ws + rows, N, Np, rows);
     return hipGetLastError();
 }
 
 template <class ET, int D, bool CAUSAL>
-static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                              const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale,
-                              hipStream_t st) {
+static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* ws,
+                              void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
     using elem = typename ET::elem;
     const int nkb = (N + KVCfg<ET, D>::BNK - 1) / KVCfg<ET, D>::BNK;
+    const int Np = ws_rows(N);
     hipLaunchKernelGGL((bwd_dkdv_kernel<ET, D, CAUSAL>), dim3((unsigned)((int64_t)nkb * Hkv * B)), dim3(256), 0,
-                       st, (const elem*)q, (const elem*)k, (const elem*)v, (const elem*)dO, lse, delta,
-                       (elem*)dk, (elem*)dv, Hq, Hkv, N, scale * kLog2e, scale);
+                       st, (const elem*)q, (const elem*)k, (const elem*)v, (const elem*)dO, ws,
+                       ws + (int64_t)B * Hq * Np, (elem*)dk, (elem*)dv, Hq, Hkv, N, Np, scale * kLog2e, scale);
     return hipGetLastError();
 }
 
 template <class ET, int D, bool CAUSAL>
-static hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                            const float* delta, void* dq, int B, int Hq, int Hkv, int N, float scale,
-                            hipStream_t st) {
+static hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dq,
+                            int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
     using elem = typename ET::elem;
     const int nmb = (N + QCfg<ET, D>::BM - 1) / QCfg<ET, D>::BM;
+    const int Np = ws_rows(N);
     hipLaunchKernelGGL((bwd_dq_kernel<ET, D, CAUSAL>), dim3((unsigned)((int64_t)nmb * Hq * B)), dim3(256), 0, st,
-                       (const elem*)q, (const elem*)k, (const elem*)v, (const elem*)dO, lse, delta, (elem*)dq,
-                       Hq, Hkv, N, scale * kLog2e, scale);
+                       (const elem*)q, (const elem*)k, (const elem*)v, (const elem*)dO, ws,
+                       ws + (int64_t)B * Hq * Np, (elem*)dq, Hq, Hkv, N, Np, scale * kLog2e, scale);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_delta(int dtype, int d, const void* o, const void* dO, float* delta, int B, int Hq, int N,
-                            hipStream_t st) {
-    if (dtype == 1 && d == 64) return launch_delta<BF16, 64>(o, dO, delta, B, Hq, N, st);
-    if (dtype == 1 && d == 128) return launch_delta<BF16, 128>(o, dO, delta, B, Hq, N, st);
-    if (dtype == 0 && d == 64) return launch_delta<F32, 64>(o, dO, delta, B, Hq, N, st);
-    if (dtype == 0 && d == 128) return launch_delta<F32, 128>(o, dO, delta, B, Hq, N, st);
+hipError_t launch_bwd_delta(int dtype, int d, const void* o, const void* dO, const float* lse, float* ws, int B,
+                            int Hq, int N, hipStream_t st) {
+    if (dtype == 1 && d == 64) return launch_delta<BF16, 64>(o, dO, lse, ws, B, Hq, N, st);
+    if (dtype == 1 && d == 128) return launch_delta<BF16, 128>(o, dO, lse, ws, B, Hq, N, st);
+    if (dtype == 0 && d == 64) return launch_delta<F32, 64>(o, dO, lse, ws, B, Hq, N, st);
+    if (dtype == 0 && d == 128) return launch_delta<F32, 128>(o, dO, lse, ws, B, Hq, N, st);
     return hipErrorInvalidValue;
 }
 
-#define FA_DISPATCH(FN, ...)                                                          \
+#define FA_DISPATCH(FN, ...)                                                                                  \
     if (dtype == 0 && d == 64) return causal ? FN<F32, 64, true>(__VA_ARGS__) : FN<F32, 64, false>(__VA_ARGS__);     \
     if (dtype == 0 && d == 128) return causal ? FN<F32, 128, true>(__VA_ARGS__) : FN<F32, 128, false>(__VA_ARGS__);  \
     return hipErrorInvalidValue;
 
 hipError_t launch_bwd_dkdv(int dtype, int d, int causal, const void* q, const void* k, const void* v,
-                           const void* dO, const float* lse, const float* delta, void* dk, void* dv, int B,
-                           int Hq, int Hkv, int N, float scale, hipStream_t st) {
-    if (dtype == 1)
-        return launch_bwd_dkdv_bf16(d, causal, q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N, scale, st);
-    FA_DISPATCH(launch_dkdv, q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N, scale, st)
+                           const void* dO, const float* ws, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                           float scale, hipStream_t st) {
+    if (dtype == 1) return launch_bwd_dkdv_bf16(d, causal, q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st);
+    FA_DISPATCH(launch_dkdv, q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st)
 }
 
 hipError_t launch_bwd_dq(int dtype, int d, int causal, const void* q, const void* k, const void* v,
-                         const void* dO, const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
-                         int N, float scale, hipStream_t st) {
-    if (dtype == 1) return launch_bwd_dq_bf16(d, causal, q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N, scale, st);
-    FA_DISPATCH(launch_dq, q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N, scale, st)
+                         const void* dO, const float* ws, void* dq, int B, int Hq, int Hkv, int N, float scale,
+                         hipStream_t st) {
+    if (dtype == 1) return launch_bwd_dq_bf16(d, causal, q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st);
+    FA_DISPATCH(launch_dq, q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st)
 }
 #undef FA_DISPATCH
 

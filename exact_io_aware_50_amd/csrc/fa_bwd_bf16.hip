@@ -1,10 +1,10 @@
 // bf16 backward pass (the tuned path; float32 uses the generic kernels in
 // fa_bwd.hip).  Same arithmetic as there; what changes is the mapping onto
-// gfx950: Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles go from HBM straight
-// into LDS in row-major layout, and every transposed operand (Q^T, dO^T, K^T)
-// is read with transposing LDS reads, so no tile is ever transposed through
-// registers.  Probabilities and dS are packed to bf16 by the hardware
-// converter.
+// gfx950: Q/dO (dK/dV kernel) and K/V (dQ kernel) tiles, and the per-row
+// statistics, go from HBM straight into LDS in row-major layout with several
+// tiles in flight; every transposed operand (Q^T, dO^T, K^T) is read with
+// transposing LDS reads, so no tile is transposed through registers; P and dS
+// are packed to bf16 by the hardware converter.
 //
 // FlashAttention legal glossary, backward paragraph and entry "Recomputation"
 // (P is recomputed from Q, K and the stored statistics), FlashAttention-2
@@ -15,26 +15,34 @@
 namespace fa {
 
 // ------------------------------------------------------------ dK, dV
-template <int D>
+template <int D, int NW, int NS>
 struct KVBf16Cfg {
-    static constexpr int kWaves = 4;
-    static constexpr int kThreads = 64 * kWaves;
-    static constexpr int BNK = 32 * kWaves;     // keys per workgroup (32 per wave)
-    static constexpr int BMQ = 32;              // query rows per step
-    using QT = LdsTile<BMQ, D, kWaves>;
-    static constexpr int kStage = 2 * QT::kElems;   // Q and dO
+    static constexpr int kWaves = NW;
+    static constexpr int kThreads = 64 * NW;
+    static constexpr int BNK = 32 * NW;                 // keys per workgroup (32 per wave)
+    static constexpr int BMQ = D == 128 ? 32 : 64;      // query rows per step
+    static constexpr int QB = BMQ / 32;
+    static constexpr int kStages = NS;
+    using QT = LdsTile<BMQ, D, NW>;
+    static constexpr int kStatChunks = BMQ / 2;         // 16-byte chunks of (LSE*log2e, D) per step
+    static constexpr int kStatPerWave = kStatChunks / NW;
+    static_assert(kStatChunks % NW == 0, "statistics split evenly over the waves");
+    static constexpr int kStatBytes = 8 * BMQ;
+    static constexpr int kStageBytes = 2 * QT::kBytes + kStatBytes;
+    static constexpr int kLoads = 2 * QT::kPerWave + 1;
 };
+template <int D>
+using KVBf16Tuned = KVBf16Cfg<D, 8, 4>;
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(
+template <int D, bool CAUSAL, class Cfg>
+__global__ __launch_bounds__(Cfg::kThreads, 2) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int N, float c2, float scale) {
-    using Cfg = KVBf16Cfg<D>;
+    const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int N, int Npad, float c2,
+    float scale) {
     using QT = typename Cfg::QT;
-    constexpr int BNK = Cfg::BNK, BMQ = Cfg::BMQ;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * Cfg::kStage];
-    __shared__ __attribute__((aligned(16))) float sstat[2][2][BMQ];   // [stage][lse*log2e | D][row]
+    constexpr int BNK = Cfg::BNK, BMQ = Cfg::BMQ, QB = Cfg::QB, NS = Cfg::kStages;
+    __shared__ __attribute__((aligned(1024))) char smem[NS * Cfg::kStageBytes];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -56,32 +64,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(
     const int per_head = nqt - qt0;
     const int total = G * per_head;
 
-    auto base_of = [&](int it, int& q0) {
+    // Step `it`: query head g*G + it / per_head, query block qt0 + it % per_head.
+    auto issue = [&](int it) {
         const int hq = g * G + it / per_head;
-        q0 = (qt0 + it % per_head) * BMQ;
-        return ((int64_t)b * Hq + hq) * N + q0;
-    };
-    float st_l = 0.f, st_d = 0.f;
-    auto fetch = [&](int it, int stage) {
-        int q0;
-        const int64_t base = base_of(it, q0);
-        uint16_t* s = smem + stage * Cfg::kStage;
-        QT::load(Q + base * D, N - q0, s, wave, lane);
-        QT::load(dO + base * D, N - q0, s + QT::kElems, wave, lane);
-        if (tid < BMQ) {
-            const bool ok = q0 + tid < N;
-            st_l = ok ? LSE[base + tid] * kLog2e : INFINITY;
-            st_d = ok ? Dl[base + tid] : 0.f;
+        const int q0 = (qt0 + it % per_head) * BMQ;
+        const int64_t bh = (int64_t)b * Hq + hq;
+        const char* st = smem + (it % NS) * Cfg::kStageBytes;
+        QT::load(Q + (bh * N + q0) * D, N - q0, (const uint16_t*)st, wave, lane);
+        QT::load(dO + (bh * N + q0) * D, N - q0, (const uint16_t*)(st + QT::kBytes), wave, lane);
+        // statistics: chunk c < BMQ/4 holds LSE*log2e rows q0+4c.., the rest D rows
+        const int c = wave * Cfg::kStatPerWave + lane;
+        if (lane < Cfg::kStatPerWave) {
+            const float* src = c < BMQ / 4 ? WSl + bh * Npad + q0 + 4 * c : WSd + bh * Npad + q0 + 4 * (c - BMQ / 4);
+            dma16(src, lds_addr(st + 2 * QT::kBytes) + 16 * wave * Cfg::kStatPerWave);
         }
     };
-    auto put_stats = [&](int stage) {
-        if (tid < BMQ) {
-            sstat[stage][0][tid] = st_l;
-            sstat[stage][1][tid] = st_d;
-        }
-    };
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+        if (t < total) issue(t);
 
-    fetch(0, 0);
     u32x4 kf[D / 16], vf[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
@@ -93,62 +94,66 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(
         kf[s] = a;
         vf[s] = c;
     }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        settle(kf[s]);
+        settle(vf[s]);
+    }
     f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
         dkacc[i] = zero16();
         dvacc[i] = zero16();
     }
-    put_stats(0);
-    wait_dma();
-    __syncthreads();
 
     for (int it = 0; it < total; ++it) {
-        int q0;
-        base_of(it, q0);
-        const int stg = it & 1;
-        if (it + 1 < total) fetch(it + 1, stg ^ 1);
-        const uint16_t* Qs = smem + stg * Cfg::kStage;
-        const uint16_t* dOs = Qs + QT::kElems;
+        const int q0 = (qt0 + it % per_head) * BMQ;
+        pipe_wait<NS, Cfg::kLoads>(it, total);
+        lds_barrier();
+        if (it + NS - 1 < total) issue(it + NS - 1);
+        const char* st = smem + (it % NS) * Cfg::kStageBytes;
+        const uint16_t* Qs = (const uint16_t*)st;
+        const uint16_t* dOs = (const uint16_t*)(st + QT::kBytes);
+        const float* sl = (const float*)(st + 2 * QT::kBytes);   // LSE*log2e [BMQ], then D [BMQ]
 
         if (!(CAUSAL && q0 + BMQ - 1 < kw)) {
-            // S = Q K^T and dP = dO V^T: rows = queries, columns = this wave's keys
-            f32x16 sacc = zero16(), dpacc = zero16();
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                sacc = mma_bf16(QT::row8(Qs, l32, 2 * s + hh), kf[s], sacc);
-                dpacc = mma_bf16(QT::row8(dOs, l32, 2 * s + hh), vf[s], dpacc);
-            }
             const bool need_mask = CAUSAL && kw + 31 > q0;
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int rb = 8 * gq + 4 * hh;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sstat[stg][0][rb]);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sstat[stg][1][rb]);
+            for (int qb = 0; qb < QB; ++qb) {
+                // S = Q K^T and dP = dO V^T: rows = queries, columns = this wave's keys
+                f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * gq + j;
-                    float p = fast_exp2(fmaf(sacc[r], c2, -l4[j]));
-                    if (need_mask && krow > q0 + rb + j) p = 0.f;
-                    sacc[r] = p;
-                    dpacc[r] = p * (dpacc[r] - d4[j]);
+                for (int s = 0; s < D / 16; ++s) {
+                    sacc = mma_bf16(QT::row8(Qs, 32 * qb + l32, 2 * s + hh), kf[s], sacc);
+                    dpacc = mma_bf16(QT::row8(dOs, 32 * qb + l32, 2 * s + hh), vf[s], dpacc);
                 }
-            }
-            // dV^T += dO^T P ;  dK^T += Q^T dS
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const u32x4 pb = pack_bf16x8(sacc, 8 * t);
-                const u32x4 sb = pack_bf16x8(dpacc, 8 * t);
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int rb = 32 * qb + 8 * gq + 4 * hh;
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + rb);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + BMQ + rb);
 #pragma unroll
-                for (int ct = 0; ct < D / 32; ++ct) {
-                    dvacc[ct] = mma_bf16(QT::tr8(dOs, 16 * t, 32 * ct, lane), pb, dvacc[ct]);
-                    dkacc[ct] = mma_bf16(QT::tr8(Qs, 16 * t, 32 * ct, lane), sb, dkacc[ct]);
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 4 * gq + j;
+                        float p = fast_exp2(fmaf(sacc[r], c2, -l4[j]));
+                        if (need_mask && krow > q0 + rb + j) p = 0.f;
+                        sacc[r] = p;
+                        dpacc[r] = p * (dpacc[r] - d4[j]);
+                    }
+                }
+                // dV^T += dO^T P ;  dK^T += Q^T dS
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const u32x4 pb = pack_bf16x8(sacc, 8 * t);
+                    const u32x4 sb = pack_bf16x8(dpacc, 8 * t);
+#pragma unroll
+                    for (int ct = 0; ct < D / 32; ++ct) {
+                        dvacc[ct] = mma_bf16(QT::tr8(dOs, 32 * qb + 16 * t, 32 * ct, lane), pb, dvacc[ct]);
+                        dkacc[ct] = mma_bf16(QT::tr8(Qs, 32 * qb + 16 * t, 32 * ct, lane), sb, dkacc[ct]);
+                    }
                 }
             }
         }
-        if (it + 1 < total) put_stats(stg ^ 1);
-        wait_dma();
-        __syncthreads();
     }
 
     if (krow < N) {
@@ -171,27 +176,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(
 }
 
 // ------------------------------------------------------------ dQ
-template <int D>
+template <int D, int NW, int NS>
 struct QBf16Cfg {
-    static constexpr int kWaves = 4;
-    static constexpr int kThreads = 64 * kWaves;
-    static constexpr int BM = 32 * kWaves;      // query rows per workgroup
+    static constexpr int kWaves = NW;
+    static constexpr int kThreads = 64 * NW;
+    static constexpr int BM = 32 * NW;          // query rows per workgroup
     static constexpr int BNK = 64;              // keys per tile
-    using KT = LdsTile<BNK, D, kWaves>;   // read as rows and transposed
-    using VT = LdsTile<BNK, D, kWaves>;  // read as rows
+    static constexpr int kStages = NS;
+    using KT = LdsTile<BNK, D, NW>;             // read as rows and transposed
+    using VT = LdsTile<BNK, D, NW>;             // read as rows
     static constexpr int kStage = KT::kElems + VT::kElems;
+    static constexpr int kLoads = KT::kPerWave + VT::kPerWave;
 };
+template <int D>
+using QBf16Tuned = QBf16Cfg<D, 8, 3>;
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
+template <int D, bool CAUSAL, class Cfg>
+__global__ __launch_bounds__(Cfg::kThreads, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    uint16_t* __restrict__ dQ, int Hq, int Hkv, int N, float c2, float scale) {
-    using Cfg = QBf16Cfg<D>;
+    const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
+    uint16_t* __restrict__ dQ, int Hq, int Hkv, int N, int Npad, float c2, float scale) {
     using KT = typename Cfg::KT;
     using VT = typename Cfg::VT;
-    constexpr int BM = Cfg::BM, BNK = Cfg::BNK;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * Cfg::kStage];
+    constexpr int BM = Cfg::BM, BNK = Cfg::BNK, NS = Cfg::kStages;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * Cfg::kStage];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -212,8 +220,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const int kend = CAUSAL ? min(N, q0 + BM) : N;
     const int ntiles = (kend + BNK - 1) / BNK;
 
-    KT::load(Kg, N, smem, wave, lane);
-    VT::load(Vg, N, smem + KT::kElems, wave, lane);
+    auto issue = [&](int t) {
+        const uint16_t* st = smem + (t % NS) * Cfg::kStage;
+        KT::load(Kg + (int64_t)t * BNK * D, N - t * BNK, st, wave, lane);
+        VT::load(Vg + (int64_t)t * BNK * D, N - t * BNK, st + KT::kElems, wave, lane);
+    };
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+        if (t < ntiles) issue(t);
 
     u32x4 qf[D / 16], of[D / 16];
 #pragma unroll
@@ -226,23 +240,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         qf[s] = a;
         of[s] = c;
     }
-    const float lse2 = qrow < N ? LSE[rowbase + qrow] * kLog2e : INFINITY;
-    const float dq_d = qrow < N ? Dl[rowbase + qrow] : 0.f;
+    const int64_t srow = ((int64_t)b * Hq + h) * Npad + qrow;
+    const float lse2 = qrow < N ? WSl[srow] : INFINITY;
+    const float dq_d = qrow < N ? WSd[srow] : 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        settle(qf[s]);
+        settle(of[s]);
+    }
+    settle(lse2);
+    settle(dq_d);
 
     f32x16 dqacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) dqacc[i] = zero16();
-    wait_dma();
-    __syncthreads();
 
     for (int j = 0; j < ntiles; ++j) {
         const int k0 = j * BNK;
-        if (j + 1 < ntiles) {
-            uint16_t* nxt = smem + ((j + 1) & 1) * Cfg::kStage;
-            KT::load(Kg + (int64_t)(k0 + BNK) * D, N - (k0 + BNK), nxt, wave, lane);
-            VT::load(Vg + (int64_t)(k0 + BNK) * D, N - (k0 + BNK), nxt + KT::kElems, wave, lane);
-        }
-        const uint16_t* Ks = smem + (j & 1) * Cfg::kStage;
+        pipe_wait<NS, Cfg::kLoads>(j, ntiles);
+        lds_barrier();
+        if (j + NS - 1 < ntiles) issue(j + NS - 1);
+        const uint16_t* Ks = smem + (j % NS) * Cfg::kStage;
         const uint16_t* Vs = Ks + KT::kElems;
 
         if (!(CAUSAL && k0 > qw + 31)) {
@@ -283,8 +301,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
                         dqacc[ct] = mma_bf16(KT::tr8(Ks, 32 * kb + 16 * t, 32 * ct, lane), sb, dqacc[ct]);
                 }
         }
-        wait_dma();
-        __syncthreads();
     }
 
     if (qrow < N) {
@@ -302,34 +318,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 }
 
 template <int D, bool CAUSAL>
-static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                              const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale,
-                              hipStream_t st) {
-    using Cfg = KVBf16Cfg<D>;
+static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* ws,
+                              void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
+    using Cfg = KVBf16Tuned<D>;
     const int nkb = (N + Cfg::BNK - 1) / Cfg::BNK;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)nkb * Hkv * B)),
+    const int Np = ws_rows(N);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, Cfg>), dim3((unsigned)((int64_t)nkb * Hkv * B)),
                        dim3(Cfg::kThreads), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dO, lse, delta, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, N, scale * kLog2e,
-                       scale);
+                       (const uint16_t*)dO, ws, ws + (int64_t)B * Hq * Np, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv,
+                       N, Np, scale * kLog2e, scale);
     return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
-static hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                            const float* delta, void* dq, int B, int Hq, int Hkv, int N, float scale,
-                            hipStream_t st) {
-    using Cfg = QBf16Cfg<D>;
+static hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dq,
+                            int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
+    using Cfg = QBf16Tuned<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)nmb * Hq * B)),
+    const int Np = ws_rows(N);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, Cfg>), dim3((unsigned)((int64_t)nmb * Hq * B)),
                        dim3(Cfg::kThreads), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dO, lse, delta, (uint16_t*)dq, Hq, Hkv, N, scale * kLog2e, scale);
+                       (const uint16_t*)dO, ws, ws + (int64_t)B * Hq * Np, (uint16_t*)dq, Hq, Hkv, N, Np,
+                       scale * kLog2e, scale);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv_bf16(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
-                                const float* lse, const float* delta, void* dk, void* dv, int B, int Hq, int Hkv,
-                                int N, float scale, hipStream_t st) {
-#define ARGS q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N, scale, st
+                                const float* ws, void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale,
+                                hipStream_t st) {
+#define ARGS q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st
     if (d == 64) return causal ? launch_dkdv<64, true>(ARGS) : launch_dkdv<64, false>(ARGS);
     if (d == 128) return causal ? launch_dkdv<128, true>(ARGS) : launch_dkdv<128, false>(ARGS);
 #undef ARGS
@@ -337,9 +354,8 @@ hipError_t launch_bwd_dkdv_bf16(int d, int causal, const void* q, const void* k,
 }
 
 hipError_t launch_bwd_dq_bf16(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
-                              const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv, int N,
-                              float scale, hipStream_t st) {
-#define ARGS q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N, scale, st
+                              const float* ws, void* dq, int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
+#define ARGS q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st
     if (d == 64) return causal ? launch_dq<64, true>(ARGS) : launch_dq<64, false>(ARGS);
     if (d == 128) return causal ? launch_dq<128, true>(ARGS) : launch_dq<128, false>(ARGS);
 #undef ARGS

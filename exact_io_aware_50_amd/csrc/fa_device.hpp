@@ -312,7 +312,54 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// ----------------------------------------------------------------------------
+// Direct global -> LDS loads are issued from inline assembly, so the compiler
+// does not see their LDS writes and never inserts its own conservative
+// "wait for every outstanding load" before an LDS read.  Completion is managed
+// explicitly: a tile is ready once this wave's loads for it are done
+// (s_waitcnt vmcnt) and every wave has passed the next s_barrier.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+// 16 bytes per lane from `gptr` to LDS address m0 + 16 * lane (m0 must be
+// wave-uniform; it is moved to a scalar register here).  M0 is written inside
+// the statement; these kernels use M0 for nothing else.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(m0))
+                 : "memory");
+}
+// Make the compiler finish its own pending loads into these registers here
+// (an empty statement that reads them), so that its waits are not placed in a
+// later pipelined loop, where they would also drain the asm-issued loads.
+__device__ __forceinline__ void settle(const u32x4& x) { asm volatile("" : : "v"(x)); }
+__device__ __forceinline__ void settle(float x) { asm volatile("" : : "v"(x)); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// Workgroup barrier that does not drain outstanding global loads; LDS reads
+// of the previous tile are completed first.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
+
+// Wait until this wave's loads for tile j have landed, with a pipeline of NS
+// stages (tiles j+1 .. j+NS-2, when they exist, may still be in flight) and L
+// load instructions per wave per tile.
+template <int NS, int L>
+__device__ __forceinline__ void pipe_wait(int j, int total) {
+    static_assert(NS >= 2 && NS <= 4 && L * (NS - 2) <= 63, "vmcnt range");
+    const int later = total - 1 - j;
+    if constexpr (NS == 2) {
+        wait_vm<0>();
+    } else if constexpr (NS == 3) {
+        if (later >= 1) wait_vm<L>(); else wait_vm<0>();
+    } else {
+        if (later >= 2) wait_vm<2 * L>(); else if (later == 1) wait_vm<L>(); else wait_vm<0>();
+    }
+}
 
 // Tile layout in LDS ("row groups"): rows are taken in groups of RG, where RG
 // rows hold exactly 64 chunks (1 KB, the bytes one wave moves with one direct
@@ -340,16 +387,16 @@ struct LdsTile {
     // Direct global -> LDS copy of rows [0, ROWS) of `src` (row stride COLS).
     // Rows at or past rows_valid re-read the last valid row: finite values the
     // caller masks out.
-    static __device__ __forceinline__ void load(const uint16_t* src, int rows_valid, uint16_t* tile, int wave,
-                                                int lane) {
+    static __device__ __forceinline__ void load(const uint16_t* src, int rows_valid, const uint16_t* tile,
+                                                int wave, int lane) {
         const int c = lane / RG, r = lane % RG;
+        const uint32_t base = lds_addr(tile);
 #pragma unroll
         for (int i = 0; i < kPerWave; ++i) {
             const int grp = i * NW + wave;
             const int row = grp * RG + r;
             const int grow = row < rows_valid ? row : rows_valid - 1;
-            __builtin_amdgcn_global_load_lds((gbl_void*)(src + (int64_t)grow * COLS + c * 8),
-                                             (lds_void*)((char*)tile + grp * RGS), 16, 0, 0);
+            dma16(src + (int64_t)grow * COLS + c * 8, base + grp * RGS);
         }
     }
     // Byte offset of (row, chunk).

@@ -19,24 +19,26 @@ hipError_t launch_fwd_fp8(int d, int causal, const void* q, const void* k, const
                           void* o, float* lse, const float* descale, int B, int Hq, int Hkv, int N,
                           float scale, hipStream_t st);
 
-hipError_t launch_bwd_delta(int dtype, int d, const void* o, const void* dO, float* delta, int B, int Hq, int N,
-                            hipStream_t st);
+// Rows per (batch, head) in the backward workspace: N rounded up to 64.
+inline int ws_rows(int N) { return (N + 63) / 64 * 64; }
+
+hipError_t launch_bwd_delta(int dtype, int d, const void* o, const void* dO, const float* lse, float* ws, int B,
+                            int Hq, int N, hipStream_t st);
 
 hipError_t launch_bwd_dkdv(int dtype, int d, int causal, const void* q, const void* k, const void* v,
-                           const void* dO, const float* lse, const float* delta, void* dk, void* dv, int B,
-                           int Hq, int Hkv, int N, float scale, hipStream_t st);
+                           const void* dO, const float* ws, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                           float scale, hipStream_t st);
 
 hipError_t launch_bwd_dq(int dtype, int d, int causal, const void* q, const void* k, const void* v,
-                         const void* dO, const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
-                         int N, float scale, hipStream_t st);
+                         const void* dO, const float* ws, void* dq, int B, int Hq, int Hkv, int N, float scale,
+                         hipStream_t st);
 
 hipError_t launch_bwd_dkdv_bf16(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
-                                const float* lse, const float* delta, void* dk, void* dv, int B, int Hq, int Hkv,
-                                int N, float scale, hipStream_t st);
+                                const float* ws, void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale,
+                                hipStream_t st);
 
 hipError_t launch_bwd_dq_bf16(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
-                              const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv, int N,
-                              float scale, hipStream_t st);
+                              const float* ws, void* dq, int B, int Hq, int Hkv, int N, float scale, hipStream_t st);
 
 hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
 

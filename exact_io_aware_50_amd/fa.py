@@ -33,11 +33,11 @@ _lib.fa_fwd.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, 
 _lib.fa_fwd.restype = _i
 _lib.fa_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_bwd.restype = _i
-_lib.fa_bwd_delta.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.fa_bwd_delta.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.fa_bwd_delta.restype = _i
-_lib.fa_bwd_dkdv.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
+_lib.fa_bwd_dkdv.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_bwd_dkdv.restype = _i
-_lib.fa_bwd_dq.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
+_lib.fa_bwd_dq.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_bwd_dq.restype = _i
 _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -71,17 +71,17 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal, 
                        float(softmax_scale), dtype, stream)
 
 
-def fa_bwd_delta(o, dO, delta, B, Hq, N, d, dtype, stream) -> int:
-    return _lib.fa_bwd_delta(o, dO, delta, B, Hq, N, d, dtype, stream)
+def fa_bwd_delta(o, dO, lse, ws, B, Hq, N, d, dtype, stream) -> int:
+    return _lib.fa_bwd_delta(o, dO, lse, ws, B, Hq, N, d, dtype, stream)
 
 
-def fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N, d, causal, softmax_scale, dtype, stream) -> int:
-    return _lib.fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, B, Hq, Hkv, N, d, int(causal), float(softmax_scale),
+def fa_bwd_dkdv(q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, d, causal, softmax_scale, dtype, stream) -> int:
+    return _lib.fa_bwd_dkdv(q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, d, int(causal), float(softmax_scale),
                             dtype, stream)
 
 
-def fa_bwd_dq(q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N, d, causal, softmax_scale, dtype, stream) -> int:
-    return _lib.fa_bwd_dq(q, k, v, dO, lse, delta, dq, B, Hq, Hkv, N, d, int(causal), float(softmax_scale),
+def fa_bwd_dq(q, k, v, dO, ws, dq, B, Hq, Hkv, N, d, causal, softmax_scale, dtype, stream) -> int:
+    return _lib.fa_bwd_dq(q, k, v, dO, ws, dq, B, Hq, Hkv, N, d, int(causal), float(softmax_scale),
                           dtype, stream)
 
 
@@ -157,7 +157,10 @@ def fwd(q, k, v, causal: bool, scale: float, descale=None, stream=None):
 
 
 def bwd(q, k, v, o, do, lse, causal: bool, scale: float, stream=None, workspace=None):
-    """(dq, dk, dv, delta) for the forward's inputs and outputs and the output gradient do."""
+    """(dq, dk, dv, workspace) for the forward's inputs and outputs and the output gradient do.
+
+    The workspace (float32) holds D = rowsum(dO * O) for [B*Hq][Np] rows, then
+    LSE*log2(e) for the same rows; Np = N rounded up to 64."""
     torch = _torch()
     B, Hq, Hkv, N, d = _shape(q, k)
     code = _dtype_code(q)
@@ -165,7 +168,7 @@ def bwd(q, k, v, o, do, lse, causal: bool, scale: float, stream=None, workspace=
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     if workspace is None:
-        workspace = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+        workspace = torch.empty(fa_bwd_workspace_bytes(B, Hq, N) // 4, dtype=torch.float32, device=q.device)
     _check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, d, causal,
                   scale, code, _stream_handle(stream)), "fa_bwd")

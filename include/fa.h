@@ -90,14 +90,15 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v,
  * paragraph and entry "Recomputation" (only the softmax statistics are kept;
  * S and P are recomputed on chip); FlashAttention-2 paragraph (the backward
  * is parallel over the key (column) blocks, without atomic adds).
- * Three kernels run in order on `stream`: D = rowsum(dO * O) into `delta_ws`,
- * then dK/dV (one workgroup per key block and K/V head, looping over the query
- * heads of its group) and dQ (one workgroup per query block and query head).
+ * Three kernels run in order on `stream`: D = rowsum(dO * O) and LSE*log2(e)
+ * into `delta_ws`, then dK/dV (one workgroup per key block and K/V head,
+ * looping over the query heads of its group) and dQ (one workgroup per query
+ * block and query head).
  *   q, k, v, o, dO, lse : as produced/consumed by fa_fwd (same dtype, F32 or
  *                         BF16 only)
  *   dq [B,Hq,N,d], dk, dv [B,Hkv,N,d] : outputs, overwritten (not accumulated)
- *   delta_ws : caller-owned device workspace of fa_bwd_workspace_bytes() bytes;
- *              holds D on return
+ *   delta_ws : caller-owned device workspace of fa_bwd_workspace_bytes() bytes,
+ *              16-byte aligned; see fa_bwd_workspace_bytes for its contents
  */
 fa_status_t fa_bwd(const void* q, const void* k, const void* v,
                    const void* o, const void* dO, const float* lse,
@@ -109,36 +110,43 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v,
 
 /*
  * The three stages of fa_bwd as separate calls, for callers that schedule or
- * time them one by one.  Same arguments, validation and layouts as fa_bwd;
- * fa_bwd_dkdv and fa_bwd_dq read the D that fa_bwd_delta wrote into `delta`,
- * and do not depend on each other.
- *   fa_bwd_delta : D[b,h,i] = sum_c dO[b,h,i,c] * O[b,h,i,c] in float32 (the
- *                  row term of the softmax gradient: sum_j P_ij dP_ij equals it)
- *   fa_bwd_dkdv  : dK, dV, parallel over key blocks ("FlashAttention" legal
- *                  glossary, FlashAttention-2 paragraph: column-parallel
- *                  backward without atomic adds); a workgroup owns one key
- *                  block of one K/V head and sums over its group's query heads
- *   fa_bwd_dq    : dQ, parallel over query blocks
+ * time them one by one; fa_bwd is exactly these three in order.  Same
+ * validation, dtypes and tensor layouts as fa_bwd.
+ *   fa_bwd_delta : fills the workspace `ws` from O, dO and LSE: the row term
+ *                  of the softmax gradient D[b,h,i] = sum_c dO[b,h,i,c] O[b,h,i,c]
+ *                  (which equals sum_j P_ij dP_ij) and LSE[b,h,i] * log2(e)
+ *   fa_bwd_dkdv  : dK, dV from the workspace, parallel over key blocks
+ *                  ("FlashAttention" legal glossary, FlashAttention-2
+ *                  paragraph: column-parallel backward without atomic adds);
+ *                  a workgroup owns one key block of one K/V head and sums
+ *                  over its group's query heads
+ *   fa_bwd_dq    : dQ from the workspace, parallel over query blocks
+ * fa_bwd_dkdv and fa_bwd_dq only read `ws` and do not depend on each other.
  */
-fa_status_t fa_bwd_delta(const void* o, const void* dO, float* delta,
+fa_status_t fa_bwd_delta(const void* o, const void* dO, const float* lse, float* ws,
                          int B, int Hq, int N, int d, int dtype,
                          hipStream_t stream);
 
 fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v,
-                        const void* dO, const float* lse, const float* delta,
+                        const void* dO, const float* ws,
                         void* dk, void* dv,
                         int B, int Hq, int Hkv, int N, int d,
                         int causal, float softmax_scale, int dtype,
                         hipStream_t stream);
 
 fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v,
-                      const void* dO, const float* lse, const float* delta,
+                      const void* dO, const float* ws,
                       void* dq,
                       int B, int Hq, int Hkv, int N, int d,
                       int causal, float softmax_scale, int dtype,
                       hipStream_t stream);
 
-/* Bytes of the fa_bwd workspace: 4 * B * Hq * N (0 for an empty problem). */
+/*
+ * Bytes of the backward workspace: 8 * B * Hq * Np with Np = N rounded up to
+ * a multiple of 64 (0 for an empty problem).  Layout: float32 D[B*Hq][Np]
+ * followed by float32 LSE*log2(e)[B*Hq][Np]; rows i >= N hold D = 0 and
+ * +infinity, so padded query rows carry zero probability.
+ */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N);
 
 /*
