@@ -127,16 +127,20 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void bwd_dkdv_bf16_kernel(
                     sacc = mma_bf16(QT::row8(Qs, 32 * qb + l32, 2 * s + hh), kf[s], sacc);
                     dpacc = mma_bf16(QT::row8(dOs, 32 * qb + l32, 2 * s + hh), vf[s], dpacc);
                 }
+                // P from the stored statistics.  Causal: key krow is hidden from
+                // query q0 + 32*qb + row(r) iff delta > 8*(r/4) + r%4, with
+                // delta = krow - q0 - 32*qb - 4*hh (forced below every row
+                // when the block needs no mask): one compare and one select
+                const int delta = need_mask ? krow - q0 - 32 * qb - 4 * hh : -64;
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    const int rb = 32 * qb + 8 * gq + 4 * hh;
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + rb);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + BMQ + rb);
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 32 * qb + 8 * gq + 4 * hh);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + BMQ + 32 * qb + 8 * gq + 4 * hh);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int r = 4 * gq + j;
                         float p = fast_exp2(fmaf(sacc[r], c2, -l4[j]));
-                        if (need_mask && krow > q0 + rb + j) p = 0.f;
+                        if (CAUSAL && delta > 8 * gq + j) p = 0.f;
                         sacc[r] = p;
                         dpacc[r] = p * (dpacc[r] - d4[j]);
                     }
@@ -278,18 +282,25 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void bwd_dq_bf16_kernel(
                     sacc[kb] = mma_bf16(KT::row8(Ks, 32 * kb + l32, 2 * s + hh), qf[s], sacc[kb]);
                     dpacc[kb] = mma_bf16(VT::row8(Vs, 32 * kb + l32, 2 * s + hh), of[s], dpacc[kb]);
                 }
-            const bool need_mask = (CAUSAL && k0 + BNK - 1 > qw) || (k0 + BNK > N);
+            // P from the stored statistics; keys after the query (causal) or
+            // past the end are zeroed in one wave-uniform branch
 #pragma unroll
             for (int kb = 0; kb < BNK / 32; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(sacc[kb][r], c2, -lse2));
-                    if (need_mask) {
+                for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c2, -lse2));
+            if ((CAUSAL && k0 + BNK - 1 > qw) || (k0 + BNK > N)) {
+#pragma unroll
+                for (int kb = 0; kb < BNK / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
                         const int key = k0 + 32 * kb + acc_row(r, hh);
-                        if ((CAUSAL && key > qrow) || key >= N) p = 0.f;
+                        if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r] = 0.f;
                     }
-                    dpacc[kb][r] = p * (dpacc[kb][r] - dq_d);
-                }
+            }
+#pragma unroll
+            for (int kb = 0; kb < BNK / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dpacc[kb][r] = sacc[kb][r] * (dpacc[kb][r] - dq_d);
             // dQ^T += K^T dS^T
 #pragma unroll
             for (int kb = 0; kb < BNK / 32; ++kb)
