@@ -331,6 +331,20 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t m0) {
                  : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(m0))
                  : "memory");
 }
+// Same copy from a wave-uniform base plus a 32-bit per-lane byte offset (the
+// scalar-base form of the instruction: no per-lane 64-bit address arithmetic).
+// (readfirstlane returns int: each half goes through uint32_t before it is
+// widened, or the low half would be sign-extended into the high one.)
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t m0) {
+    const uint64_t p = (uint64_t)(uintptr_t)sbase;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+    const uint64_t ps = ((uint64_t)hi << 32) | (uint64_t)lo;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(ps), "s"(__builtin_amdgcn_readfirstlane(m0))
+                 : "memory");
+}
 // Make the compiler finish its own pending loads into these registers here
 // (an empty statement that reads them), so that its waits are not placed in a
 // later pipelined loop, where they would also drain the asm-issued loads.

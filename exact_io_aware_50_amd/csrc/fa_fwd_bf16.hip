@@ -6,8 +6,8 @@
 // fewer non-matmul operations).  What differs from the pages' CUDA design is
 // how the same steps map onto gfx950:
 //  - K and V tiles go from HBM straight into LDS (global_load_lds, no staging
-//    registers) in their global row-major layout, several tiles in flight,
-//    one barrier per tile;
+//    registers) in their global row-major layout, four tiles resident or in
+//    flight;
 //  - S^T = K_j Q^T puts keys down the accumulator rows, so each lane owns one
 //    query and the row max / row sum need one cross-half exchange
 //    (v_permlane32_swap) per tile;
@@ -20,47 +20,74 @@
 //    stale max.  Both readings give the same softmax: exp2(s - m) / l is
 //    invariant to the reference m, and the stale reference bounds each
 //    exponential by 2^8, far from float overflow.
+//
+// Schedule ("ping-pong").  A gfx950 SIMD runs the matrix instructions of one
+// wave and the vector instructions of another side by side, but a single wave
+// issues a vector instruction only about every 8 cycles, so a wave that
+// interleaves its own exponentials with its own products leaves one of the
+// two units idle much of the time.  Each wave therefore alternates two phases:
+//   G(t): S_t = K_t Q^T and O += P_{t-1} V_{t-1}   (32 products at d = 128)
+//   X(t): mask, row max, rescale, P_t = exp2(...), pack, row sum (vector only)
+// and the workgroup's two wave groups (waves w and w+4 share a SIMD) run one
+// phase apart with a barrier after every phase: on each SIMD one wave feeds
+// the matrix core while the other does the softmax of its previous tile.
+// Inside G the LDS fragment reads are scheduled about d/16 fragments ahead of
+// the products that consume them.
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
 
-template <int D, int NW, int QB, int BN_, int NS, int MINW>
+template <int D>
 struct FwdBf16Cfg {
-    static constexpr int kWaves = NW;
-    static constexpr int kThreads = 64 * NW;
-    static constexpr int kQB = QB;                    // 32-row query blocks per wave
-    static constexpr int BM = 32 * QB * NW;           // query rows per workgroup
-    static constexpr int BN = BN_;                    // keys per K/V tile
-    static constexpr int kStages = NS;                // K/V tiles resident or in flight
-    static constexpr int kMinWaves = MINW;            // occupancy target (waves per SIMD)
-    using KT = LdsTile<BN, D, NW>;                    // read as rows
-    using VT = LdsTile<BN, D, NW>;                    // read transposed
-    static constexpr int kStage = KT::kElems + VT::kElems;   // elements per stage
-    static constexpr int kLoads = KT::kPerWave + VT::kPerWave;
+    static constexpr int kWaves = 8;                  // two groups of four, one wave of each per SIMD
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int BM = 32 * kWaves;            // query rows per workgroup (32 per wave)
+    static constexpr int BN = 64;                     // keys per K/V tile
+    static constexpr int kStages = 4;                 // K/V tiles resident or in flight
+    using KT = LdsTile<BN, D, kWaves>;                // K read as rows, V read transposed
+    static constexpr int kStage = 2 * KT::kElems;     // elements per stage (K then V)
+    static constexpr int kLoads = 2 * KT::kPerWave;   // direct loads per wave per tile
     static constexpr float kTau = 8.0f;               // log2 slack before the max is moved
 };
 
-// Tuned shape (measured on MI355X at B=4, H=32, N=4096, d=128, causal): 8 waves
-// of 32 query rows share each K/V tile, 64-key tiles, two waves per SIMD;
-// four stages: the tile being finished (V), the next one (K) and two in
-// flight.  Two 32-row blocks per wave (each K/V fragment read feeding two
-// products) needs one wave per SIMD and measured slower.
+// Order of one G phase for the instruction scheduler: L = d/16 K fragments
+// read ahead of the score products, then V^T fragments (two reads each) about
+// L fragments ahead of theirs.
 template <int D>
-using FwdBf16Tuned = FwdBf16Cfg<D, 8, 1, 64, 4, 2>;
+__device__ __forceinline__ void sched_gemm_phase() {
+    constexpr int L = D / 16;
+#pragma unroll
+    for (int i = 0; i < L; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // LDS read
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * L; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
 
-template <int D, bool CAUSAL, class Cfg>
-__global__ __launch_bounds__(Cfg::kThreads, Cfg::kMinWaves) void fwd_bf16_kernel(
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, float c2) {
+    using Cfg = FwdBf16Cfg<D>;
     using KT = typename Cfg::KT;
-    using VT = typename Cfg::VT;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::kStages, QB = Cfg::kQB;
-    constexpr int KB = BN / 32;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * Cfg::kStage];
+    constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::kStages, KB = BN / 32;
+    constexpr int kStage = Cfg::kStage, kLoads = Cfg::kLoads;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * kStage];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: phase branches stay scalar
     const int l32 = lane & 31, hh = lane >> 5;
+    const int grp = wave >> 2;                                   // waves w and w+4 share a SIMD
 
     const int nmb = (N + BM - 1) / BM;
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -73,197 +100,219 @@ __global__ __launch_bounds__(Cfg::kThreads, Cfg::kMinWaves) void fwd_bf16_kernel
     const uint16_t* Vh = V + ((int64_t)b * Hkv + g) * N * D;
 
     const int q0 = mb * BM;
-    const int qw = q0 + 32 * QB * wave;               // first query row of this wave
-    int qrow[QB];                                     // this lane's query row in each block
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) qrow[qb] = qw + 32 * qb + l32;
-
+    const int qw = q0 + 32 * wave;                    // first query row of this wave
+    const int qrow = qw + l32;                        // this lane's query row
     const int kend = CAUSAL ? min(N, q0 + BM) : N;
-    const int ntiles = (kend + BN - 1) / BN;
+    const int ntiles = (kend + BN - 1) / BN;          // tiles of the workgroup
+    const int ntw = qw >= N ? 0 : CAUSAL ? (min(N, qw + 32) + BN - 1) / BN : ntiles;   // tiles of this wave
 
-    // the first NS-1 K/V tiles go in flight while Q is fetched
-    auto issue = [&](int t) {
-        const uint16_t* st = smem + (t % NS) * Cfg::kStage;
-        KT::load(Kh + (int64_t)t * BN * D, N - t * BN, st, wave, lane);
-        VT::load(Vh + (int64_t)t * BN * D, N - t * BN, st + KT::kElems, wave, lane);
-    };
+    // ---- direct loads: this wave's row groups of a K/V tile, as byte offsets
+    // from the tile's first row (rows past the end re-read the last row)
+    uint32_t voff[KT::kPerWave];
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t)
+    for (int i = 0; i < KT::kPerWave; ++i) {
+        const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
+        voff[i] = (uint32_t)(row * D + (lane / KT::RG) * 8) * 2u;
+    }
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const uint32_t st = lds_addr(smem + (t % NS) * kStage);
+        const uint16_t* kb = Kh + (int64_t)t * BN * D;
+        const uint16_t* vb = Vh + (int64_t)t * BN * D;
+        const int rows_valid = N - t * BN;
+        if (rows_valid >= BN) {
+#pragma unroll
+            for (int i = 0; i < KT::kPerWave; ++i) dma16s(kb, voff[i], st + (i * NW + wave) * KT::RGS);
+#pragma unroll
+            for (int i = 0; i < KT::kPerWave; ++i) dma16s(vb, voff[i], st + KT::kBytes + (i * NW + wave) * KT::RGS);
+        } else {
+#pragma unroll
+            for (int i = 0; i < KT::kPerWave; ++i) {
+                const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
+                const int grow = row < rows_valid ? row : rows_valid - 1;
+                const uint32_t off = (uint32_t)(grow * D + (lane / KT::RG) * 8) * 2u;
+                dma16s(kb, off, st + (i * NW + wave) * KT::RGS);
+                dma16s(vb, off, st + KT::kBytes + (i * NW + wave) * KT::RGS);
+            }
+        }
+    };
+    // the first NS tiles go in flight while Q is fetched
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
         if (t < ntiles) issue(t);
 
-    u32x4 qf[QB][D / 16];
+    u32x4 qf[D / 16];                                 // Q block as B operands, for the whole kernel
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int s = 0; s < D / 16; ++s) {
+        u32x4 v = {};
+        if (qrow < N) v = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + 16 * s + 8 * hh);
+        qf[s] = v;
+    }
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            u32x4 v = {};
-            if (qrow[qb] < N) v = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow[qb] * D + 16 * s + 8 * hh);
-            qf[qb][s] = v;
-        }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) settle(qf[qb][s]);
+    for (int s = 0; s < D / 16; ++s) settle(qf[s]);
+    wait_vm<0>();
 
-    f32x16 oacc[QB][D / 32];
-    float m[QB], lsum[QB], mx[QB];
+    f32x16 oacc[D / 32];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
+    float m = kNegBig, lsum = 0.f;
+    f32x16 sacc[KB];
+    u32x4 pf[KB][2];
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) oacc[qb][i] = zero16();
-        m[qb] = kNegBig;
-        lsum[qb] = 0.f;
+    for (int kb = 0; kb < KB; ++kb) {
+        sacc[kb] = zero16();
+        pf[kb][0] = pf[kb][1] = u32x4{};
     }
 
-    // S^T = K_t Q^T for tile t (stage t % NS): rows = keys, columns = queries.
-    // Each K fragment read from LDS feeds the QB query blocks.
-    auto scores = [&](int t, f32x16 (&sacc)[QB][KB]) {
-        const uint16_t* Ks = smem + (t % NS) * Cfg::kStage;
+    // S^T = K_t Q^T (stage t % NS): rows = keys, columns = this wave's queries
+    auto do_s = [&](int t) __attribute__((always_inline)) {
+        const uint16_t* Ks = smem + (t % NS) * kStage;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) sacc[qb][kb] = zero16();
+        for (int kb = 0; kb < KB; ++kb) sacc[kb] = zero16();
 #pragma unroll
         for (int s = 0; s < D / 16; ++s)
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const u32x4 a = KT::row8(Ks, 32 * kb + l32, 2 * s + hh);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = mma_bf16(a, qf[qb][s], sacc[qb][kb]);
-            }
+            for (int kb = 0; kb < KB; ++kb) sacc[kb] = mma_bf16(KT::row8(Ks, 32 * kb + l32, 2 * s + hh), qf[s], sacc[kb]);
     };
-    // mask keys past the diagonal (causal) or past the end, then the row maxima
-    auto mask_max = [&](int t, f32x16 (&sacc)[QB][KB]) {
-        const int k0 = t * BN;
-        if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + acc_row(r, hh);
-                        if ((CAUSAL && key > qrow[qb]) || key >= N) sacc[qb][kb][r] = -INFINITY;
-                    }
-        }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float x = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x = fmaxf(x, sacc[qb][kb][r]);
-            mx[qb] = pair_max(x);
-        }
-    };
-    // this wave has keys to look at in tile t
-    auto active = [&](int t) { return t < ntiles && !(CAUSAL && t * BN > qw + 32 * QB - 1); };
-
-    // One pipeline step: while the matrix cores form the scores of tile j+1,
-    // the vector units exponentiate tile j; then P_j V_j runs and the row
-    // maxima of tile j+1 are taken.  Tiles j and j+1 are both resident in LDS.
-    auto step = [&](int j, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
-        if (j + 1 < ntiles) pipe_wait<NS - 1, Cfg::kLoads>(j + 1, ntiles);
-        lds_barrier();                               // tile j+1 visible, stage of tile j-1 free
-        if (j + NS - 1 < ntiles) issue(j + NS - 1);
-        if (!active(j)) return;
-        const uint16_t* Vs = smem + (j % NS) * Cfg::kStage + KT::kElems;
-
-        // ---- running max (base 2, scale*log2(e) in c2); moved only when some
-        // row of the wave grew by more than 2^tau
-        float mnew[QB];
-        bool grow = false;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            mnew[qb] = fmaxf(m[qb], mx[qb] * c2);
-            grow |= mnew[qb] > m[qb] + Cfg::kTau;
-        }
-        if (__any(grow)) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float alpha = fast_exp2(m[qb] - mnew[qb]);
-                m[qb] = mnew[qb];
-                lsum[qb] *= alpha;
-#pragma unroll
-                for (int ct = 0; ct < D / 32; ++ct) oacc[qb][ct] *= alpha;
-            }
-        }
-        // ---- scores of tile j+1 (matrix cores; computed unconditionally so
-        // they share a basic block with the exponentials; without a next tile
-        // they read an idle stage and are discarded) ...
-        scores(j + 1, nxt);
-        // ---- ... while tile j is exponentiated and packed (vector units);
-        // l sums the bf16-rounded values, the same numbers the product uses
-        u32x4 pf[QB][KB][2];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) cur[qb][kb][r] = fast_exp2(fmaf(cur[qb][kb][r], c2, -m[qb]));
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    pf[qb][kb][t] = pack_bf16x8(cur[qb][kb], 8 * t);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) rs[i] = dot2_bf16_sum(pf[qb][kb][t][i], rs[i]);
-                }
-            }
-            lsum[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-        }
-        // ---- O^T += V_j^T P_j^T; each V^T fragment feeds the QB blocks
+    // O^T += V_t^T P_t^T
+    auto do_pv = [&](int t) __attribute__((always_inline)) {
+        const uint16_t* Vs = smem + (t % NS) * kStage + KT::kElems;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-                for (int ct = 0; ct < D / 32; ++ct) {
-                    const u32x4 a = VT::tr8(Vs, 32 * kb + 16 * t, 32 * ct, lane);
+                for (int ct = 0; ct < D / 32; ++ct)
+                    oacc[ct] = mma_bf16(KT::tr8(Vs, 32 * kb + 16 * t2, 32 * ct, lane), pf[kb][t2], oacc[ct]);
+    };
+    // G(t), t >= 1: scores of tile t (past this wave's last tile they are
+    // discarded) and the product of tile t-1 (P is zero past the last tile)
+    auto gemm = [&](int t) __attribute__((always_inline)) {
+        do_s(t);
+        do_pv(t - 1);
+        sched_gemm_phase<D>();
+    };
+    // X(t)
+    auto softmax = [&](int t) __attribute__((always_inline)) {
+        if (t >= ntw) {
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) oacc[qb][ct] = mma_bf16(a, pf[qb][kb][t], oacc[qb][ct]);
+            for (int kb = 0; kb < KB; ++kb) pf[kb][0] = pf[kb][1] = u32x4{};
+            return;
+        }
+        const int k0 = t * BN;
+        // ---- keys past the diagonal (causal) or past the end
+        if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * kb + acc_row(r, hh);
+                    if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r] = -INFINITY;
                 }
-        if (active(j + 1)) mask_max(j + 1, nxt);
+        }
+        // ---- running max (base 2, scale*log2(e) in c2); moved only when some
+        // row of the wave grew by more than 2^tau
+        float x = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x = fmaxf(x, sacc[kb][r]);
+        x = pair_max(x);
+        const float mnew = fmaxf(m, x * c2);
+        if (__any(mnew > m + Cfg::kTau)) {
+            const float alpha = fast_exp2(m - mnew);
+            m = mnew;
+            lsum *= alpha;
+#pragma unroll
+            for (int ct = 0; ct < D / 32; ++ct) oacc[ct] *= alpha;
+        }
+        // ---- P = exp2(c2 s - m), packed to bf16; l sums the rounded values
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c2, -m));
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+                pf[kb][t2] = pack_bf16x8(sacc[kb], 8 * t2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rs[i] = dot2_bf16_sum(pf[kb][t2][i], rs[i]);
+            }
+        }
+        lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     };
 
-    f32x16 sA[QB][KB], sB[QB][KB];
-    pipe_wait<NS, Cfg::kLoads>(0, ntiles);
+    // ---- phases.  Slot s ends with a barrier.  The stage of tile u >= NS is
+    // refilled at slot 2u - 4 (its previous tile, u - NS, was last read in
+    // slot 2u - 5); before the barrier ending odd slot s, tile (s+1)/2 has
+    // landed (one later tile may still be in flight).
+    auto head_even = [&](int s) __attribute__((always_inline)) {
+        const int u = s / 2 + 2;
+        if (s >= 4 && u < ntiles) issue(u);
+    };
+    auto tail_odd = [&](int s) __attribute__((always_inline)) {
+        const int tv = (s + 1) / 2;
+        if (tv >= NS && tv < ntiles) {
+            if (tv + 1 < ntiles) wait_vm<kLoads>();
+            else wait_vm<0>();
+        }
+        lds_barrier();
+    };
     lds_barrier();
-    scores(0, sA);
-    mask_max(0, sA);
-    for (int j = 0; j < ntiles; j += 2) {
-        step(j, sA, sB);
-        if (j + 1 < ntiles) step(j + 1, sB, sA);
+    if (grp == 0) {
+        // G(t) in slot 2t, X(t) in slot 2t + 1
+        head_even(0);
+        do_s(0);
+        lds_barrier();
+        softmax(0);
+        tail_odd(1);
+        for (int t = 1; t <= ntiles; ++t) {
+            head_even(2 * t);
+            gemm(t);
+            lds_barrier();
+            softmax(t);                               // t == ntiles: past every wave's last tile
+            tail_odd(2 * t + 1);
+        }
+    } else {
+        // X(t-1) in slot 2t, G(t) in slot 2t + 1
+        head_even(0);
+        lds_barrier();
+        do_s(0);
+        tail_odd(1);
+        for (int t = 1; t <= ntiles; ++t) {
+            head_even(2 * t);
+            softmax(t - 1);
+            lds_barrier();
+            gemm(t);
+            tail_odd(2 * t + 1);
+        }
     }
 
     // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
+    const float ltot = pair_sum(lsum);
+    if (qrow < N) {
+        const float inv = 1.0f / ltot;
+        uint16_t* Orow = O + (((int64_t)b * Hq + h) * N + qrow) * D;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float ltot = pair_sum(lsum[qb]);
-        if (qrow[qb] < N) {
-            const float inv = 1.0f / ltot;
-            uint16_t* Orow = O + (((int64_t)b * Hq + h) * N + qrow[qb]) * D;
+        for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
-            for (int ct = 0; ct < D / 32; ++ct)
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    u32x2 w;
-                    w[0] = pack_bf16x2(oacc[qb][ct][4 * gq] * inv, oacc[qb][ct][4 * gq + 1] * inv);
-                    w[1] = pack_bf16x2(oacc[qb][ct][4 * gq + 2] * inv, oacc[qb][ct][4 * gq + 3] * inv);
-                    *reinterpret_cast<u32x2*>(Orow + 32 * ct + 8 * gq + 4 * hh) = w;
-                }
-            if (hh == 0) LSE[((int64_t)b * Hq + h) * N + qrow[qb]] = (m[qb] + log2f(ltot)) * kLn2;
-        }
+            for (int gq = 0; gq < 4; ++gq) {
+                u32x2 w;
+                w[0] = pack_bf16x2(oacc[ct][4 * gq] * inv, oacc[ct][4 * gq + 1] * inv);
+                w[1] = pack_bf16x2(oacc[ct][4 * gq + 2] * inv, oacc[ct][4 * gq + 3] * inv);
+                *reinterpret_cast<u32x2*>(Orow + 32 * ct + 8 * gq + 4 * hh) = w;
+            }
+        if (hh == 0) LSE[((int64_t)b * Hq + h) * N + qrow] = (m + log2f(ltot)) * kLn2;
     }
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                          int N, float scale, hipStream_t st) {
-    using Cfg = FwdBf16Tuned<D>;
+    using Cfg = FwdBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, Cfg>), dim3((unsigned)((int64_t)nmb * Hq * B)), dim3(Cfg::kThreads),
-                       0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, Hq,
-                       Hkv, N, scale * kLog2e);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)nmb * Hq * B)), dim3(Cfg::kThreads), 0,
+                       st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, N,
+                       scale * kLog2e);
     return hipGetLastError();
 }
 
