@@ -15,37 +15,81 @@
 namespace fa {
 
 // ------------------------------------------------------------ dK, dV
-template <int D, int NW, int NS>
+//
+// A workgroup holds 256 keys (32 per wave: K as MFMA operands in registers,
+// V in LDS, dK and dV accumulators) and walks the steps (query head of the
+// group, query block).  Ping-pong schedule as in the forward: waves w and w+4
+// share a SIMD, each wave alternates
+//   G(i): dV^T += dO_{i-1}^T P_{i-1}, dK^T += Q_{i-1}^T dS_{i-1}, then
+//         S_i = Q_i K^T and dP_i = dO_i V^T
+//   X(i): P_i = exp2(c2 s - LSE log2 e), causal mask, dS_i = P_i (dP_i - D), pack
+// and the two wave groups run one phase apart, a barrier after every phase.
+template <int D>
 struct KVBf16Cfg {
-    static constexpr int kWaves = NW;
-    static constexpr int kThreads = 64 * NW;
-    static constexpr int BNK = 32 * NW;                 // keys per workgroup (32 per wave)
+    static constexpr int kWaves = 8;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int BNK = 32 * kWaves;             // keys per workgroup (32 per wave)
     static constexpr int BMQ = D == 128 ? 32 : 64;      // query rows per step
     static constexpr int QB = BMQ / 32;
-    static constexpr int kStages = NS;
-    using QT = LdsTile<BMQ, D, NW>;
+    static constexpr int kStages = 4;
+    using QT = LdsTile<BMQ, D, kWaves>;
+    using VT = LdsTile<BNK, D, kWaves>;                 // the workgroup's V rows, read as B operands of dP
     static constexpr int kStatChunks = BMQ / 2;         // 16-byte chunks of (LSE*log2e, D) per step
-    static constexpr int kStatPerWave = kStatChunks / NW;
-    static_assert(kStatChunks % NW == 0, "statistics split evenly over the waves");
+    static constexpr int kStatPerWave = kStatChunks / kWaves;
+    static_assert(kStatChunks % kWaves == 0, "statistics split evenly over the waves");
     static constexpr int kStatBytes = 8 * BMQ;
     static constexpr int kStageBytes = 2 * QT::kBytes + kStatBytes;
+    static constexpr int kLdsBytes = VT::kBytes + kStages * kStageBytes;
     static constexpr int kLoads = 2 * QT::kPerWave + 1;
 };
-template <int D>
-using KVBf16Tuned = KVBf16Cfg<D, 8, 4>;
 
-template <int D, bool CAUSAL, class Cfg>
-__global__ __launch_bounds__(Cfg::kThreads, 2) void bwd_dkdv_bf16_kernel(
+// G phase order: L reads ahead; the dV/dK products (two transposed reads per
+// fragment) first, then the S products (one read: Q) alternating with the dP
+// products (dO and V rows).
+template <int L>
+__device__ __forceinline__ void sched_dkdv_phase() {
+#pragma unroll
+    for (int i = 0; i < L; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    static_assert(L % 4 == 0, "whole (S, dP) pairs");
+#pragma unroll
+    for (int i = 0; i < 8 - L / 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < L / 2; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int N, int Npad, float c2,
     float scale) {
+    using Cfg = KVBf16Cfg<D>;
     using QT = typename Cfg::QT;
-    constexpr int BNK = Cfg::BNK, BMQ = Cfg::BMQ, QB = Cfg::QB, NS = Cfg::kStages;
-    __shared__ __attribute__((aligned(1024))) char smem[NS * Cfg::kStageBytes];
+    constexpr int NW = Cfg::kWaves, BNK = Cfg::BNK, BMQ = Cfg::BMQ, QB = Cfg::QB, NS = Cfg::kStages;
+    constexpr int kLoads = Cfg::kLoads;
+    static_assert(QB * D == 128, "16 + 16 products per G phase");
+    __shared__ __attribute__((aligned(1024))) char lds[Cfg::kLdsBytes];
+    using VT = typename Cfg::VT;
+    // stages first: their fragment offsets stay inside the 16-bit immediate of
+    // the LDS reads (the V rows sit above them)
+    char* smem = lds;                                   // Q / dO / statistics stages
+    const uint16_t* Vl = (const uint16_t*)(lds + NS * Cfg::kStageBytes);   // V rows k0 .. k0+255
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
+    const int grp = wave >> 2;                      // waves w and w+4 share a SIMD
 
     const int nkb = (N + BNK - 1) / BNK;
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -61,102 +105,202 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void bwd_dkdv_bf16_kernel(
 
     const int nqt = (N + BMQ - 1) / BMQ;
     const int qt0 = CAUSAL ? k0 / BMQ : 0;          // earlier query blocks see none of these keys
-    const int per_head = nqt - qt0;
-    const int total = G * per_head;
+    const int total = G * (nqt - qt0);              // steps: (head g*G + i / (nqt-qt0), block qt0 + i % (nqt-qt0))
 
-    // Step `it`: query head g*G + it / per_head, query block qt0 + it % per_head.
-    auto issue = [&](int it) {
-        const int hq = g * G + it / per_head;
-        const int q0 = (qt0 + it % per_head) * BMQ;
-        const int64_t bh = (int64_t)b * Hq + hq;
-        const char* st = smem + (it % NS) * Cfg::kStageBytes;
-        QT::load(Q + (bh * N + q0) * D, N - q0, (const uint16_t*)st, wave, lane);
-        QT::load(dO + (bh * N + q0) * D, N - q0, (const uint16_t*)(st + QT::kBytes), wave, lane);
+    // ---- direct loads of step u (issued in step order: one running position).
+    // The per-lane offsets are recomputed at every issue from an opaque copy
+    // of the lane index: kept live across the loop they would be spilled, and
+    // a scratch reload is a vector-memory load whose wait would also drain
+    // the tile loads in flight.
+    int ih = 0, iq = qt0;                           // head offset and query block of the next step to load
+    int u_next = 0;
+    auto issue = [&](int u) __attribute__((always_inline)) {
+        const int64_t bh = (int64_t)b * Hq + g * G + ih;
+        const int q0 = iq * BMQ;
+        const uint32_t st = lds_addr(smem + (u % NS) * Cfg::kStageBytes);
+        const uint16_t* qb = Q + (bh * N + q0) * D;
+        const uint16_t* ob = dO + (bh * N + q0) * D;
+        const int rows_valid = N - q0;
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int i = 0; i < QT::kPerWave; ++i) {
+            const int row = (i * NW + wave) * QT::RG + ln % QT::RG;
+            const int grow = row < rows_valid ? row : rows_valid - 1;
+            const uint32_t off = (uint32_t)(grow * D + (ln / QT::RG) * 8) * 2u;
+            dma16s(qb, off, st + (i * NW + wave) * QT::RGS);
+            dma16s(ob, off, st + QT::kBytes + (i * NW + wave) * QT::RGS);
+        }
         // statistics: chunk c < BMQ/4 holds LSE*log2e rows q0+4c.., the rest D rows
         const int c = wave * Cfg::kStatPerWave + lane;
         if (lane < Cfg::kStatPerWave) {
             const float* src = c < BMQ / 4 ? WSl + bh * Npad + q0 + 4 * c : WSd + bh * Npad + q0 + 4 * (c - BMQ / 4);
-            dma16(src, lds_addr(st + 2 * QT::kBytes) + 16 * wave * Cfg::kStatPerWave);
+            dma16(src, st + 2 * QT::kBytes + 16 * wave * Cfg::kStatPerWave);
         }
+        if (++iq == nqt) {
+            iq = qt0;
+            ++ih;
+        }
+        (void)u;
     };
+    VT::load(Vg + (int64_t)k0 * D, N - k0, Vl, wave, lane);
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t)
-        if (t < total) issue(t);
-
-    u32x4 kf[D / 16], vf[D / 16];
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-        u32x4 a = {}, c = {};
-        if (krow < N) {
-            a = *reinterpret_cast<const u32x4*>(Kg + (int64_t)krow * D + 16 * s + 8 * hh);
-            c = *reinterpret_cast<const u32x4*>(Vg + (int64_t)krow * D + 16 * s + 8 * hh);
+    for (int t = 0; t < NS; ++t)
+        if (t < total) {
+            issue(u_next);
+            ++u_next;
         }
-        kf[s] = a;
-        vf[s] = c;
-    }
+
+    u32x4 kf[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-        settle(kf[s]);
-        settle(vf[s]);
+        u32x4 a = {};
+        if (krow < N) a = *reinterpret_cast<const u32x4*>(Kg + (int64_t)krow * D + 16 * s + 8 * hh);
+        kf[s] = a;
     }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) settle(kf[s]);
+    wait_vm<0>();
+
     f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-        dkacc[i] = zero16();
-        dvacc[i] = zero16();
+    for (int i = 0; i < D / 32; ++i) dkacc[i] = dvacc[i] = zero16();
+    f32x16 sacc[QB], dpacc[QB];
+    u32x4 pb[QB][2], sb[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        sacc[qb] = dpacc[qb] = zero16();
+        pb[qb][0] = pb[qb][1] = sb[qb][0] = sb[qb][1] = u32x4{};
     }
 
-    for (int it = 0; it < total; ++it) {
-        const int q0 = (qt0 + it % per_head) * BMQ;
-        pipe_wait<NS, Cfg::kLoads>(it, total);
-        lds_barrier();
-        if (it + NS - 1 < total) issue(it + NS - 1);
-        const char* st = smem + (it % NS) * Cfg::kStageBytes;
+    // S = Q K^T and dP = dO V^T of step i: rows = queries, columns = this wave's keys
+    auto do_sdp = [&](int i) __attribute__((always_inline)) {
+        const char* st = smem + (i % NS) * Cfg::kStageBytes;
         const uint16_t* Qs = (const uint16_t*)st;
         const uint16_t* dOs = (const uint16_t*)(st + QT::kBytes);
-        const float* sl = (const float*)(st + 2 * QT::kBytes);   // LSE*log2e [BMQ], then D [BMQ]
-
-        if (!(CAUSAL && q0 + BMQ - 1 < kw)) {
-            const bool need_mask = CAUSAL && kw + 31 > q0;
+        // the V fragments are the same every step; an opaque zero offset keeps
+        // their reads here instead of hoisted (and held) outside the loop
+        int vz = 0;
+        asm volatile("" : "+s"(vz));
+        const uint16_t* Vw = Vl + vz;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb] = dpacc[qb] = zero16();
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                // S = Q K^T and dP = dO V^T: rows = queries, columns = this wave's keys
-                f32x16 sacc = zero16(), dpacc = zero16();
+                sacc[qb] = mma_bf16(QT::row8(Qs, 32 * qb + l32, 2 * s + hh), kf[s], sacc[qb]);
+                dpacc[qb] = mma_bf16(QT::row8(dOs, 32 * qb + l32, 2 * s + hh),
+                                     VT::row8(Vw, 32 * wave + l32, 2 * s + hh), dpacc[qb]);
+            }
+    };
+    // dV^T += dO_i^T P_i ;  dK^T += Q_i^T dS_i
+    auto do_dvdk = [&](int i) __attribute__((always_inline)) {
+        const char* st = smem + (i % NS) * Cfg::kStageBytes;
+        const uint16_t* Qs = (const uint16_t*)st;
+        const uint16_t* dOs = (const uint16_t*)(st + QT::kBytes);
 #pragma unroll
-                for (int s = 0; s < D / 16; ++s) {
-                    sacc = mma_bf16(QT::row8(Qs, 32 * qb + l32, 2 * s + hh), kf[s], sacc);
-                    dpacc = mma_bf16(QT::row8(dOs, 32 * qb + l32, 2 * s + hh), vf[s], dpacc);
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int ct = 0; ct < D / 32; ++ct) {
+                    dvacc[ct] = mma_bf16(QT::tr8(dOs, 32 * qb + 16 * t, 32 * ct, lane), pb[qb][t], dvacc[ct]);
+                    dkacc[ct] = mma_bf16(QT::tr8(Qs, 32 * qb + 16 * t, 32 * ct, lane), sb[qb][t], dkacc[ct]);
                 }
-                // P from the stored statistics.  Causal: key krow is hidden from
-                // query q0 + 32*qb + row(r) iff delta > 8*(r/4) + r%4, with
-                // delta = krow - q0 - 32*qb - 4*hh (forced below every row
-                // when the block needs no mask): one compare and one select
-                const int delta = need_mask ? krow - q0 - 32 * qb - 4 * hh : -64;
+    };
+    // G(i), i >= 1 (i == total: the products of the last step only)
+    auto gemm = [&](int i) __attribute__((always_inline)) {
+        do_dvdk(i - 1);
+        do_sdp(i);
+        sched_dkdv_phase<D == 128 ? 8 : 4>();
+    };
+    // X(i): step i's query block is xq
+    int xq = qt0;
+    auto softmax = [&](int i) __attribute__((always_inline)) {
+        if (i >= total) {
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 32 * qb + 8 * gq + 4 * hh);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + BMQ + 32 * qb + 8 * gq + 4 * hh);
+            for (int qb = 0; qb < QB; ++qb) pb[qb][0] = pb[qb][1] = sb[qb][0] = sb[qb][1] = u32x4{};
+            return;
+        }
+        const int q0 = xq * BMQ;
+        if (++xq == nqt) xq = qt0;
+        const float* sl = (const float*)(smem + (i % NS) * Cfg::kStageBytes + 2 * QT::kBytes);
+        // causal: key krow is hidden from query q0 + 32*qb + row(r) iff
+        // delta > 8*(r/4) + r%4, delta = krow - q0 - 32*qb - 4*hh (forced
+        // below every row when the block needs no mask)
+        const bool need_mask = CAUSAL && kw + 31 > q0;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r = 4 * gq + j;
-                        float p = fast_exp2(fmaf(sacc[r], c2, -l4[j]));
-                        if (CAUSAL && delta > 8 * gq + j) p = 0.f;
-                        sacc[r] = p;
-                        dpacc[r] = p * (dpacc[r] - d4[j]);
-                    }
-                }
-                // dV^T += dO^T P ;  dK^T += Q^T dS
+        for (int qb = 0; qb < QB; ++qb) {
+            const int delta = need_mask ? krow - q0 - 32 * qb - 4 * hh : -64;
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const u32x4 pb = pack_bf16x8(sacc, 8 * t);
-                    const u32x4 sb = pack_bf16x8(dpacc, 8 * t);
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 32 * qb + 8 * gq + 4 * hh);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + BMQ + 32 * qb + 8 * gq + 4 * hh);
 #pragma unroll
-                    for (int ct = 0; ct < D / 32; ++ct) {
-                        dvacc[ct] = mma_bf16(QT::tr8(dOs, 32 * qb + 16 * t, 32 * ct, lane), pb, dvacc[ct]);
-                        dkacc[ct] = mma_bf16(QT::tr8(Qs, 32 * qb + 16 * t, 32 * ct, lane), sb, dkacc[ct]);
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * gq + j;
+                    float p = fast_exp2(fmaf(sacc[qb][r], c2, -l4[j]));
+                    if (CAUSAL && delta > 8 * gq + j) p = 0.f;
+                    sacc[qb][r] = p;
+                    dpacc[qb][r] = p * (dpacc[qb][r] - d4[j]);
                 }
             }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                pb[qb][t] = pack_bf16x8(sacc[qb], 8 * t);
+                sb[qb][t] = pack_bf16x8(dpacc[qb], 8 * t);
+            }
+            // one query block at a time (its statistics reads are not hoisted
+            // above the previous block's arithmetic)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- phases (slot s ends with a barrier).  Each group loads step
+    // i+NS-2 right after its own G(i) (that stage held step i-2, last read in
+    // slot 2i-1); before the barrier ending odd slot s, step tv = (s+1)/2 has
+    // landed, while up to NS-3 later steps may still be in flight.
+    static_assert(NS >= 4 && (NS - 3) * kLoads <= 63, "vmcnt range");
+    auto refill = [&](int i) __attribute__((always_inline)) {
+        if (i >= 2 && i + NS - 2 < total) {
+            issue(u_next);
+            ++u_next;
+        }
+    };
+    auto tail_odd = [&](int s) __attribute__((always_inline)) {
+        const int tv = (s + 1) / 2;
+        if (tv >= NS && tv < total) {
+            const int later = min(NS - 3, total - 1 - tv);
+            wait_vm_dyn<kLoads, NS - 3>(later);
+        }
+        lds_barrier();
+    };
+    lds_barrier();
+    if (grp == 0) {
+        // G(i) in slot 2i, X(i) in slot 2i + 1
+        do_sdp(0);
+        lds_barrier();
+        softmax(0);
+        tail_odd(1);
+        for (int i = 1; i <= total; ++i) {
+            gemm(i);
+            refill(i);
+            lds_barrier();
+            softmax(i);
+            tail_odd(2 * i + 1);
+        }
+    } else {
+        // X(i-1) in slot 2i, G(i) in slot 2i + 1
+        lds_barrier();
+        do_sdp(0);
+        tail_odd(1);
+        for (int i = 1; i <= total; ++i) {
+            softmax(i - 1);
+            lds_barrier();
+            gemm(i);
+            refill(i);
+            tail_odd(2 * i + 1);
         }
     }
 
@@ -180,33 +324,61 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void bwd_dkdv_bf16_kernel(
 }
 
 // ------------------------------------------------------------ dQ
-template <int D, int NW, int NS>
-struct QBf16Cfg {
-    static constexpr int kWaves = NW;
-    static constexpr int kThreads = 64 * NW;
-    static constexpr int BM = 32 * NW;          // query rows per workgroup
-    static constexpr int BNK = 64;              // keys per tile
-    static constexpr int kStages = NS;
-    using KT = LdsTile<BNK, D, NW>;             // read as rows and transposed
-    using VT = LdsTile<BNK, D, NW>;             // read as rows
-    static constexpr int kStage = KT::kElems + VT::kElems;
-    static constexpr int kLoads = KT::kPerWave + VT::kPerWave;
-};
+//
+// Same ping-pong schedule as the bf16 forward: waves w and w+4 share a SIMD,
+// each wave alternates
+//   G(t): dQ^T += K_{t-1}^T dS_{t-1}^T, then S_t^T = K_t Q^T, dP_t^T = V_t dO^T
+//   X(t): P_t = exp2(c2 s - LSE log2 e), mask, dS_t = P_t (dP_t - D), pack
+// and the two wave groups run one phase apart, a barrier after every phase.
 template <int D>
-using QBf16Tuned = QBf16Cfg<D, 8, 3>;
+struct QBf16Cfg {
+    static constexpr int kWaves = 8;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int BM = 32 * kWaves;      // query rows per workgroup
+    static constexpr int BNK = 64;              // keys per tile
+    static constexpr int kStages = 4;
+    using KT = LdsTile<BNK, D, kWaves>;         // K (rows and transposed), V (rows)
+    static constexpr int kStage = 2 * KT::kElems;
+    static constexpr int kLoads = 2 * KT::kPerWave;
+};
 
-template <int D, bool CAUSAL, class Cfg>
-__global__ __launch_bounds__(Cfg::kThreads, 2) void bwd_dq_bf16_kernel(
+// G phase order: L = d/16 reads ahead; the dQ products (two transposed
+// reads per fragment) first, then the S and dP products (one read each).
+template <int D>
+__device__ __forceinline__ void sched_dq_phase() {
+    constexpr int L = D / 16;
+#pragma unroll
+    for (int i = 0; i < L; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < D / 4 - L; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
     uint16_t* __restrict__ dQ, int Hq, int Hkv, int N, int Npad, float c2, float scale) {
+    using Cfg = QBf16Cfg<D>;
     using KT = typename Cfg::KT;
-    using VT = typename Cfg::VT;
-    constexpr int BM = Cfg::BM, BNK = Cfg::BNK, NS = Cfg::kStages;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * Cfg::kStage];
+    constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BNK = Cfg::BNK, NS = Cfg::kStages, KB = BNK / 32;
+    constexpr int kStage = Cfg::kStage, kLoads = Cfg::kLoads;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * kStage];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
+    const int grp = wave >> 2;                  // waves w and w+4 share a SIMD
 
     const int nmb = (N + BM - 1) / BM;
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -223,14 +395,37 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void bwd_dq_bf16_kernel(
     const int qrow = qw + l32;
     const int kend = CAUSAL ? min(N, q0 + BM) : N;
     const int ntiles = (kend + BNK - 1) / BNK;
+    const int ntw = qw >= N ? 0 : CAUSAL ? (min(N, qw + 32) + BNK - 1) / BNK : ntiles;
 
-    auto issue = [&](int t) {
-        const uint16_t* st = smem + (t % NS) * Cfg::kStage;
-        KT::load(Kg + (int64_t)t * BNK * D, N - t * BNK, st, wave, lane);
-        VT::load(Vg + (int64_t)t * BNK * D, N - t * BNK, st + KT::kElems, wave, lane);
+    uint32_t voff[KT::kPerWave];
+#pragma unroll
+    for (int i = 0; i < KT::kPerWave; ++i) {
+        const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
+        voff[i] = (uint32_t)(row * D + (lane / KT::RG) * 8) * 2u;
+    }
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const uint32_t st = lds_addr(smem + (t % NS) * kStage);
+        const uint16_t* kb = Kg + (int64_t)t * BNK * D;
+        const uint16_t* vb = Vg + (int64_t)t * BNK * D;
+        const int rows_valid = N - t * BNK;
+        if (rows_valid >= BNK) {
+#pragma unroll
+            for (int i = 0; i < KT::kPerWave; ++i) dma16s(kb, voff[i], st + (i * NW + wave) * KT::RGS);
+#pragma unroll
+            for (int i = 0; i < KT::kPerWave; ++i) dma16s(vb, voff[i], st + KT::kBytes + (i * NW + wave) * KT::RGS);
+        } else {
+#pragma unroll
+            for (int i = 0; i < KT::kPerWave; ++i) {
+                const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
+                const int grow = row < rows_valid ? row : rows_valid - 1;
+                const uint32_t off = (uint32_t)(grow * D + (lane / KT::RG) * 8) * 2u;
+                dma16s(kb, off, st + (i * NW + wave) * KT::RGS);
+                dma16s(vb, off, st + KT::kBytes + (i * NW + wave) * KT::RGS);
+            }
+        }
     };
 #pragma unroll
-    for (int t = 0; t < NS - 1; ++t)
+    for (int t = 0; t < NS; ++t)
         if (t < ntiles) issue(t);
 
     u32x4 qf[D / 16], of[D / 16];
@@ -254,63 +449,122 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void bwd_dq_bf16_kernel(
     }
     settle(lse2);
     settle(dq_d);
+    wait_vm<0>();
 
     f32x16 dqacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) dqacc[i] = zero16();
+    f32x16 sacc[KB], dpacc[KB];
+    u32x4 dsf[KB][2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        sacc[kb] = dpacc[kb] = zero16();
+        dsf[kb][0] = dsf[kb][1] = u32x4{};
+    }
 
-    for (int j = 0; j < ntiles; ++j) {
-        const int k0 = j * BNK;
-        pipe_wait<NS, Cfg::kLoads>(j, ntiles);
-        lds_barrier();
-        if (j + NS - 1 < ntiles) issue(j + NS - 1);
-        const uint16_t* Ks = smem + (j % NS) * Cfg::kStage;
+    // S^T = K_t Q^T and dP^T = V_t dO^T: rows = keys, columns = this wave's queries
+    auto do_sdp = [&](int t) __attribute__((always_inline)) {
+        const uint16_t* Ks = smem + (t % NS) * kStage;
         const uint16_t* Vs = Ks + KT::kElems;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sacc[kb] = dpacc[kb] = zero16();
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                sacc[kb] = mma_bf16(KT::row8(Ks, 32 * kb + l32, 2 * s + hh), qf[s], sacc[kb]);
+                dpacc[kb] = mma_bf16(KT::row8(Vs, 32 * kb + l32, 2 * s + hh), of[s], dpacc[kb]);
+            }
+    };
+    // dQ^T += K_t^T dS_t^T
+    auto do_dq = [&](int t) __attribute__((always_inline)) {
+        const uint16_t* Ks = smem + (t % NS) * kStage;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                for (int ct = 0; ct < D / 32; ++ct)
+                    dqacc[ct] = mma_bf16(KT::tr8(Ks, 32 * kb + 16 * t2, 32 * ct, lane), dsf[kb][t2], dqacc[ct]);
+    };
+    // G(t), t >= 1 (past this wave's last tile the scores are discarded and
+    // dS is zero)
+    auto gemm = [&](int t) __attribute__((always_inline)) {
+        do_dq(t - 1);
+        do_sdp(t);
+        sched_dq_phase<D>();
+    };
+    // X(t): P from the stored statistics; keys after the query (causal) or
+    // past the end zeroed in one wave-uniform branch; dS packed to bf16
+    auto softmax = [&](int t) __attribute__((always_inline)) {
+        if (t >= ntw) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) dsf[kb][0] = dsf[kb][1] = u32x4{};
+            return;
+        }
+        const int k0 = t * BNK;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c2, -lse2));
+        if ((CAUSAL && k0 + BNK - 1 > qw) || (k0 + BNK > N)) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * kb + acc_row(r, hh);
+                    if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r] = 0.f;
+                }
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dpacc[kb][r] = sacc[kb][r] * (dpacc[kb][r] - dq_d);
+            dsf[kb][0] = pack_bf16x8(dpacc[kb], 0);
+            dsf[kb][1] = pack_bf16x8(dpacc[kb], 8);
+        }
+    };
 
-        if (!(CAUSAL && k0 > qw + 31)) {
-            // S^T = K Q^T and dP^T = V dO^T: rows = keys, columns = this wave's queries
-            f32x16 sacc[BNK / 32], dpacc[BNK / 32];
-#pragma unroll
-            for (int kb = 0; kb < BNK / 32; ++kb) {
-                sacc[kb] = zero16();
-                dpacc[kb] = zero16();
-            }
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-                for (int kb = 0; kb < BNK / 32; ++kb) {
-                    sacc[kb] = mma_bf16(KT::row8(Ks, 32 * kb + l32, 2 * s + hh), qf[s], sacc[kb]);
-                    dpacc[kb] = mma_bf16(VT::row8(Vs, 32 * kb + l32, 2 * s + hh), of[s], dpacc[kb]);
-                }
-            // P from the stored statistics; keys after the query (causal) or
-            // past the end are zeroed in one wave-uniform branch
-#pragma unroll
-            for (int kb = 0; kb < BNK / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c2, -lse2));
-            if ((CAUSAL && k0 + BNK - 1 > qw) || (k0 + BNK > N)) {
-#pragma unroll
-                for (int kb = 0; kb < BNK / 32; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + acc_row(r, hh);
-                        if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r] = 0.f;
-                    }
-            }
-#pragma unroll
-            for (int kb = 0; kb < BNK / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) dpacc[kb][r] = sacc[kb][r] * (dpacc[kb][r] - dq_d);
-            // dQ^T += K^T dS^T
-#pragma unroll
-            for (int kb = 0; kb < BNK / 32; ++kb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const u32x4 sb = pack_bf16x8(dpacc[kb], 8 * t);
-#pragma unroll
-                    for (int ct = 0; ct < D / 32; ++ct)
-                        dqacc[ct] = mma_bf16(KT::tr8(Ks, 32 * kb + 16 * t, 32 * ct, lane), sb, dqacc[ct]);
-                }
+    // ---- phases (slot s ends with a barrier).  Each group refills the
+    // stage of tile t+2 (its previous tile, t-2, was last read in slot 2t-1)
+    // right after its own G(t); before the barrier ending odd slot s, tile
+    // (s+1)/2 has landed (one later tile may still be in flight).
+    auto refill = [&](int t) __attribute__((always_inline)) {
+        if (t + 2 >= NS && t + 2 < ntiles) issue(t + 2);
+    };
+    auto tail_odd = [&](int s) __attribute__((always_inline)) {
+        const int tv = (s + 1) / 2;
+        if (tv >= NS && tv < ntiles) {
+            if (tv + 1 < ntiles) wait_vm<kLoads>();
+            else wait_vm<0>();
+        }
+        lds_barrier();
+    };
+    lds_barrier();
+    if (grp == 0) {
+        // G(t) in slot 2t, X(t) in slot 2t + 1
+        do_sdp(0);
+        lds_barrier();
+        softmax(0);
+        tail_odd(1);
+        for (int t = 1; t <= ntiles; ++t) {
+            gemm(t);
+            refill(t);
+            lds_barrier();
+            softmax(t);
+            tail_odd(2 * t + 1);
+        }
+    } else {
+        // X(t-1) in slot 2t, G(t) in slot 2t + 1
+        lds_barrier();
+        do_sdp(0);
+        tail_odd(1);
+        for (int t = 1; t <= ntiles; ++t) {
+            softmax(t - 1);
+            lds_barrier();
+            gemm(t);
+            refill(t);
+            tail_odd(2 * t + 1);
         }
     }
 
@@ -331,10 +585,10 @@ __global__ __launch_bounds__(Cfg::kThreads, 2) void bwd_dq_bf16_kernel(
 template <int D, bool CAUSAL>
 static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* ws,
                               void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
-    using Cfg = KVBf16Tuned<D>;
+    using Cfg = KVBf16Cfg<D>;
     const int nkb = (N + Cfg::BNK - 1) / Cfg::BNK;
     const int Np = ws_rows(N);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, Cfg>), dim3((unsigned)((int64_t)nkb * Hkv * B)),
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)nkb * Hkv * B)),
                        dim3(Cfg::kThreads), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dO, ws, ws + (int64_t)B * Hq * Np, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv,
                        N, Np, scale * kLog2e, scale);
@@ -344,10 +598,10 @@ static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const
 template <int D, bool CAUSAL>
 static hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dq,
                             int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
-    using Cfg = QBf16Tuned<D>;
+    using Cfg = QBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
     const int Np = ws_rows(N);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, Cfg>), dim3((unsigned)((int64_t)nmb * Hq * B)),
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)nmb * Hq * B)),
                        dim3(Cfg::kThreads), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dO, ws, ws + (int64_t)B * Hq * Np, (uint16_t*)dq, Hq, Hkv, N, Np,
                        scale * kLog2e, scale);

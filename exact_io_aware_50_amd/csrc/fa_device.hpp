@@ -355,6 +355,17 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
+// vmcnt(later * L) for a run-time later in [0, MAXL] (the count is an
+// immediate of the instruction).
+template <int L, int MAXL>
+__device__ __forceinline__ void wait_vm_dyn(int later) {
+    if constexpr (MAXL >= 5) { if (later >= 5) { wait_vm<5 * L>(); return; } }
+    if constexpr (MAXL >= 4) { if (later == 4) { wait_vm<4 * L>(); return; } }
+    if constexpr (MAXL >= 3) { if (later == 3) { wait_vm<3 * L>(); return; } }
+    if constexpr (MAXL >= 2) { if (later == 2) { wait_vm<2 * L>(); return; } }
+    if constexpr (MAXL >= 1) { if (later == 1) { wait_vm<L>(); return; } }
+    wait_vm<0>();
+}
 // Workgroup barrier that does not drain outstanding global loads; LDS reads
 // of the previous tile are completed first.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); }
