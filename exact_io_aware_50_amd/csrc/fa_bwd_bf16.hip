@@ -255,11 +255,21 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
             // above the previous block's arithmetic)
             __builtin_amdgcn_sched_barrier(0);
         }
+        // the packed operands are finished here, inside this phase (not sunk
+        // past the barrier into the next matrix phase)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                settle(pb[qb][t]);
+                settle(sb[qb][t]);
+            }
     };
 
-    // ---- phases (slot s ends with a barrier).  Each group loads step
-    // i+NS-2 right after its own G(i) (that stage held step i-2, last read in
-    // slot 2i-1); before the barrier ending odd slot s, step tv = (s+1)/2 has
+    // ---- phases (slot s ends with a barrier).  In loop round i both groups
+    // load step i+NS-2 (that stage held step i-2, last read in slot 2i-1)
+    // during their vector phase (slot 2i+1 for the first group, 2i for the
+    // second); before the barrier ending odd slot s, step tv = (s+1)/2 has
     // landed, while up to NS-3 later steps may still be in flight.
     static_assert(NS >= 4 && (NS - 3) * kLoads <= 63, "vmcnt range");
     auto refill = [&](int i) __attribute__((always_inline)) {
@@ -285,9 +295,9 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         tail_odd(1);
         for (int i = 1; i <= total; ++i) {
             gemm(i);
-            refill(i);
             lds_barrier();
             softmax(i);
+            refill(i);
             tail_odd(2 * i + 1);
         }
     } else {
@@ -297,9 +307,9 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         tail_odd(1);
         for (int i = 1; i <= total; ++i) {
             softmax(i - 1);
+            refill(i);
             lds_barrier();
             gemm(i);
-            refill(i);
             tail_odd(2 * i + 1);
         }
     }
@@ -523,12 +533,19 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
             dsf[kb][0] = pack_bf16x8(dpacc[kb], 0);
             dsf[kb][1] = pack_bf16x8(dpacc[kb], 8);
         }
+        // dS is finished inside this phase (not sunk into the next matrix phase)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            settle(dsf[kb][0]);
+            settle(dsf[kb][1]);
+        }
     };
 
-    // ---- phases (slot s ends with a barrier).  Each group refills the
-    // stage of tile t+2 (its previous tile, t-2, was last read in slot 2t-1)
-    // right after its own G(t); before the barrier ending odd slot s, tile
-    // (s+1)/2 has landed (one later tile may still be in flight).
+    // ---- phases (slot s ends with a barrier).  In loop round t both groups
+    // refill the stage of tile t+2 (its previous tile, t-2, was last read in
+    // slot 2t-1) during their vector phase (slot 2t+1 for the first group,
+    // 2t for the second); before the barrier ending odd slot s, tile (s+1)/2
+    // has landed (one later tile may still be in flight).
     auto refill = [&](int t) __attribute__((always_inline)) {
         if (t + 2 >= NS && t + 2 < ntiles) issue(t + 2);
     };
@@ -549,9 +566,9 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
         tail_odd(1);
         for (int t = 1; t <= ntiles; ++t) {
             gemm(t);
-            refill(t);
             lds_barrier();
             softmax(t);
+            refill(t);
             tail_odd(2 * t + 1);
         }
     } else {
@@ -561,9 +578,9 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
         tail_odd(1);
         for (int t = 1; t <= ntiles; ++t) {
             softmax(t - 1);
+            refill(t);
             lds_barrier();
             gemm(t);
-            refill(t);
             tail_odd(2 * t + 1);
         }
     }

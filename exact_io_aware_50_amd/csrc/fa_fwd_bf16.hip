@@ -239,6 +239,12 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
             }
         }
         lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        // P is finished inside this phase (not sunk into the next matrix phase)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            settle(pf[kb][0]);
+            settle(pf[kb][1]);
+        }
     };
 
     // ---- phases.  Slot s ends with a barrier.  The stage of tile u >= NS is
