@@ -345,24 +345,6 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
                  : "v"(voff), "s"(ps), "s"(__builtin_amdgcn_readfirstlane(m0))
                  : "memory");
 }
-// The same two copies, issued only once `after` has been computed (an unused
-// input operand): places a load at a chosen point of a vector-only phase.
-__device__ __forceinline__ void dma16s_after(const void* sbase, uint32_t voff, uint32_t m0, float after) {
-    const uint64_t p = (uint64_t)(uintptr_t)sbase;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
-    const uint64_t ps = ((uint64_t)hi << 32) | (uint64_t)lo;
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(ps), "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(after)
-                 : "memory");
-}
-__device__ __forceinline__ void dma16_after(const void* gptr, uint32_t m0, float after) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(after)
-                 : "memory");
-}
 // Make the compiler finish its own pending loads into these registers here
 // (an empty statement that reads them), so that its waits are not placed in a
 // later pipelined loop, where they would also drain the asm-issued loads.
