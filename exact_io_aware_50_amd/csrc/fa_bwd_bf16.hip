@@ -227,23 +227,33 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         if (++xq == nqt) xq = qt0;
         const float* sl = (const float*)(smem + (i % NS) * Cfg::kStageBytes + 2 * QT::kBytes);
         // causal: key krow is hidden from query q0 + 32*qb + row(r) iff
-        // delta > 8*(r/4) + r%4, delta = krow - q0 - 32*qb - 4*hh (forced
-        // below every row when the block needs no mask)
+        // delta > 8*(r/4) + r%4, delta = krow - q0 - 32*qb - 4*hh; steps whose
+        // queries all follow this wave's keys skip the test (uniform branch)
         const bool need_mask = CAUSAL && kw + 31 > q0;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const int delta = need_mask ? krow - q0 - 32 * qb - 4 * hh : -64;
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 32 * qb + 8 * gq + 4 * hh);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * gq + j;
+                    sacc[qb][r] = fast_exp2(fmaf(sacc[qb][r], c2, -l4[j]));
+                }
+            }
+            if (need_mask) {
+                const int delta = krow - q0 - 32 * qb - 4 * hh;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (delta > 8 * (r / 4) + r % 4) sacc[qb][r] = 0.f;
+            }
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
                 const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + BMQ + 32 * qb + 8 * gq + 4 * hh);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 4 * gq + j;
-                    float p = fast_exp2(fmaf(sacc[qb][r], c2, -l4[j]));
-                    if (CAUSAL && delta > 8 * gq + j) p = 0.f;
-                    sacc[qb][r] = p;
-                    dpacc[qb][r] = p * (dpacc[qb][r] - d4[j]);
+                    dpacc[qb][r] = sacc[qb][r] * (dpacc[qb][r] - d4[j]);
                 }
             }
 #pragma unroll
@@ -267,10 +277,10 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
     };
 
     // ---- phases (slot s ends with a barrier).  In loop round i both groups
-    // load step i+NS-2 (that stage held step i-2, last read in slot 2i-1)
-    // during their vector phase (slot 2i+1 for the first group, 2i for the
-    // second); before the barrier ending odd slot s, step tv = (s+1)/2 has
-    // landed, while up to NS-3 later steps may still be in flight.
+    // load step i+NS-2 (that stage held step i-2, last read in slot 2i-1) at
+    // the start of their vector phase (slot 2i+1 for the first group, 2i for
+    // the second); before the barrier ending odd slot s, step tv = (s+1)/2
+    // has landed, while up to NS-3 later steps may still be in flight.
     static_assert(NS >= 4 && (NS - 3) * kLoads <= 63, "vmcnt range");
     auto refill = [&](int i) __attribute__((always_inline)) {
         if (i >= 2 && i + NS - 2 < total) {
@@ -296,8 +306,8 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         for (int i = 1; i <= total; ++i) {
             gemm(i);
             lds_barrier();
-            softmax(i);
             refill(i);
+            softmax(i);
             tail_odd(2 * i + 1);
         }
     } else {
@@ -306,8 +316,8 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         do_sdp(0);
         tail_odd(1);
         for (int i = 1; i <= total; ++i) {
-            softmax(i - 1);
             refill(i);
+            softmax(i - 1);
             lds_barrier();
             gemm(i);
             tail_odd(2 * i + 1);
