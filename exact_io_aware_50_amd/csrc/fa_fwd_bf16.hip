@@ -114,26 +114,27 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
         const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
         voff[i] = (uint32_t)(row * D + (lane / KT::RG) * 8) * 2u;
     }
-    auto issue = [&](int t) __attribute__((always_inline)) {
-        const uint32_t st = lds_addr(smem + (t % NS) * kStage);
-        const uint16_t* kb = Kh + (int64_t)t * BN * D;
-        const uint16_t* vb = Vh + (int64_t)t * BN * D;
+    // half = 0: the K rows of tile t, 1: its V rows
+    auto issue_half = [&](int t, const int half) __attribute__((always_inline)) {
+        const uint32_t st = lds_addr(smem + (t % NS) * kStage) + half * KT::kBytes;
+        const uint16_t* src = (half ? Vh : Kh) + (int64_t)t * BN * D;
         const int rows_valid = N - t * BN;
         if (rows_valid >= BN) {
 #pragma unroll
-            for (int i = 0; i < KT::kPerWave; ++i) dma16s(kb, voff[i], st + (i * NW + wave) * KT::RGS);
-#pragma unroll
-            for (int i = 0; i < KT::kPerWave; ++i) dma16s(vb, voff[i], st + KT::kBytes + (i * NW + wave) * KT::RGS);
+            for (int i = 0; i < KT::kPerWave; ++i) dma16s(src, voff[i], st + (i * NW + wave) * KT::RGS);
         } else {
 #pragma unroll
             for (int i = 0; i < KT::kPerWave; ++i) {
                 const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
                 const int grow = row < rows_valid ? row : rows_valid - 1;
                 const uint32_t off = (uint32_t)(grow * D + (lane / KT::RG) * 8) * 2u;
-                dma16s(kb, off, st + (i * NW + wave) * KT::RGS);
-                dma16s(vb, off, st + KT::kBytes + (i * NW + wave) * KT::RGS);
+                dma16s(src, off, st + (i * NW + wave) * KT::RGS);
             }
         }
+    };
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        issue_half(t, 0);
+        issue_half(t, 1);
     };
     // the first NS tiles go in flight while Q is fetched
 #pragma unroll
@@ -247,47 +248,50 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
         }
     };
 
-    // ---- phases.  Slot s ends with a barrier.  The stage of tile u >= NS is
-    // refilled at slot 2u - 4 (its previous tile, u - NS, was last read in
-    // slot 2u - 5); before the barrier ending odd slot s, tile (s+1)/2 has
-    // landed (one later tile may still be in flight).
-    auto head_even = [&](int s) __attribute__((always_inline)) {
-        const int u = s / 2 + 2;
-        if (s >= 4 && u < ntiles) issue(u);
+    // ---- phases.  Slot s ends with a barrier.  For tile u >= NS the K rows
+    // are loaded at the start of slot 2u - 4 and the V rows at the start of
+    // slot 2u - 3 (the stage's previous tile, u - NS, was last read as K in
+    // slot 2u - 7 and as V in slot 2u - 5), so every slot carries half a
+    // tile of loads.  Before the barrier ending odd slot 2tv - 1, K_tv (and
+    // everything issued before it) has landed; V_tv, K_tv+1 and V_tv+1 may
+    // still be in flight.
+    auto head = [&](int s) __attribute__((always_inline)) {
+        const int u = (s >> 1) + 2;
+        if (s >= 4 && u < ntiles) issue_half(u, s & 1);
     };
     auto tail_odd = [&](int s) __attribute__((always_inline)) {
         const int tv = (s + 1) / 2;
         if (tv >= NS && tv < ntiles) {
-            if (tv + 1 < ntiles) wait_vm<kLoads>();
-            else wait_vm<0>();
+            if (tv + 1 < ntiles) wait_vm<3 * KT::kPerWave>();
+            else wait_vm<KT::kPerWave>();
         }
         lds_barrier();
     };
     lds_barrier();
     if (grp == 0) {
         // G(t) in slot 2t, X(t) in slot 2t + 1
-        head_even(0);
         do_s(0);
         lds_barrier();
         softmax(0);
         tail_odd(1);
         for (int t = 1; t <= ntiles; ++t) {
-            head_even(2 * t);
+            head(2 * t);
             gemm(t);
             lds_barrier();
+            head(2 * t + 1);
             softmax(t);                               // t == ntiles: past every wave's last tile
             tail_odd(2 * t + 1);
         }
     } else {
         // X(t-1) in slot 2t, G(t) in slot 2t + 1
-        head_even(0);
         lds_barrier();
         do_s(0);
         tail_odd(1);
         for (int t = 1; t <= ntiles; ++t) {
-            head_even(2 * t);
+            head(2 * t);
             softmax(t - 1);
             lds_barrier();
+            head(2 * t + 1);
             gemm(t);
             tail_odd(2 * t + 1);
         }
