@@ -252,6 +252,38 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return x * per + (x < rem ? x : rem) + i;
 }
 
+// Persistent launches: one workgroup per resident slot, each looping over
+// work items.  The hardware dispatches workgroups in order, so with items of
+// unequal length (causal row blocks) a non-persistent grid leaves CUs idle
+// while a busy XCD holds up the dispatch of the next workgroups.
+//
+// Items [0, total) are split into 8 contiguous ranges, one per XCD (workgroup
+// w runs on XCD w % 8), so that the items sharing K and V stay on one L2.
+// The Cx workgroups of an XCD take its items in rounds of Cx, alternating
+// direction every round: with items listed long-to-short inside each run of
+// row blocks, a workgroup that drew a long item in one round draws a short
+// one in the next.  With total <= gridDim.x every workgroup gets at most one
+// item, the mapping of xcd_remap.
+struct PersistentSched {
+    int first, cnt, c, cx;
+    __device__ __forceinline__ explicit PersistentSched(int total) {
+        constexpr int kXcd = 8;
+        const int x = blockIdx.x % kXcd, w = gridDim.x;
+        c = blockIdx.x / kXcd;
+        cx = w / kXcd + (x < w % kXcd ? 1 : 0);
+        const int per = total / kXcd, rem = total % kXcd;
+        first = x * per + (x < rem ? x : rem);
+        cnt = per + (x < rem ? 1 : 0);
+    }
+    // round r has items left for this XCD
+    __device__ __forceinline__ bool more(int r) const { return r * cx < cnt; }
+    // this workgroup's item in round r, or -1 (the last, partial round)
+    __device__ __forceinline__ int item(int r) const {
+        const int j = r * cx + ((r & 1) ? cx - 1 - c : c);
+        return j < cnt ? first + j : -1;
+    }
+};
+
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll

@@ -77,241 +77,250 @@ __device__ __forceinline__ void sched_gemm_phase() {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, float c2) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int N, float c2) {
     using Cfg = FwdBf16Cfg<D>;
     using KT = typename Cfg::KT;
     constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::kStages, KB = BN / 32;
     constexpr int kStage = Cfg::kStage, kLoads = Cfg::kLoads;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * kStage];
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: phase branches stay scalar
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int grp = wave >> 2;                                   // waves w and w+4 share a SIMD
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: phase branches stay scalar
+    const int grp = wave >> 2;                                           // waves w and w+4 share a SIMD
 
     const int nmb = (N + BM - 1) / BM;
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    const int mbi = lin % nmb, bh = lin / nmb;
-    const int h = bh % Hq, b = bh / Hq;
-    const int mb = CAUSAL ? nmb - 1 - mbi : mbi;      // longest causal rows first
-    const int g = h / (Hq / Hkv);
-    const uint16_t* Qh = Q + ((int64_t)b * Hq + h) * N * D;
-    const uint16_t* Kh = K + ((int64_t)b * Hkv + g) * N * D;
-    const uint16_t* Vh = V + ((int64_t)b * Hkv + g) * N * D;
+    const PersistentSched sched(nmb * Hq * B);
+    for (int r = 0; sched.more(r); ++r) {
+        const int lin = sched.item(r);
+        if (lin < 0) continue;
+        const int lane = threadIdx.x & 63;
+        const int l32 = lane & 31, hh = lane >> 5;
+        const int mbi = lin % nmb, bh = lin / nmb;
+        const int h = bh % Hq, b = bh / Hq;
+        const int mb = CAUSAL ? nmb - 1 - mbi : mbi;      // longest causal rows first
+        const int g = h / (Hq / Hkv);
+        const uint16_t* Qh = Q + ((int64_t)b * Hq + h) * N * D;
+        const uint16_t* Kh = K + ((int64_t)b * Hkv + g) * N * D;
+        const uint16_t* Vh = V + ((int64_t)b * Hkv + g) * N * D;
 
-    const int q0 = mb * BM;
-    const int qw = q0 + 32 * wave;                    // first query row of this wave
-    const int qrow = qw + l32;                        // this lane's query row
-    const int kend = CAUSAL ? min(N, q0 + BM) : N;
-    const int ntiles = (kend + BN - 1) / BN;          // tiles of the workgroup
-    const int ntw = qw >= N ? 0 : CAUSAL ? (min(N, qw + 32) + BN - 1) / BN : ntiles;   // tiles of this wave
+        const int q0 = mb * BM;
+        const int qw = q0 + 32 * wave;                    // first query row of this wave
+        const int qrow = qw + l32;                        // this lane's query row
+        const int kend = CAUSAL ? min(N, q0 + BM) : N;
+        const int ntiles = (kend + BN - 1) / BN;          // tiles of the workgroup
+        const int ntw = qw >= N ? 0 : CAUSAL ? (min(N, qw + 32) + BN - 1) / BN : ntiles;   // tiles of this wave
 
-    // ---- direct loads: this wave's row groups of a K/V tile, as byte offsets
-    // from the tile's first row (rows past the end re-read the last row)
-    uint32_t voff[KT::kPerWave];
+        // ---- direct loads: this wave's row groups of a K/V tile, as byte offsets
+        // from the tile's first row (rows past the end re-read the last row)
+        uint32_t voff[KT::kPerWave];
 #pragma unroll
-    for (int i = 0; i < KT::kPerWave; ++i) {
-        const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
-        voff[i] = (uint32_t)(row * D + (lane / KT::RG) * 8) * 2u;
-    }
-    // half = 0: the K rows of tile t, 1: its V rows
-    auto issue_half = [&](int t, const int half) __attribute__((always_inline)) {
-        const uint32_t st = lds_addr(smem + (t % NS) * kStage) + half * KT::kBytes;
-        const uint16_t* src = (half ? Vh : Kh) + (int64_t)t * BN * D;
-        const int rows_valid = N - t * BN;
-        if (rows_valid >= BN) {
+        for (int i = 0; i < KT::kPerWave; ++i) {
+            const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
+            voff[i] = (uint32_t)(row * D + (lane / KT::RG) * 8) * 2u;
+        }
+        // half = 0: the K rows of tile t, 1: its V rows
+        auto issue_half = [&](int t, const int half) __attribute__((always_inline)) {
+            const uint32_t st = lds_addr(smem + (t % NS) * kStage) + half * KT::kBytes;
+            const uint16_t* src = (half ? Vh : Kh) + (int64_t)t * BN * D;
+            const int rows_valid = N - t * BN;
+            if (rows_valid >= BN) {
 #pragma unroll
-            for (int i = 0; i < KT::kPerWave; ++i) dma16s(src, voff[i], st + (i * NW + wave) * KT::RGS);
-        } else {
+                for (int i = 0; i < KT::kPerWave; ++i) dma16s(src, voff[i], st + (i * NW + wave) * KT::RGS);
+            } else {
 #pragma unroll
-            for (int i = 0; i < KT::kPerWave; ++i) {
-                const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
-                const int grow = row < rows_valid ? row : rows_valid - 1;
-                const uint32_t off = (uint32_t)(grow * D + (lane / KT::RG) * 8) * 2u;
-                dma16s(src, off, st + (i * NW + wave) * KT::RGS);
+                for (int i = 0; i < KT::kPerWave; ++i) {
+                    const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
+                    const int grow = row < rows_valid ? row : rows_valid - 1;
+                    const uint32_t off = (uint32_t)(grow * D + (lane / KT::RG) * 8) * 2u;
+                    dma16s(src, off, st + (i * NW + wave) * KT::RGS);
+                }
             }
+        };
+        auto issue = [&](int t) __attribute__((always_inline)) {
+            issue_half(t, 0);
+            issue_half(t, 1);
+        };
+        // the first NS tiles go in flight while Q is fetched
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+            if (t < ntiles) issue(t);
+
+        u32x4 qf[D / 16];                                 // Q block as B operands, for the whole kernel
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            u32x4 v = {};
+            if (qrow < N) v = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + 16 * s + 8 * hh);
+            qf[s] = v;
         }
-    };
-    auto issue = [&](int t) __attribute__((always_inline)) {
-        issue_half(t, 0);
-        issue_half(t, 1);
-    };
-    // the first NS tiles go in flight while Q is fetched
 #pragma unroll
-    for (int t = 0; t < NS; ++t)
-        if (t < ntiles) issue(t);
+        for (int s = 0; s < D / 16; ++s) settle(qf[s]);
+        wait_vm<0>();
 
-    u32x4 qf[D / 16];                                 // Q block as B operands, for the whole kernel
+        f32x16 oacc[D / 32];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-        u32x4 v = {};
-        if (qrow < N) v = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + 16 * s + 8 * hh);
-        qf[s] = v;
-    }
+        for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
+        float m = kNegBig, lsum = 0.f;
+        f32x16 sacc[KB];
+        u32x4 pf[KB][2];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) settle(qf[s]);
-    wait_vm<0>();
-
-    f32x16 oacc[D / 32];
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
-    float m = kNegBig, lsum = 0.f;
-    f32x16 sacc[KB];
-    u32x4 pf[KB][2];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        sacc[kb] = zero16();
-        pf[kb][0] = pf[kb][1] = u32x4{};
-    }
-
-    // S^T = K_t Q^T (stage t % NS): rows = keys, columns = this wave's queries
-    auto do_s = [&](int t) __attribute__((always_inline)) {
-        const uint16_t* Ks = smem + (t % NS) * kStage;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) sacc[kb] = zero16();
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) sacc[kb] = mma_bf16(KT::row8(Ks, 32 * kb + l32, 2 * s + hh), qf[s], sacc[kb]);
-    };
-    // O^T += V_t^T P_t^T
-    auto do_pv = [&](int t) __attribute__((always_inline)) {
-        const uint16_t* Vs = smem + (t % NS) * kStage + KT::kElems;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-                for (int ct = 0; ct < D / 32; ++ct)
-                    oacc[ct] = mma_bf16(KT::tr8(Vs, 32 * kb + 16 * t2, 32 * ct, lane), pf[kb][t2], oacc[ct]);
-    };
-    // G(t), t >= 1: scores of tile t (past this wave's last tile they are
-    // discarded) and the product of tile t-1 (P is zero past the last tile)
-    auto gemm = [&](int t) __attribute__((always_inline)) {
-        do_s(t);
-        do_pv(t - 1);
-        sched_gemm_phase<D>();
-    };
-    // X(t)
-    auto softmax = [&](int t) __attribute__((always_inline)) {
-        if (t >= ntw) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) pf[kb][0] = pf[kb][1] = u32x4{};
-            return;
+        for (int kb = 0; kb < KB; ++kb) {
+            sacc[kb] = zero16();
+            pf[kb][0] = pf[kb][1] = u32x4{};
         }
-        const int k0 = t * BN;
-        // ---- keys past the diagonal (causal) or past the end
-        if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
+
+        // S^T = K_t Q^T (stage t % NS): rows = keys, columns = this wave's queries
+        auto do_s = [&](int t) __attribute__((always_inline)) {
+            const uint16_t* Ks = smem + (t % NS) * kStage;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sacc[kb] = zero16();
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) sacc[kb] = mma_bf16(KT::row8(Ks, 32 * kb + l32, 2 * s + hh), qf[s], sacc[kb]);
+        };
+        // O^T += V_t^T P_t^T
+        auto do_pv = [&](int t) __attribute__((always_inline)) {
+            const uint16_t* Vs = smem + (t % NS) * kStage + KT::kElems;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * kb + acc_row(r, hh);
-                    if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r] = -INFINITY;
+                for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                    for (int ct = 0; ct < D / 32; ++ct)
+                        oacc[ct] = mma_bf16(KT::tr8(Vs, 32 * kb + 16 * t2, 32 * ct, lane), pf[kb][t2], oacc[ct]);
+        };
+        // G(t), t >= 1: scores of tile t (past this wave's last tile they are
+        // discarded) and the product of tile t-1 (P is zero past the last tile)
+        auto gemm = [&](int t) __attribute__((always_inline)) {
+            do_s(t);
+            do_pv(t - 1);
+            sched_gemm_phase<D>();
+        };
+        // X(t)
+        auto softmax = [&](int t) __attribute__((always_inline)) {
+            if (t >= ntw) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) pf[kb][0] = pf[kb][1] = u32x4{};
+                return;
+            }
+            const int k0 = t * BN;
+            // ---- keys past the diagonal (causal) or past the end
+            if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
+                // row indices from an opaque copy of the lane half: hoisted
+                // out of the item loop, they and the masks derived from them
+                // would stay live in registers
+                int hm = hh;
+                asm volatile("" : "+v"(hm));
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * kb + acc_row(r, hm);
+                        if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r] = -INFINITY;
+                    }
+            }
+            // ---- running max (base 2, scale*log2(e) in c2); moved only when some
+            // row of the wave grew by more than 2^tau
+            float x = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x = fmaxf(x, sacc[kb][r]);
+            x = pair_max(x);
+            const float mnew = fmaxf(m, x * c2);
+            if (__any(mnew > m + Cfg::kTau)) {
+                const float alpha = fast_exp2(m - mnew);
+                m = mnew;
+                lsum *= alpha;
+#pragma unroll
+                for (int ct = 0; ct < D / 32; ++ct) oacc[ct] *= alpha;
+            }
+            // ---- P = exp2(c2 s - m), packed to bf16; l sums the rounded values
+            float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c2, -m));
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    pf[kb][t2] = pack_bf16x8(sacc[kb], 8 * t2);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) rs[i] = dot2_bf16_sum(pf[kb][t2][i], rs[i]);
                 }
-        }
-        // ---- running max (base 2, scale*log2(e) in c2); moved only when some
-        // row of the wave grew by more than 2^tau
-        float x = -INFINITY;
+            }
+            lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+            // P is finished inside this phase (not sunk into the next matrix phase)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) x = fmaxf(x, sacc[kb][r]);
-        x = pair_max(x);
-        const float mnew = fmaxf(m, x * c2);
-        if (__any(mnew > m + Cfg::kTau)) {
-            const float alpha = fast_exp2(m - mnew);
-            m = mnew;
-            lsum *= alpha;
-#pragma unroll
-            for (int ct = 0; ct < D / 32; ++ct) oacc[ct] *= alpha;
-        }
-        // ---- P = exp2(c2 s - m), packed to bf16; l sums the rounded values
-        float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c2, -m));
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-                pf[kb][t2] = pack_bf16x8(sacc[kb], 8 * t2);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) rs[i] = dot2_bf16_sum(pf[kb][t2][i], rs[i]);
+            for (int kb = 0; kb < KB; ++kb) {
+                settle(pf[kb][0]);
+                settle(pf[kb][1]);
+            }
+        };
+
+        // ---- phases.  Slot s ends with a barrier.  For tile u >= NS the K rows
+        // are loaded at the start of slot 2u - 4 and the V rows at the start of
+        // slot 2u - 3 (the stage's previous tile, u - NS, was last read as K in
+        // slot 2u - 7 and as V in slot 2u - 5), so every slot carries half a
+        // tile of loads.  Before the barrier ending odd slot 2tv - 1, K_tv (and
+        // everything issued before it) has landed; V_tv, K_tv+1 and V_tv+1 may
+        // still be in flight.
+        auto head = [&](int s) __attribute__((always_inline)) {
+            const int u = (s >> 1) + 2;
+            if (s >= 4 && u < ntiles) issue_half(u, s & 1);
+        };
+        auto tail_odd = [&](int s) __attribute__((always_inline)) {
+            const int tv = (s + 1) / 2;
+            if (tv >= NS && tv < ntiles) {
+                if (tv + 1 < ntiles) wait_vm<3 * KT::kPerWave>();
+                else wait_vm<KT::kPerWave>();
+            }
+            lds_barrier();
+        };
+        lds_barrier();
+        if (grp == 0) {
+            // G(t) in slot 2t, X(t) in slot 2t + 1
+            do_s(0);
+            lds_barrier();
+            softmax(0);
+            tail_odd(1);
+            for (int t = 1; t <= ntiles; ++t) {
+                head(2 * t);
+                gemm(t);
+                lds_barrier();
+                head(2 * t + 1);
+                softmax(t);                               // t == ntiles: past every wave's last tile
+                tail_odd(2 * t + 1);
+            }
+        } else {
+            // X(t-1) in slot 2t, G(t) in slot 2t + 1
+            lds_barrier();
+            do_s(0);
+            tail_odd(1);
+            for (int t = 1; t <= ntiles; ++t) {
+                head(2 * t);
+                softmax(t - 1);
+                lds_barrier();
+                head(2 * t + 1);
+                gemm(t);
+                tail_odd(2 * t + 1);
             }
         }
-        lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-        // P is finished inside this phase (not sunk into the next matrix phase)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            settle(pf[kb][0]);
-            settle(pf[kb][1]);
-        }
-    };
 
-    // ---- phases.  Slot s ends with a barrier.  For tile u >= NS the K rows
-    // are loaded at the start of slot 2u - 4 and the V rows at the start of
-    // slot 2u - 3 (the stage's previous tile, u - NS, was last read as K in
-    // slot 2u - 7 and as V in slot 2u - 5), so every slot carries half a
-    // tile of loads.  Before the barrier ending odd slot 2tv - 1, K_tv (and
-    // everything issued before it) has landed; V_tv, K_tv+1 and V_tv+1 may
-    // still be in flight.
-    auto head = [&](int s) __attribute__((always_inline)) {
-        const int u = (s >> 1) + 2;
-        if (s >= 4 && u < ntiles) issue_half(u, s & 1);
-    };
-    auto tail_odd = [&](int s) __attribute__((always_inline)) {
-        const int tv = (s + 1) / 2;
-        if (tv >= NS && tv < ntiles) {
-            if (tv + 1 < ntiles) wait_vm<3 * KT::kPerWave>();
-            else wait_vm<KT::kPerWave>();
-        }
-        lds_barrier();
-    };
-    lds_barrier();
-    if (grp == 0) {
-        // G(t) in slot 2t, X(t) in slot 2t + 1
-        do_s(0);
-        lds_barrier();
-        softmax(0);
-        tail_odd(1);
-        for (int t = 1; t <= ntiles; ++t) {
-            head(2 * t);
-            gemm(t);
-            lds_barrier();
-            head(2 * t + 1);
-            softmax(t);                               // t == ntiles: past every wave's last tile
-            tail_odd(2 * t + 1);
-        }
-    } else {
-        // X(t-1) in slot 2t, G(t) in slot 2t + 1
-        lds_barrier();
-        do_s(0);
-        tail_odd(1);
-        for (int t = 1; t <= ntiles; ++t) {
-            head(2 * t);
-            softmax(t - 1);
-            lds_barrier();
-            head(2 * t + 1);
-            gemm(t);
-            tail_odd(2 * t + 1);
-        }
-    }
-
-    // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
-    const float ltot = pair_sum(lsum);
-    if (qrow < N) {
-        const float inv = 1.0f / ltot;
-        uint16_t* Orow = O + (((int64_t)b * Hq + h) * N + qrow) * D;
+        // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
+        const float ltot = pair_sum(lsum);
+        if (qrow < N) {
+            const float inv = 1.0f / ltot;
+            uint16_t* Orow = O + (((int64_t)b * Hq + h) * N + qrow) * D;
 #pragma unroll
-        for (int ct = 0; ct < D / 32; ++ct)
+            for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                u32x2 w;
-                w[0] = pack_bf16x2(oacc[ct][4 * gq] * inv, oacc[ct][4 * gq + 1] * inv);
-                w[1] = pack_bf16x2(oacc[ct][4 * gq + 2] * inv, oacc[ct][4 * gq + 3] * inv);
-                *reinterpret_cast<u32x2*>(Orow + 32 * ct + 8 * gq + 4 * hh) = w;
-            }
-        if (hh == 0) LSE[((int64_t)b * Hq + h) * N + qrow] = (m + log2f(ltot)) * kLn2;
+                for (int gq = 0; gq < 4; ++gq) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(oacc[ct][4 * gq] * inv, oacc[ct][4 * gq + 1] * inv);
+                    w[1] = pack_bf16x2(oacc[ct][4 * gq + 2] * inv, oacc[ct][4 * gq + 3] * inv);
+                    *reinterpret_cast<u32x2*>(Orow + 32 * ct + 8 * gq + 4 * hh) = w;
+                }
+            if (hh == 0) LSE[((int64_t)b * Hq + h) * N + qrow] = (m + log2f(ltot)) * kLn2;
+        }
     }
 }
 
@@ -320,8 +329,10 @@ static hipError_t launch(const void* q, const void* k, const void* v, void* o, f
                          int N, float scale, hipStream_t st) {
     using Cfg = FwdBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)nmb * Hq * B)), dim3(Cfg::kThreads), 0,
-                       st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, Hq, Hkv, N,
+    static std::atomic<int> slots{0};
+    const int grid = persistent_grid((const void*)fwd_bf16_kernel<D, CAUSAL>, Cfg::kThreads, nmb * Hq * B, slots);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, B, Hq, Hkv, N,
                        scale * kLog2e);
     return hipGetLastError();
 }

@@ -5,7 +5,30 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <atomic>
+
 namespace fa {
+
+// Workgroups of a persistent launch: every resident slot of the current
+// device (CUs x workgroups per CU), at most `items`.  The CU count and the
+// kernel's occupancy are queried once and kept in `cache` (a property of the
+// device and the code object, the same on every call); if a query fails the
+// grid is `items`, one item per workgroup, which the kernels' schedule also
+// handles.
+inline int persistent_grid(const void* kernel, int threads, int items, std::atomic<int>& cache) {
+    int slots = cache.load(std::memory_order_relaxed);
+    if (slots == 0) {
+        int dev = 0, cus = 0, per = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess || cus <= 0 ||
+            per <= 0)
+            return items;
+        slots = cus * per;
+        cache.store(slots, std::memory_order_relaxed);
+    }
+    return items < slots ? items : slots;
+}
 
 // dtype: 0 = float32, 1 = bfloat16 (fp8 goes through launch_fwd_fp8)
 hipError_t launch_fwd(int dtype, int d, int causal, const void* q, const void* k, const void* v,
