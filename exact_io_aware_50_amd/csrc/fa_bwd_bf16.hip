@@ -72,7 +72,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Hq, int Hkv, int N, int Npad, float c2,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int n_rows, int Npad, float c2,
     float scale) {
     using Cfg = KVBf16Cfg<D>;
     using QT = typename Cfg::QT;
@@ -91,255 +91,269 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
     const int l32 = lane & 31, hh = lane >> 5;
     const int grp = wave >> 2;                      // waves w and w+4 share a SIMD
 
-    const int nkb = (N + BNK - 1) / BNK;
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    const int kbk = lin % nkb, bg = lin / nkb;      // ascending key blocks: causal-heavy first
-    const int g = bg % Hkv, b = bg / Hkv;
-    const int G = Hq / Hkv;
-    const int k0 = kbk * BNK;
-    const int kw = k0 + 32 * wave;
-    const int krow = kw + l32;
+    const int nkb = (n_rows + BNK - 1) / BNK;
+    const PersistentSched sched(nkb * Hkv * B);
+    for (int r = 0; sched.more(r); ++r) {
+        const int lin = sched.item(r);
+        if (lin < 0) continue;
+        // the sequence length as an opaque per-item value: whatever derives
+        // from it (tail clamps and masks) is computed per item, not hoisted
+        // out of the item loop into registers for the whole kernel
+        int N = n_rows;
+        asm volatile("" : "+s"(N));
+        const int kbk = lin % nkb, bg = lin / nkb;      // ascending key blocks: causal-heavy first
+        const int g = bg % Hkv, b = bg / Hkv;
+        const int G = Hq / Hkv;
+        const int k0 = kbk * BNK;
+        const int kw = k0 + 32 * wave;
+        const int krow = kw + l32;
 
-    const uint16_t* Kg = K + ((int64_t)b * Hkv + g) * N * D;
-    const uint16_t* Vg = V + ((int64_t)b * Hkv + g) * N * D;
+        const uint16_t* Kg = K + ((int64_t)b * Hkv + g) * N * D;
+        const uint16_t* Vg = V + ((int64_t)b * Hkv + g) * N * D;
 
-    const int nqt = (N + BMQ - 1) / BMQ;
-    const int qt0 = CAUSAL ? k0 / BMQ : 0;          // earlier query blocks see none of these keys
-    const int total = G * (nqt - qt0);              // steps: (head g*G + i / (nqt-qt0), block qt0 + i % (nqt-qt0))
+        const int nqt = (N + BMQ - 1) / BMQ;
+        const int qt0 = CAUSAL ? k0 / BMQ : 0;          // earlier query blocks see none of these keys
+        const int total = G * (nqt - qt0);              // steps: (head g*G + i / (nqt-qt0), block qt0 + i % (nqt-qt0))
 
-    // ---- direct loads of step u (issued in step order: one running position).
-    // The per-lane offsets are recomputed at every issue from an opaque copy
-    // of the lane index: kept live across the loop they would be spilled, and
-    // a scratch reload is a vector-memory load whose wait would also drain
-    // the tile loads in flight.
-    int ih = 0, iq = qt0;                           // head offset and query block of the next step to load
-    int u_next = 0;
-    auto issue = [&](int u) __attribute__((always_inline)) {
-        const int64_t bh = (int64_t)b * Hq + g * G + ih;
-        const int q0 = iq * BMQ;
-        const uint32_t st = lds_addr(smem + (u % NS) * Cfg::kStageBytes);
-        const uint16_t* qb = Q + (bh * N + q0) * D;
-        const uint16_t* ob = dO + (bh * N + q0) * D;
-        const int rows_valid = N - q0;
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
+        // ---- direct loads of step u (issued in step order: one running position).
+        // The per-lane offsets are recomputed at every issue from an opaque copy
+        // of the lane index: kept live across the loop they would be spilled, and
+        // a scratch reload is a vector-memory load whose wait would also drain
+        // the tile loads in flight.
+        int ih = 0, iq = qt0;                           // head offset and query block of the next step to load
+        int u_next = 0;
+        auto issue = [&](int u) __attribute__((always_inline)) {
+            const int64_t bh = (int64_t)b * Hq + g * G + ih;
+            const int q0 = iq * BMQ;
+            const uint32_t st = lds_addr(smem + (u % NS) * Cfg::kStageBytes);
+            const uint16_t* qb = Q + (bh * N + q0) * D;
+            const uint16_t* ob = dO + (bh * N + q0) * D;
+            const int rows_valid = N - q0;
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
 #pragma unroll
-        for (int i = 0; i < QT::kPerWave; ++i) {
-            const int row = (i * NW + wave) * QT::RG + ln % QT::RG;
-            const int grow = row < rows_valid ? row : rows_valid - 1;
-            const uint32_t off = (uint32_t)(grow * D + (ln / QT::RG) * 8) * 2u;
-            dma16s(qb, off, st + (i * NW + wave) * QT::RGS);
-            dma16s(ob, off, st + QT::kBytes + (i * NW + wave) * QT::RGS);
-        }
-        // statistics: chunk c < BMQ/4 holds LSE*log2e rows q0+4c.., the rest D rows
-        const int c = wave * Cfg::kStatPerWave + lane;
-        if (lane < Cfg::kStatPerWave) {
-            const float* src = c < BMQ / 4 ? WSl + bh * Npad + q0 + 4 * c : WSd + bh * Npad + q0 + 4 * (c - BMQ / 4);
-            dma16(src, st + 2 * QT::kBytes + 16 * wave * Cfg::kStatPerWave);
-        }
-        if (++iq == nqt) {
-            iq = qt0;
-            ++ih;
-        }
-        (void)u;
-    };
-    VT::load(Vg + (int64_t)k0 * D, N - k0, Vl, wave, lane);
-#pragma unroll
-    for (int t = 0; t < NS; ++t)
-        if (t < total) {
-            issue(u_next);
-            ++u_next;
-        }
-
-    u32x4 kf[D / 16];
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-        u32x4 a = {};
-        if (krow < N) a = *reinterpret_cast<const u32x4*>(Kg + (int64_t)krow * D + 16 * s + 8 * hh);
-        kf[s] = a;
-    }
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) settle(kf[s]);
-    wait_vm<0>();
-
-    f32x16 dkacc[D / 32], dvacc[D / 32];
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) dkacc[i] = dvacc[i] = zero16();
-    f32x16 sacc[QB], dpacc[QB];
-    u32x4 pb[QB][2], sb[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        sacc[qb] = dpacc[qb] = zero16();
-        pb[qb][0] = pb[qb][1] = sb[qb][0] = sb[qb][1] = u32x4{};
-    }
-
-    // S = Q K^T and dP = dO V^T of step i: rows = queries, columns = this wave's keys
-    auto do_sdp = [&](int i) __attribute__((always_inline)) {
-        const char* st = smem + (i % NS) * Cfg::kStageBytes;
-        const uint16_t* Qs = (const uint16_t*)st;
-        const uint16_t* dOs = (const uint16_t*)(st + QT::kBytes);
-        // the V fragments are the same every step; an opaque zero offset keeps
-        // their reads here instead of hoisted (and held) outside the loop
-        int vz = 0;
-        asm volatile("" : "+s"(vz));
-        const uint16_t* Vw = Vl + vz;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[qb] = dpacc[qb] = zero16();
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                sacc[qb] = mma_bf16(QT::row8(Qs, 32 * qb + l32, 2 * s + hh), kf[s], sacc[qb]);
-                dpacc[qb] = mma_bf16(QT::row8(dOs, 32 * qb + l32, 2 * s + hh),
-                                     VT::row8(Vw, 32 * wave + l32, 2 * s + hh), dpacc[qb]);
+            for (int i = 0; i < QT::kPerWave; ++i) {
+                const int row = (i * NW + wave) * QT::RG + ln % QT::RG;
+                const int grow = row < rows_valid ? row : rows_valid - 1;
+                const uint32_t off = (uint32_t)(grow * D + (ln / QT::RG) * 8) * 2u;
+                dma16s(qb, off, st + (i * NW + wave) * QT::RGS);
+                dma16s(ob, off, st + QT::kBytes + (i * NW + wave) * QT::RGS);
             }
-    };
-    // dV^T += dO_i^T P_i ;  dK^T += Q_i^T dS_i
-    auto do_dvdk = [&](int i) __attribute__((always_inline)) {
-        const char* st = smem + (i % NS) * Cfg::kStageBytes;
-        const uint16_t* Qs = (const uint16_t*)st;
-        const uint16_t* dOs = (const uint16_t*)(st + QT::kBytes);
+            // statistics: chunk c < BMQ/4 holds LSE*log2e rows q0+4c.., the rest D rows
+            const int c = wave * Cfg::kStatPerWave + lane;
+            if (lane < Cfg::kStatPerWave) {
+                const float* src = c < BMQ / 4 ? WSl + bh * Npad + q0 + 4 * c : WSd + bh * Npad + q0 + 4 * (c - BMQ / 4);
+                dma16(src, st + 2 * QT::kBytes + 16 * wave * Cfg::kStatPerWave);
+            }
+            if (++iq == nqt) {
+                iq = qt0;
+                ++ih;
+            }
+            (void)u;
+        };
+        VT::load(Vg + (int64_t)k0 * D, N - k0, Vl, wave, lane);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+        for (int t = 0; t < NS; ++t)
+            if (t < total) {
+                issue(u_next);
+                ++u_next;
+            }
+
+        u32x4 kf[D / 16];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int ct = 0; ct < D / 32; ++ct) {
-                    dvacc[ct] = mma_bf16(QT::tr8(dOs, 32 * qb + 16 * t, 32 * ct, lane), pb[qb][t], dvacc[ct]);
-                    dkacc[ct] = mma_bf16(QT::tr8(Qs, 32 * qb + 16 * t, 32 * ct, lane), sb[qb][t], dkacc[ct]);
-                }
-    };
-    // G(i), i >= 1 (i == total: the products of the last step only)
-    auto gemm = [&](int i) __attribute__((always_inline)) {
-        do_dvdk(i - 1);
-        do_sdp(i);
-        sched_dkdv_phase<D == 128 ? 8 : 4>();
-    };
-    // X(i): step i's query block is xq
-    int xq = qt0;
-    auto softmax = [&](int i) __attribute__((always_inline)) {
-        if (i >= total) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) pb[qb][0] = pb[qb][1] = sb[qb][0] = sb[qb][1] = u32x4{};
-            return;
+        for (int s = 0; s < D / 16; ++s) {
+            u32x4 a = {};
+            if (krow < N) a = *reinterpret_cast<const u32x4*>(Kg + (int64_t)krow * D + 16 * s + 8 * hh);
+            kf[s] = a;
         }
-        const int q0 = xq * BMQ;
-        if (++xq == nqt) xq = qt0;
-        const float* sl = (const float*)(smem + (i % NS) * Cfg::kStageBytes + 2 * QT::kBytes);
-        // causal: key krow is hidden from query q0 + 32*qb + row(r) iff
-        // delta > 8*(r/4) + r%4, delta = krow - q0 - 32*qb - 4*hh; steps whose
-        // queries all follow this wave's keys skip the test (uniform branch)
-        const bool need_mask = CAUSAL && kw + 31 > q0;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) settle(kf[s]);
+        wait_vm<0>();
+
+        f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) dkacc[i] = dvacc[i] = zero16();
+        f32x16 sacc[QB], dpacc[QB];
+        u32x4 pb[QB][2], sb[QB][2];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 32 * qb + 8 * gq + 4 * hh);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * gq + j;
-                    sacc[qb][r] = fast_exp2(fmaf(sacc[qb][r], c2, -l4[j]));
-                }
-            }
-            if (need_mask) {
-                const int delta = krow - q0 - 32 * qb - 4 * hh;
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (delta > 8 * (r / 4) + r % 4) sacc[qb][r] = 0.f;
-            }
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + BMQ + 32 * qb + 8 * gq + 4 * hh);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * gq + j;
-                    dpacc[qb][r] = sacc[qb][r] * (dpacc[qb][r] - d4[j]);
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                pb[qb][t] = pack_bf16x8(sacc[qb], 8 * t);
-                sb[qb][t] = pack_bf16x8(dpacc[qb], 8 * t);
-            }
-            // one query block at a time (its statistics reads are not hoisted
-            // above the previous block's arithmetic)
-            __builtin_amdgcn_sched_barrier(0);
+            sacc[qb] = dpacc[qb] = zero16();
+            pb[qb][0] = pb[qb][1] = sb[qb][0] = sb[qb][1] = u32x4{};
         }
-        // the packed operands are finished here, inside this phase (not sunk
-        // past the barrier into the next matrix phase)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                settle(pb[qb][t]);
-                settle(sb[qb][t]);
-            }
-    };
 
-    // ---- phases (slot s ends with a barrier).  In loop round i both groups
-    // load step i+NS-2 (that stage held step i-2, last read in slot 2i-1) at
-    // the start of their vector phase (slot 2i+1 for the first group, 2i for
-    // the second); before the barrier ending odd slot s, step tv = (s+1)/2
-    // has landed, while up to NS-3 later steps may still be in flight.
-    static_assert(NS >= 4 && (NS - 3) * kLoads <= 63, "vmcnt range");
-    auto refill = [&](int i) __attribute__((always_inline)) {
-        if (i >= 2 && i + NS - 2 < total) {
-            issue(u_next);
-            ++u_next;
-        }
-    };
-    auto tail_odd = [&](int s) __attribute__((always_inline)) {
-        const int tv = (s + 1) / 2;
-        if (tv >= NS && tv < total) {
-            const int later = min(NS - 3, total - 1 - tv);
-            wait_vm_dyn<kLoads, NS - 3>(later);
-        }
-        lds_barrier();
-    };
-    lds_barrier();
-    if (grp == 0) {
-        // G(i) in slot 2i, X(i) in slot 2i + 1
-        do_sdp(0);
-        lds_barrier();
-        softmax(0);
-        tail_odd(1);
-        for (int i = 1; i <= total; ++i) {
-            gemm(i);
-            lds_barrier();
-            refill(i);
-            softmax(i);
-            tail_odd(2 * i + 1);
-        }
-    } else {
-        // X(i-1) in slot 2i, G(i) in slot 2i + 1
-        lds_barrier();
-        do_sdp(0);
-        tail_odd(1);
-        for (int i = 1; i <= total; ++i) {
-            refill(i);
-            softmax(i - 1);
-            lds_barrier();
-            gemm(i);
-            tail_odd(2 * i + 1);
-        }
-    }
-
-    if (krow < N) {
-        uint16_t* dKr = dK + (((int64_t)b * Hkv + g) * N + krow) * D;
-        uint16_t* dVr = dV + (((int64_t)b * Hkv + g) * N + krow) * D;
+        // S = Q K^T and dP = dO V^T of step i: rows = queries, columns = this wave's keys
+        auto do_sdp = [&](int i) __attribute__((always_inline)) {
+            const char* st = smem + (i % NS) * Cfg::kStageBytes;
+            const uint16_t* Qs = (const uint16_t*)st;
+            const uint16_t* dOs = (const uint16_t*)(st + QT::kBytes);
+            // the V fragments are the same every step; an opaque zero offset keeps
+            // their reads here instead of hoisted (and held) outside the loop
+            int vz = 0;
+            asm volatile("" : "+s"(vz));
+            const uint16_t* Vw = Vl + vz;
 #pragma unroll
-        for (int ct = 0; ct < D / 32; ++ct)
+            for (int qb = 0; qb < QB; ++qb) sacc[qb] = dpacc[qb] = zero16();
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int c = 32 * ct + 8 * gq + 4 * hh;
-                u32x2 wk, wv;
-                wk[0] = pack_bf16x2(dkacc[ct][4 * gq] * scale, dkacc[ct][4 * gq + 1] * scale);
-                wk[1] = pack_bf16x2(dkacc[ct][4 * gq + 2] * scale, dkacc[ct][4 * gq + 3] * scale);
-                wv[0] = pack_bf16x2(dvacc[ct][4 * gq], dvacc[ct][4 * gq + 1]);
-                wv[1] = pack_bf16x2(dvacc[ct][4 * gq + 2], dvacc[ct][4 * gq + 3]);
-                *reinterpret_cast<u32x2*>(dKr + c) = wk;
-                *reinterpret_cast<u32x2*>(dVr + c) = wv;
+            for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    sacc[qb] = mma_bf16(QT::row8(Qs, 32 * qb + l32, 2 * s + hh), kf[s], sacc[qb]);
+                    dpacc[qb] = mma_bf16(QT::row8(dOs, 32 * qb + l32, 2 * s + hh),
+                                         VT::row8(Vw, 32 * wave + l32, 2 * s + hh), dpacc[qb]);
+                }
+        };
+        // dV^T += dO_i^T P_i ;  dK^T += Q_i^T dS_i
+        auto do_dvdk = [&](int i) __attribute__((always_inline)) {
+            const char* st = smem + (i % NS) * Cfg::kStageBytes;
+            const uint16_t* Qs = (const uint16_t*)st;
+            const uint16_t* dOs = (const uint16_t*)(st + QT::kBytes);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int ct = 0; ct < D / 32; ++ct) {
+                        dvacc[ct] = mma_bf16(QT::tr8(dOs, 32 * qb + 16 * t, 32 * ct, lane), pb[qb][t], dvacc[ct]);
+                        dkacc[ct] = mma_bf16(QT::tr8(Qs, 32 * qb + 16 * t, 32 * ct, lane), sb[qb][t], dkacc[ct]);
+                    }
+        };
+        // G(i), i >= 1 (i == total: the products of the last step only)
+        auto gemm = [&](int i) __attribute__((always_inline)) {
+            do_dvdk(i - 1);
+            do_sdp(i);
+            sched_dkdv_phase<D == 128 ? 8 : 4>();
+        };
+        // X(i): step i's query block is xq
+        int xq = qt0;
+        auto softmax = [&](int i) __attribute__((always_inline)) {
+            if (i >= total) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) pb[qb][0] = pb[qb][1] = sb[qb][0] = sb[qb][1] = u32x4{};
+                return;
             }
+            const int q0 = xq * BMQ;
+            if (++xq == nqt) xq = qt0;
+            const float* sl = (const float*)(smem + (i % NS) * Cfg::kStageBytes + 2 * QT::kBytes);
+            // causal: key krow is hidden from query q0 + 32*qb + row(r) iff
+            // delta > 8*(r/4) + r%4, delta = krow - q0 - 32*qb - 4*hh; steps whose
+            // queries all follow this wave's keys skip the test (uniform branch)
+            const bool need_mask = CAUSAL && kw + 31 > q0;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + 32 * qb + 8 * gq + 4 * hh);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 4 * gq + j;
+                        sacc[qb][r] = fast_exp2(fmaf(sacc[qb][r], c2, -l4[j]));
+                    }
+                }
+                if (need_mask) {
+                    const int delta = krow - q0 - 32 * qb - 4 * hh;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (delta > 8 * (r / 4) + r % 4) sacc[qb][r] = 0.f;
+                }
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + BMQ + 32 * qb + 8 * gq + 4 * hh);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 4 * gq + j;
+                        dpacc[qb][r] = sacc[qb][r] * (dpacc[qb][r] - d4[j]);
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    pb[qb][t] = pack_bf16x8(sacc[qb], 8 * t);
+                    sb[qb][t] = pack_bf16x8(dpacc[qb], 8 * t);
+                }
+                // one query block at a time (its statistics reads are not hoisted
+                // above the previous block's arithmetic)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // the packed operands are finished here, inside this phase (not sunk
+            // past the barrier into the next matrix phase)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    settle(pb[qb][t]);
+                    settle(sb[qb][t]);
+                }
+        };
+
+        // ---- phases (slot s ends with a barrier).  In loop round i both groups
+        // load step i+NS-2 (that stage held step i-2, last read in slot 2i-1) at
+        // the start of their vector phase (slot 2i+1 for the first group, 2i for
+        // the second); before the barrier ending odd slot s, step tv = (s+1)/2
+        // has landed, while up to NS-3 later steps may still be in flight.
+        static_assert(NS >= 4 && (NS - 3) * kLoads <= 63, "vmcnt range");
+        auto refill = [&](int i) __attribute__((always_inline)) {
+            if (i >= 2 && i + NS - 2 < total) {
+                issue(u_next);
+                ++u_next;
+            }
+        };
+        auto tail_odd = [&](int s) __attribute__((always_inline)) {
+            const int tv = (s + 1) / 2;
+            if (tv >= NS && tv < total) {
+                const int later = min(NS - 3, total - 1 - tv);
+                wait_vm_dyn<kLoads, NS - 3>(later);
+            }
+            lds_barrier();
+        };
+        lds_barrier();
+        if (grp == 0) {
+            // G(i) in slot 2i, X(i) in slot 2i + 1
+            do_sdp(0);
+            lds_barrier();
+            softmax(0);
+            tail_odd(1);
+            for (int i = 1; i <= total; ++i) {
+                gemm(i);
+                lds_barrier();
+                refill(i);
+                softmax(i);
+                tail_odd(2 * i + 1);
+            }
+        } else {
+            // X(i-1) in slot 2i, G(i) in slot 2i + 1
+            lds_barrier();
+            do_sdp(0);
+            tail_odd(1);
+            for (int i = 1; i <= total; ++i) {
+                refill(i);
+                softmax(i - 1);
+                lds_barrier();
+                gemm(i);
+                tail_odd(2 * i + 1);
+            }
+        }
+
+        if (krow < N) {
+            // per-lane row pointers from an opaque lane: hoisted out of the
+            // item loop they would be spilled
+            int le = lane;
+            asm volatile("" : "+v"(le));
+            const int64_t row = ((int64_t)b * Hkv + g) * N + kw + (le & 31);
+            uint16_t* dKr = dK + row * D;
+            uint16_t* dVr = dV + row * D;
+#pragma unroll
+            for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int c = 32 * ct + 8 * gq + 4 * (le >> 5);
+                    u32x2 wk, wv;
+                    wk[0] = pack_bf16x2(dkacc[ct][4 * gq] * scale, dkacc[ct][4 * gq + 1] * scale);
+                    wk[1] = pack_bf16x2(dkacc[ct][4 * gq + 2] * scale, dkacc[ct][4 * gq + 3] * scale);
+                    wv[0] = pack_bf16x2(dvacc[ct][4 * gq], dvacc[ct][4 * gq + 1]);
+                    wv[1] = pack_bf16x2(dvacc[ct][4 * gq + 2], dvacc[ct][4 * gq + 3]);
+                    *reinterpret_cast<u32x2*>(dKr + c) = wk;
+                    *reinterpret_cast<u32x2*>(dVr + c) = wv;
+                }
+        }
     }
 }
 
@@ -388,7 +402,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
-    uint16_t* __restrict__ dQ, int Hq, int Hkv, int N, int Npad, float c2, float scale) {
+    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int n_rows, int Npad, float c2, float scale) {
     using Cfg = QBf16Cfg<D>;
     using KT = typename Cfg::KT;
     constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BNK = Cfg::BNK, NS = Cfg::kStages, KB = BNK / 32;
@@ -400,212 +414,222 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     const int l32 = lane & 31, hh = lane >> 5;
     const int grp = wave >> 2;                  // waves w and w+4 share a SIMD
 
-    const int nmb = (N + BM - 1) / BM;
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    const int mbi = lin % nmb, bh = lin / nmb;
-    const int h = bh % Hq, b = bh / Hq;
-    const int mb = CAUSAL ? nmb - 1 - mbi : mbi;
-    const int g = h / (Hq / Hkv);
-    const int64_t rowbase = ((int64_t)b * Hq + h) * N;
-    const uint16_t* Kg = K + ((int64_t)b * Hkv + g) * N * D;
-    const uint16_t* Vg = V + ((int64_t)b * Hkv + g) * N * D;
+    const int nmb = (n_rows + BM - 1) / BM;
+    const PersistentSched sched(nmb * Hq * B);
+    for (int r = 0; sched.more(r); ++r) {
+        const int lin = sched.item(r);
+        if (lin < 0) continue;
+        // the sequence length as an opaque per-item value: whatever derives
+        // from it (tail clamps and masks) is computed per item, not hoisted
+        // out of the item loop into registers for the whole kernel
+        int N = n_rows;
+        asm volatile("" : "+s"(N));
+        const int mbi = lin % nmb, bh = lin / nmb;
+        const int h = bh % Hq, b = bh / Hq;
+        const int mb = CAUSAL ? nmb - 1 - mbi : mbi;
+        const int g = h / (Hq / Hkv);
+        const int64_t rowbase = ((int64_t)b * Hq + h) * N;
+        const uint16_t* Kg = K + ((int64_t)b * Hkv + g) * N * D;
+        const uint16_t* Vg = V + ((int64_t)b * Hkv + g) * N * D;
 
-    const int q0 = mb * BM;
-    const int qw = q0 + 32 * wave;
-    const int qrow = qw + l32;
-    const int kend = CAUSAL ? min(N, q0 + BM) : N;
-    const int ntiles = (kend + BNK - 1) / BNK;
-    const int ntw = qw >= N ? 0 : CAUSAL ? (min(N, qw + 32) + BNK - 1) / BNK : ntiles;
+        const int q0 = mb * BM;
+        const int qw = q0 + 32 * wave;
+        const int qrow = qw + l32;
+        const int kend = CAUSAL ? min(N, q0 + BM) : N;
+        const int ntiles = (kend + BNK - 1) / BNK;
+        const int ntw = qw >= N ? 0 : CAUSAL ? (min(N, qw + 32) + BNK - 1) / BNK : ntiles;
 
-    uint32_t voff[KT::kPerWave];
-#pragma unroll
-    for (int i = 0; i < KT::kPerWave; ++i) {
-        const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
-        voff[i] = (uint32_t)(row * D + (lane / KT::RG) * 8) * 2u;
-    }
-    auto issue = [&](int t) __attribute__((always_inline)) {
-        const uint32_t st = lds_addr(smem + (t % NS) * kStage);
-        const uint16_t* kb = Kg + (int64_t)t * BNK * D;
-        const uint16_t* vb = Vg + (int64_t)t * BNK * D;
-        const int rows_valid = N - t * BNK;
-        if (rows_valid >= BNK) {
-#pragma unroll
-            for (int i = 0; i < KT::kPerWave; ++i) dma16s(kb, voff[i], st + (i * NW + wave) * KT::RGS);
-#pragma unroll
-            for (int i = 0; i < KT::kPerWave; ++i) dma16s(vb, voff[i], st + KT::kBytes + (i * NW + wave) * KT::RGS);
-        } else {
+        // direct loads of tile t; the per-lane offsets are recomputed at every
+        // issue from an opaque copy of the lane index (kept live across the
+        // loop they would take registers the products need)
+        auto issue = [&](int t) __attribute__((always_inline)) {
+            const uint32_t st = lds_addr(smem + (t % NS) * kStage);
+            const uint16_t* kb = Kg + (int64_t)t * BNK * D;
+            const uint16_t* vb = Vg + (int64_t)t * BNK * D;
+            const int rows_valid = N - t * BNK;
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
 #pragma unroll
             for (int i = 0; i < KT::kPerWave; ++i) {
-                const int row = (i * NW + wave) * KT::RG + lane % KT::RG;
+                const int row = (i * NW + wave) * KT::RG + ln % KT::RG;
                 const int grow = row < rows_valid ? row : rows_valid - 1;
-                const uint32_t off = (uint32_t)(grow * D + (lane / KT::RG) * 8) * 2u;
+                const uint32_t off = (uint32_t)(grow * D + (ln / KT::RG) * 8) * 2u;
                 dma16s(kb, off, st + (i * NW + wave) * KT::RGS);
                 dma16s(vb, off, st + KT::kBytes + (i * NW + wave) * KT::RGS);
             }
-        }
-    };
+        };
 #pragma unroll
-    for (int t = 0; t < NS; ++t)
-        if (t < ntiles) issue(t);
+        for (int t = 0; t < NS; ++t)
+            if (t < ntiles) issue(t);
 
-    u32x4 qf[D / 16], of[D / 16];
+        u32x4 qf[D / 16], of[D / 16];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-        u32x4 a = {}, c = {};
-        if (qrow < N) {
-            a = *reinterpret_cast<const u32x4*>(Q + (rowbase + qrow) * D + 16 * s + 8 * hh);
-            c = *reinterpret_cast<const u32x4*>(dO + (rowbase + qrow) * D + 16 * s + 8 * hh);
-        }
-        qf[s] = a;
-        of[s] = c;
-    }
-    const int64_t srow = ((int64_t)b * Hq + h) * Npad + qrow;
-    const float lse2 = qrow < N ? WSl[srow] : INFINITY;
-    const float dq_d = qrow < N ? WSd[srow] : 0.f;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-        settle(qf[s]);
-        settle(of[s]);
-    }
-    settle(lse2);
-    settle(dq_d);
-    wait_vm<0>();
-
-    f32x16 dqacc[D / 32];
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) dqacc[i] = zero16();
-    f32x16 sacc[KB], dpacc[KB];
-    u32x4 dsf[KB][2];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        sacc[kb] = dpacc[kb] = zero16();
-        dsf[kb][0] = dsf[kb][1] = u32x4{};
-    }
-
-    // S^T = K_t Q^T and dP^T = V_t dO^T: rows = keys, columns = this wave's queries
-    auto do_sdp = [&](int t) __attribute__((always_inline)) {
-        const uint16_t* Ks = smem + (t % NS) * kStage;
-        const uint16_t* Vs = Ks + KT::kElems;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) sacc[kb] = dpacc[kb] = zero16();
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                sacc[kb] = mma_bf16(KT::row8(Ks, 32 * kb + l32, 2 * s + hh), qf[s], sacc[kb]);
-                dpacc[kb] = mma_bf16(KT::row8(Vs, 32 * kb + l32, 2 * s + hh), of[s], dpacc[kb]);
+        for (int s = 0; s < D / 16; ++s) {
+            u32x4 a = {}, c = {};
+            if (qrow < N) {
+                a = *reinterpret_cast<const u32x4*>(Q + (rowbase + qrow) * D + 16 * s + 8 * hh);
+                c = *reinterpret_cast<const u32x4*>(dO + (rowbase + qrow) * D + 16 * s + 8 * hh);
             }
-    };
-    // dQ^T += K_t^T dS_t^T
-    auto do_dq = [&](int t) __attribute__((always_inline)) {
-        const uint16_t* Ks = smem + (t % NS) * kStage;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-                for (int ct = 0; ct < D / 32; ++ct)
-                    dqacc[ct] = mma_bf16(KT::tr8(Ks, 32 * kb + 16 * t2, 32 * ct, lane), dsf[kb][t2], dqacc[ct]);
-    };
-    // G(t), t >= 1 (past this wave's last tile the scores are discarded and
-    // dS is zero)
-    auto gemm = [&](int t) __attribute__((always_inline)) {
-        do_dq(t - 1);
-        do_sdp(t);
-        sched_dq_phase<D>();
-    };
-    // X(t): P from the stored statistics; keys after the query (causal) or
-    // past the end zeroed in one wave-uniform branch; dS packed to bf16
-    auto softmax = [&](int t) __attribute__((always_inline)) {
-        if (t >= ntw) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) dsf[kb][0] = dsf[kb][1] = u32x4{};
-            return;
+            qf[s] = a;
+            of[s] = c;
         }
-        const int k0 = t * BNK;
+        const int64_t srow = ((int64_t)b * Hq + h) * Npad + qrow;
+        const float lse2 = qrow < N ? WSl[srow] : INFINITY;
+        const float dq_d = qrow < N ? WSd[srow] : 0.f;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int s = 0; s < D / 16; ++s) {
+            settle(qf[s]);
+            settle(of[s]);
+        }
+        settle(lse2);
+        settle(dq_d);
+        wait_vm<0>();
+
+        f32x16 dqacc[D / 32];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c2, -lse2));
-        if ((CAUSAL && k0 + BNK - 1 > qw) || (k0 + BNK > N)) {
+        for (int i = 0; i < D / 32; ++i) dqacc[i] = zero16();
+        f32x16 sacc[KB], dpacc[KB];
+        u32x4 dsf[KB][2];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            sacc[kb] = dpacc[kb] = zero16();
+            dsf[kb][0] = dsf[kb][1] = u32x4{};
+        }
+
+        // S^T = K_t Q^T and dP^T = V_t dO^T: rows = keys, columns = this wave's queries
+        auto do_sdp = [&](int t) __attribute__((always_inline)) {
+            const uint16_t* Ks = smem + (t % NS) * kStage;
+            const uint16_t* Vs = Ks + KT::kElems;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sacc[kb] = dpacc[kb] = zero16();
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    sacc[kb] = mma_bf16(KT::row8(Ks, 32 * kb + l32, 2 * s + hh), qf[s], sacc[kb]);
+                    dpacc[kb] = mma_bf16(KT::row8(Vs, 32 * kb + l32, 2 * s + hh), of[s], dpacc[kb]);
+                }
+        };
+        // dQ^T += K_t^T dS_t^T
+        auto do_dq = [&](int t) __attribute__((always_inline)) {
+            const uint16_t* Ks = smem + (t % NS) * kStage;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * kb + acc_row(r, hh);
-                    if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r] = 0.f;
+                for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                    for (int ct = 0; ct < D / 32; ++ct)
+                        dqacc[ct] = mma_bf16(KT::tr8(Ks, 32 * kb + 16 * t2, 32 * ct, lane), dsf[kb][t2], dqacc[ct]);
+        };
+        // G(t), t >= 1 (past this wave's last tile the scores are discarded and
+        // dS is zero)
+        auto gemm = [&](int t) __attribute__((always_inline)) {
+            do_dq(t - 1);
+            do_sdp(t);
+            sched_dq_phase<D>();
+        };
+        // X(t): P from the stored statistics; keys after the query (causal) or
+        // past the end zeroed in one wave-uniform branch; dS packed to bf16
+        auto softmax = [&](int t) __attribute__((always_inline)) {
+            if (t >= ntw) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) dsf[kb][0] = dsf[kb][1] = u32x4{};
+                return;
+            }
+            const int k0 = t * BNK;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c2, -lse2));
+            if ((CAUSAL && k0 + BNK - 1 > qw) || (k0 + BNK > N)) {
+                // row indices from an opaque copy of the lane half: hoisted
+                // out of the item loop, they and the masks derived from them
+                // would stay live in registers
+                int hm = hh;
+                asm volatile("" : "+v"(hm));
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * kb + acc_row(r, hm);
+                        if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r] = 0.f;
+                    }
+            }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dpacc[kb][r] = sacc[kb][r] * (dpacc[kb][r] - dq_d);
+                dsf[kb][0] = pack_bf16x8(dpacc[kb], 0);
+                dsf[kb][1] = pack_bf16x8(dpacc[kb], 8);
+            }
+            // dS is finished inside this phase (not sunk into the next matrix phase)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                settle(dsf[kb][0]);
+                settle(dsf[kb][1]);
+            }
+        };
+
+        // ---- phases (slot s ends with a barrier).  In loop round t both groups
+        // refill the stage of tile t+2 (its previous tile, t-2, was last read in
+        // slot 2t-1) during their vector phase (slot 2t+1 for the first group,
+        // 2t for the second); before the barrier ending odd slot s, tile (s+1)/2
+        // has landed (one later tile may still be in flight).
+        auto refill = [&](int t) __attribute__((always_inline)) {
+            if (t + 2 >= NS && t + 2 < ntiles) issue(t + 2);
+        };
+        auto tail_odd = [&](int s) __attribute__((always_inline)) {
+            const int tv = (s + 1) / 2;
+            if (tv >= NS && tv < ntiles) {
+                if (tv + 1 < ntiles) wait_vm<kLoads>();
+                else wait_vm<0>();
+            }
+            lds_barrier();
+        };
+        lds_barrier();
+        if (grp == 0) {
+            // G(t) in slot 2t, X(t) in slot 2t + 1
+            do_sdp(0);
+            lds_barrier();
+            softmax(0);
+            tail_odd(1);
+            for (int t = 1; t <= ntiles; ++t) {
+                gemm(t);
+                lds_barrier();
+                softmax(t);
+                refill(t);
+                tail_odd(2 * t + 1);
+            }
+        } else {
+            // X(t-1) in slot 2t, G(t) in slot 2t + 1
+            lds_barrier();
+            do_sdp(0);
+            tail_odd(1);
+            for (int t = 1; t <= ntiles; ++t) {
+                softmax(t - 1);
+                refill(t);
+                lds_barrier();
+                gemm(t);
+                tail_odd(2 * t + 1);
+            }
+        }
+
+        if (qrow < N) {
+            // per-lane row pointer from an opaque lane: hoisted out of the
+            // item loop it would be spilled
+            int le = lane;
+            asm volatile("" : "+v"(le));
+            uint16_t* dQr = dQ + (rowbase + qw + (le & 31)) * D + 4 * (le >> 5);
+#pragma unroll
+            for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(dqacc[ct][4 * gq] * scale, dqacc[ct][4 * gq + 1] * scale);
+                    w[1] = pack_bf16x2(dqacc[ct][4 * gq + 2] * scale, dqacc[ct][4 * gq + 3] * scale);
+                    *reinterpret_cast<u32x2*>(dQr + 32 * ct + 8 * gq) = w;
                 }
         }
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dpacc[kb][r] = sacc[kb][r] * (dpacc[kb][r] - dq_d);
-            dsf[kb][0] = pack_bf16x8(dpacc[kb], 0);
-            dsf[kb][1] = pack_bf16x8(dpacc[kb], 8);
-        }
-        // dS is finished inside this phase (not sunk into the next matrix phase)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            settle(dsf[kb][0]);
-            settle(dsf[kb][1]);
-        }
-    };
-
-    // ---- phases (slot s ends with a barrier).  In loop round t both groups
-    // refill the stage of tile t+2 (its previous tile, t-2, was last read in
-    // slot 2t-1) during their vector phase (slot 2t+1 for the first group,
-    // 2t for the second); before the barrier ending odd slot s, tile (s+1)/2
-    // has landed (one later tile may still be in flight).
-    auto refill = [&](int t) __attribute__((always_inline)) {
-        if (t + 2 >= NS && t + 2 < ntiles) issue(t + 2);
-    };
-    auto tail_odd = [&](int s) __attribute__((always_inline)) {
-        const int tv = (s + 1) / 2;
-        if (tv >= NS && tv < ntiles) {
-            if (tv + 1 < ntiles) wait_vm<kLoads>();
-            else wait_vm<0>();
-        }
-        lds_barrier();
-    };
-    lds_barrier();
-    if (grp == 0) {
-        // G(t) in slot 2t, X(t) in slot 2t + 1
-        do_sdp(0);
-        lds_barrier();
-        softmax(0);
-        tail_odd(1);
-        for (int t = 1; t <= ntiles; ++t) {
-            gemm(t);
-            lds_barrier();
-            softmax(t);
-            refill(t);
-            tail_odd(2 * t + 1);
-        }
-    } else {
-        // X(t-1) in slot 2t, G(t) in slot 2t + 1
-        lds_barrier();
-        do_sdp(0);
-        tail_odd(1);
-        for (int t = 1; t <= ntiles; ++t) {
-            softmax(t - 1);
-            refill(t);
-            lds_barrier();
-            gemm(t);
-            tail_odd(2 * t + 1);
-        }
-    }
-
-    if (qrow < N) {
-        uint16_t* dQr = dQ + (rowbase + qrow) * D;
-#pragma unroll
-        for (int ct = 0; ct < D / 32; ++ct)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                u32x2 w;
-                w[0] = pack_bf16x2(dqacc[ct][4 * gq] * scale, dqacc[ct][4 * gq + 1] * scale);
-                w[1] = pack_bf16x2(dqacc[ct][4 * gq + 2] * scale, dqacc[ct][4 * gq + 3] * scale);
-                *reinterpret_cast<u32x2*>(dQr + 32 * ct + 8 * gq + 4 * hh) = w;
-            }
     }
 }
 
@@ -615,10 +639,12 @@ static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const
     using Cfg = KVBf16Cfg<D>;
     const int nkb = (N + Cfg::BNK - 1) / Cfg::BNK;
     const int Np = ws_rows(N);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)nkb * Hkv * B)),
-                       dim3(Cfg::kThreads), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dO, ws, ws + (int64_t)B * Hq * Np, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv,
-                       N, Np, scale * kLog2e, scale);
+    static std::atomic<int> slots{0};
+    const int grid = persistent_grid((const void*)bwd_dkdv_bf16_kernel<D, CAUSAL>, Cfg::kThreads, nkb * Hkv * B, slots);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
+                       ws + (int64_t)B * Hq * Np, (uint16_t*)dk, (uint16_t*)dv, B, Hq, Hkv, N, Np, scale * kLog2e,
+                       scale);
     return hipGetLastError();
 }
 
@@ -628,10 +654,11 @@ static hipError_t launch_dq(const void* q, const void* k, const void* v, const v
     using Cfg = QBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
     const int Np = ws_rows(N);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)((int64_t)nmb * Hq * B)),
-                       dim3(Cfg::kThreads), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dO, ws, ws + (int64_t)B * Hq * Np, (uint16_t*)dq, Hq, Hkv, N, Np,
-                       scale * kLog2e, scale);
+    static std::atomic<int> slots{0};
+    const int grid = persistent_grid((const void*)bwd_dq_bf16_kernel<D, CAUSAL>, Cfg::kThreads, nmb * Hq * B, slots);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
+                       ws + (int64_t)B * Hq * Np, (uint16_t*)dq, B, Hq, Hkv, N, Np, scale * kLog2e, scale);
     return hipGetLastError();
 }
 
