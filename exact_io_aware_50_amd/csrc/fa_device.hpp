@@ -483,28 +483,6 @@ struct LdsTile {
     }
 };
 
-// A matrix phase as an explicit software pipeline: NSTEP products run in
-// program order, and the LDS fragment of step k is read AHEAD steps before
-// its product, into a ring of AHEAD + 1 registers.  read(k) returns the
-// fragment of step k, mma(k, frag) issues the product; both are called with
-// constant k once the loops are unrolled.  A scheduling fence after every
-// step keeps the order as written, so the read-ahead depth (and with it the
-// partial LDS waits the compiler derives) does not depend on how the
-// instruction scheduler happens to resolve a larger region.
-template <int NSTEP, int AHEAD, typename Read, typename Mma>
-__device__ __forceinline__ void pipelined_phase(Read&& read, Mma&& mma) {
-    constexpr int W = AHEAD + 1;
-    u32x4 ring[W];
-#pragma unroll
-    for (int k = 0; k < AHEAD && k < NSTEP; ++k) ring[k % W] = read(k);
-#pragma unroll
-    for (int k = 0; k < NSTEP; ++k) {
-        if (k + AHEAD < NSTEP) ring[(k + AHEAD) % W] = read(k + AHEAD);
-        mma(k, ring[k % W]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
 __device__ __forceinline__ f32x16 mma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
