@@ -19,8 +19,9 @@
 namespace fa {
 
 // ------------------------------------------------------------ workspace: D, LSE*log2e
-// Row r of the padded [B*Hq][Np] layout: D = sum_c dO*O and LSE*log2(e) for
-// query rows < N; D = 0 and +infinity (zero probability) for padding rows.
+// Row r of the padded [B*Hq][Np] layout: -D = -sum_c dO*O and LSE*log2(e) for
+// query rows < N; 0 and +infinity (zero probability) for padding rows.  -D
+// rather than D: the bf16 dK/dV kernel starts its dP accumulators from it.
 template <class ET, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const typename ET::elem* __restrict__ O,
                                                         const typename ET::elem* __restrict__ dO,
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const typename ET::elem*
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (seg == 0 && row < rows) {
-        WSd[row] = acc;
+        WSd[row] = -acc;
         WSl[row] = valid ? LSE[bh * N + i] * kLog2e : INFINITY;
     }
 }
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
                         float p = fast_exp2(fmaf(sacc[qb][r], c2, -l4[j]));
                         if (need_mask && krow > q0 + rb + j) p = 0.f;
                         sacc[qb][r] = p;
-                        dpacc[qb][r] = p * (dpacc[qb][r] - d4[j]);
+                        dpacc[qb][r] = p * (dpacc[qb][r] + d4[j]);     // d4 = -D
                     }
                 }
             // dV^T += dO^T P ;  dK^T += Q^T dS
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
     }
     const int64_t srow = ((int64_t)b * Hq + h) * Np + qrow;
     const float lse2 = qrow < N ? WSl[srow] : INFINITY;
-    const float dq_d = qrow < N ? WSd[srow] : 0.f;
+    const float dq_nd = qrow < N ? WSd[srow] : 0.f;     // the workspace holds -D
 
     f32x16 dqacc[D / 32];
 #pragma unroll
@@ -336,7 +337,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
                         const int key = k0 + 32 * kb + acc_row(r, hh);
                         if ((CAUSAL && key > qrow) || key >= N) p = 0.f;
                     }
-                    dpacc[kb][r] = p * (dpacc[kb][r] - dq_d);
+                    dpacc[kb][r] = p * (dpacc[kb][r] + dq_nd);
                 }
             // dQ^T += K^T dS^T
 #pragma unroll

@@ -43,13 +43,14 @@ struct KVBf16Cfg {
     static constexpr int kLoads = 2 * QT::kPerWave + 1;
 };
 
-// G phase order: L reads ahead; the dV/dK products (two transposed reads per
+// G phase order: the NSTAT reads of the statistics that start dP and L
+// fragment reads ahead; the dV/dK products (two transposed reads per
 // fragment) first, then the S products (one read: Q) alternating with the dP
 // products (dO and V rows).
-template <int L>
+template <int L, int NSTAT>
 __device__ __forceinline__ void sched_dkdv_phase() {
 #pragma unroll
-    for (int i = 0; i < L; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < L + NSTAT; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
             asm volatile("" : "+s"(vz));
             const uint16_t* Vw = Vl + vz;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sacc[qb] = dpacc[qb] = zero16();
+            for (int qb = 0; qb < QB; ++qb) sacc[qb] = zero16();
 #pragma unroll
             for (int s = 0; s < D / 16; ++s)
 #pragma unroll
@@ -217,11 +218,29 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
                         dkacc[ct] = mma_bf16(QT::tr8(Qs, 32 * qb + 16 * t, 32 * ct, lane), sb[qb][t], dkacc[ct]);
                     }
         };
+        // dP of step i starts from -D of its query rows (the workspace holds
+        // -D), so the accumulator ends as dP - D and dS = P (dP - D) is one
+        // multiply in the vector phase
+        auto init_dp = [&](int i) __attribute__((always_inline)) {
+            const float* sd = (const float*)(smem + (i % NS) * Cfg::kStageBytes + 2 * QT::kBytes) + BMQ;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sd + 32 * qb + 8 * gq + 4 * hh);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) dpacc[qb][4 * gq + j] = d4[j];
+                }
+        };
         // G(i), i >= 1 (i == total: the products of the last step only)
         auto gemm = [&](int i) __attribute__((always_inline)) {
+            init_dp(i);
             do_dvdk(i - 1);
             do_sdp(i);
-            sched_dkdv_phase<D == 128 ? 8 : 4>();
+            // 8 fragments ahead at d = 128 causal; the non-causal kernel has 4
+            // (with 8 it needs more than 256 registers and the scheduler drops
+            // the read-ahead altogether)
+            sched_dkdv_phase<D == 128 && CAUSAL ? 8 : 4, 4 * QB>();
         };
         // X(i): step i's query block is xq
         int xq = qt0;
@@ -256,14 +275,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
                         if (delta > 8 * (r / 4) + r % 4) sacc[qb][r] = 0.f;
                 }
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + BMQ + 32 * qb + 8 * gq + 4 * hh);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r = 4 * gq + j;
-                        dpacc[qb][r] = sacc[qb][r] * (dpacc[qb][r] - d4[j]);
-                    }
-                }
+                for (int r = 0; r < 16; ++r) dpacc[qb][r] = sacc[qb][r] * dpacc[qb][r];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     pb[qb][t] = pack_bf16x8(sacc[qb], 8 * t);
@@ -307,6 +319,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         lds_barrier();
         if (grp == 0) {
             // G(i) in slot 2i, X(i) in slot 2i + 1
+            init_dp(0);
             do_sdp(0);
             lds_barrier();
             softmax(0);
@@ -321,6 +334,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         } else {
             // X(i-1) in slot 2i, G(i) in slot 2i + 1
             lds_barrier();
+            init_dp(0);
             do_sdp(0);
             tail_odd(1);
             for (int i = 1; i <= total; ++i) {
@@ -475,14 +489,14 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
         }
         const int64_t srow = ((int64_t)b * Hq + h) * Npad + qrow;
         const float lse2 = qrow < N ? WSl[srow] : INFINITY;
-        const float dq_d = qrow < N ? WSd[srow] : 0.f;
+        const float dq_nd = qrow < N ? WSd[srow] : 0.f;     // the workspace holds -D
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
             settle(qf[s]);
             settle(of[s]);
         }
         settle(lse2);
-        settle(dq_d);
+        settle(dq_nd);
         wait_vm<0>();
 
         f32x16 dqacc[D / 32];
@@ -558,7 +572,7 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dpacc[kb][r] = sacc[kb][r] * (dpacc[kb][r] - dq_d);
+                for (int r = 0; r < 16; ++r) dpacc[kb][r] = sacc[kb][r] * (dpacc[kb][r] + dq_nd);
                 dsf[kb][0] = pack_bf16x8(dpacc[kb], 0);
                 dsf[kb][1] = pack_bf16x8(dpacc[kb], 8);
             }

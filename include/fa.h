@@ -112,9 +112,10 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v,
  * The three stages of fa_bwd as separate calls, for callers that schedule or
  * time them one by one; fa_bwd is exactly these three in order.  Same
  * validation, dtypes and tensor layouts as fa_bwd.
- *   fa_bwd_delta : fills the workspace `ws` from O, dO and LSE: the row term
- *                  of the softmax gradient D[b,h,i] = sum_c dO[b,h,i,c] O[b,h,i,c]
- *                  (which equals sum_j P_ij dP_ij) and LSE[b,h,i] * log2(e)
+ *   fa_bwd_delta : fills the workspace `ws` from O, dO and LSE: the negated
+ *                  row term of the softmax gradient, -D[b,h,i] with
+ *                  D[b,h,i] = sum_c dO[b,h,i,c] O[b,h,i,c] (which equals
+ *                  sum_j P_ij dP_ij), and LSE[b,h,i] * log2(e)
  *   fa_bwd_dkdv  : dK, dV from the workspace, parallel over key blocks
  *                  ("FlashAttention" legal glossary, FlashAttention-2
  *                  paragraph: column-parallel backward without atomic adds);
@@ -143,8 +144,8 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of the backward workspace: 8 * B * Hq * Np with Np = N rounded up to
- * a multiple of 64 (0 for an empty problem).  Layout: float32 D[B*Hq][Np]
- * followed by float32 LSE*log2(e)[B*Hq][Np]; rows i >= N hold D = 0 and
+ * a multiple of 64 (0 for an empty problem).  Layout: float32 -D[B*Hq][Np]
+ * followed by float32 LSE*log2(e)[B*Hq][Np]; rows i >= N hold 0 and
  * +infinity, so padded query rows carry zero probability.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N);
