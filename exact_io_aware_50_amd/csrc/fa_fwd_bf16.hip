@@ -262,7 +262,8 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
         // slot 2u - 7 and as V in slot 2u - 5), so every slot carries half a
         // tile of loads.  Before the barrier ending odd slot 2tv - 1, K_tv (and
         // everything issued before it) has landed; V_tv, K_tv+1 and V_tv+1 may
-        // still be in flight.
+        // still be in flight.  The V rows of the last tile are waited for before
+        // the barrier ending slot 2 ntiles - 1, ahead of their one read.
         auto head = [&](int s) __attribute__((always_inline)) {
             const int u = (s >> 1) + 2;
             if (s >= 4 && u < ntiles) issue_half(u, s & 1);
@@ -272,6 +273,8 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
             if (tv >= NS && tv < ntiles) {
                 if (tv + 1 < ntiles) wait_vm<3 * KT::kPerWave>();
                 else wait_vm<KT::kPerWave>();
+            } else if (tv == ntiles && ntiles > NS) {
+                wait_vm<0>();                         // V of the last tile (read in G(ntiles))
             }
             lds_barrier();
         };
