@@ -14,6 +14,11 @@
 namespace fa {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// empty asms consuming a value: its computation stays before this point
+__device__ __forceinline__ void settle8(const u32x8& x) { asm volatile("" : : "v"(x)); }
+__device__ __forceinline__ void settle16(const f32x16& x) { asm volatile("" : : "v"(x)); }
 
 // ------------------------------------------------------------ quantiser
 __global__ void q8_clear_kernel(float* descale) {
@@ -297,8 +302,338 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
     }
 }
 
+// ------------------------------------------------------------ fp8 forward, d = 128
+//
+// The schedule of the bf16 forward (two wave groups one phase apart, K and V
+// tiles loaded straight into a ring of four LDS stages in their row-major
+// layout, persistent workgroups) with E4M3 operands:
+//  - S^T = K_t Q^T: per 32-key block, d/64 fp8 products whose K fragment is
+//    two 16-byte row reads;
+//  - O^T += V_t^T P^T: one fp8 product per 32 d-columns covers all 64 keys.
+//    Its V^T fragment comes from four transposing byte reads of the
+//    row-major V tile (ds_read_b64_tr_b8: within a 16-lane group, output lane
+//    i, byte j is byte i % 8 of what source lane 2j + i/8 read).  Source lanes
+//    2j and 2j + 1 read 8 columns each of the same key, so every lane receives
+//    one column over eight keys, in the order its P bytes hold the keys.
+//  - P is scaled by 2^7 before its E4M3 rounding (exp2(c s - m + 7)), and the
+//    running max is moved when a row grows by more than a factor 2, so the
+//    scaled P stays at most 256, below the largest E4M3 value 448; l adds the
+//    unrounded scaled values and the scale leaves with it.
+template <int D>
+struct FwdFp8Cfg {
+    static constexpr int kWaves = 8;                  // two groups of four, one wave of each per SIMD
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int BM = 32 * kWaves;            // query rows per workgroup
+    static constexpr int BN = 64;                     // keys per K/V tile
+    static constexpr int kStages = 4;
+    using KT = LdsTile<BN, D / 2, kWaves>;            // byte rows, in 16-bit units
+    static constexpr int kStage = 2 * KT::kElems;     // 16-bit units per stage (K then V)
+    static constexpr float kTau = 1.0f;               // log2 slack before the max is moved
+    static constexpr float kPLog2 = 7.0f;             // log2 of the P scale
+};
+
+// G phase order: the K fragments (two reads) of the score products, then the
+// V^T fragments (four reads) of the P V products, each read three products
+// ahead.
+__device__ __forceinline__ void sched_fp8_phase() {
+    constexpr int NS_ = 4, NT = 8, A = 3;
+#pragma unroll
+    for (int f = 0; f < A; ++f) {
+        if (f < NS_) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (j + A < NS_) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else if (j + A < NT) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
+    const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, const float* __restrict__ descale, int B, int Hq, int Hkv,
+    int n_rows, float scale) {
+    using Cfg = FwdFp8Cfg<D>;
+    using KT = typename Cfg::KT;
+    constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::kStages, KB = BN / 32;
+    constexpr int kStage = Cfg::kStage;
+    static_assert(D == 128, "one row group per wave per tile");
+    static_assert((NS & (NS - 1)) == 0, "stage index by mask");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * kStage];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave >> 2;
+    const float c2 = scale * kLog2e * descale[0] * descale[1];
+    const float sv = descale[2];
+
+    const int nmb = (n_rows + BM - 1) / BM;
+    const PersistentSched sched(nmb * Hq * B);
+    for (int r = 0; sched.more(r); ++r) {
+        const int lin = sched.item(r);
+        if (lin < 0) continue;
+        // the sequence length as an opaque per-item value: whatever derives
+        // from it (tail clamps and masks) is computed per item, not hoisted
+        // out of the item loop into registers for the whole kernel
+        int N = n_rows;
+        asm volatile("" : "+s"(N));
+        const int lane = threadIdx.x & 63;
+        const int l32 = lane & 31, hh = lane >> 5;
+        const int mbi = lin % nmb, bh = lin / nmb;
+        const int h = bh % Hq, b = bh / Hq;
+        const int mb = CAUSAL ? nmb - 1 - mbi : mbi;      // longest causal rows first
+        const int g = h / (Hq / Hkv);
+        const uint8_t* Qh = Q + ((int64_t)b * Hq + h) * N * D;
+        const uint8_t* Kh = K + ((int64_t)b * Hkv + g) * N * D;
+        const uint8_t* Vh = V + ((int64_t)b * Hkv + g) * N * D;
+
+        const int q0 = mb * BM;
+        const int qw = q0 + 32 * wave;
+        const int qrow = qw + l32;
+        const int kend = CAUSAL ? min(N, q0 + BM) : N;
+        const int ntiles = (kend + BN - 1) / BN;
+        const int ntw = qw >= N ? 0 : CAUSAL ? (min(N, qw + 32) + BN - 1) / BN : ntiles;
+        auto stage = [&](int t) __attribute__((always_inline)) { return smem + (t & (NS - 1)) * kStage; };
+
+        // ---- direct loads: this wave's row group of a K/V tile (rows past the
+        // end re-read the last row)
+        const uint32_t voff = (uint32_t)((wave * KT::RG + lane % KT::RG) * D + (lane / KT::RG) * 16);
+        auto issue_half = [&](int t, const int half) __attribute__((always_inline)) {
+            const uint32_t st = lds_addr(stage(t)) + half * KT::kBytes;
+            const uint8_t* src = (half ? Vh : Kh) + (int64_t)t * BN * D;
+            const int rows_valid = N - t * BN;
+            if (rows_valid >= BN) {
+                dma16s(src, voff, st + wave * KT::RGS);
+            } else {
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const int row = wave * KT::RG + ln % KT::RG;
+                const int grow = row < rows_valid ? row : rows_valid - 1;
+                dma16s(src, (uint32_t)(grow * D + (ln / KT::RG) * 16), st + wave * KT::RGS);
+            }
+        };
+        auto issue = [&](int t) __attribute__((always_inline)) {
+            issue_half(t, 0);
+            issue_half(t, 1);
+        };
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+            if (t < ntiles) issue(t);
+
+        // Q rows as B operands: 32 bytes per lane and product (rows past the
+        // end read the last row; those queries are never stored)
+        u32x8 qf[D / 64];
+        {
+            const int row = min(qrow, N - 1);
+#pragma unroll
+            for (int s2 = 0; s2 < D / 64; ++s2) qf[s2] = *reinterpret_cast<const u32x8*>(Qh + (int64_t)row * D + 64 * s2 + 32 * hh);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < D / 64; ++s2) settle8(qf[s2]);
+        wait_vm<0>();
+
+        f32x16 oacc[D / 32];
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
+        float m = kNegBig, lsum = 0.f;
+        f32x16 sacc[KB];
+        u32x8 pf = {};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sacc[kb] = zero16();
+
+        // S^T = K_t Q^T: rows = keys, columns = this wave's queries
+        auto do_s = [&](int t) __attribute__((always_inline)) {
+            const uint16_t* Ks = stage(t);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sacc[kb] = zero16();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int s2 = 0; s2 < D / 64; ++s2) {
+                    const u32x4 lo = KT::row8(Ks, 32 * kb + l32, 4 * s2 + 2 * hh);
+                    const u32x4 hi = KT::row8(Ks, 32 * kb + l32, 4 * s2 + 2 * hh + 1);
+                    const u32x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    sacc[kb] = mma_fp8(a, qf[s2], sacc[kb]);
+                }
+        };
+        // O^T += V_t^T P^T.  Read p (0..3) of a fragment gives this lane the
+        // keys 32(p/2) + 16(p%2) + 8(j/4) + 4hh + j%4, j = 0..7: key of byte
+        // e = 8p + j of P.
+        const int g16 = lane >> 4, s16 = lane & 15, jj = s16 >> 1, qq = s16 & 1;
+        auto do_pv = [&](int t) __attribute__((always_inline)) {
+            const char* Vb = (const char*)(stage(t) + KT::kElems);
+#pragma unroll
+            for (int ct = 0; ct < D / 32; ++ct) {
+                u32x8 a;
+#pragma unroll
+                for (int pq = 0; pq < 4; ++pq) {
+                    const int key = 32 * (pq >> 1) + 16 * (pq & 1) + 8 * (jj >> 2) + 4 * (g16 >> 1) + (jj & 3);
+                    const int col = 32 * ct + 16 * (g16 & 1) + 8 * qq;
+                    const char* ad = Vb + KT::off(key, col >> 4) + (col & 15);
+                    const auto w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (__attribute__((address_space(3))) i32x2*)(__attribute__((address_space(3))) char*)ad);
+                    a[2 * pq] = (uint32_t)w[0];
+                    a[2 * pq + 1] = (uint32_t)w[1];
+                }
+                oacc[ct] = mma_fp8(a, pf, oacc[ct]);
+            }
+        };
+        // The scaled fp8 products are not held in their phase by the ordering
+        // hints alone: consuming their results at the end of the phase keeps
+        // them (and their completion) before the barrier.  The matrix phase is
+        // much shorter than the vector phase here, so the wait costs nothing.
+        auto gemm = [&](int t) __attribute__((always_inline)) {
+            do_s(t);
+            do_pv(t - 1);
+            sched_fp8_phase();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) settle16(sacc[kb]);
+#pragma unroll
+            for (int ct = 0; ct < D / 32; ++ct) settle16(oacc[ct]);
+        };
+        // X(t)
+        auto softmax = [&](int t) __attribute__((always_inline)) {
+            if (t >= ntw) {
+                pf = u32x8{};
+                return;
+            }
+            const int k0 = t * BN;
+            if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N) {
+                int hm = hh;
+                asm volatile("" : "+v"(hm));
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int r2 = 0; r2 < 16; ++r2) {
+                        const int key = k0 + 32 * kb + acc_row(r2, hm);
+                        if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r2] = -INFINITY;
+                    }
+            }
+            float x = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r2 = 0; r2 < 16; ++r2) x = fmaxf(x, sacc[kb][r2]);
+            x = pair_max(x);
+            const float mnew = fmaxf(m, x * c2);
+            if (__any(mnew > m + Cfg::kTau)) {
+                const float alpha = fast_exp2(m - mnew);
+                m = mnew;
+                lsum *= alpha;
+#pragma unroll
+                for (int ct = 0; ct < D / 32; ++ct) oacc[ct] *= alpha;
+            }
+            // P * 2^7 = exp2(c2 s - m + 7), packed to E4M3: byte e of pf is
+            // register e % 16 of key block e / 16
+            const float base = Cfg::kPLog2 - m;
+            float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = fast_exp2(fmaf(sacc[w >> 2][4 * (w & 3) + i], c2, base));
+                    rs[i] += p[i];
+                }
+                int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                pk = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], pk, true);
+                pf[w] = (uint32_t)pk;
+            }
+            lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+            settle8(pf);
+        };
+
+        // ---- phases: as in the bf16 forward (K rows of tile u >= NS at the
+        // start of slot 2u - 4, V rows at the start of slot 2u - 3)
+        auto head = [&](int s2) __attribute__((always_inline)) {
+            const int u = (s2 >> 1) + 2;
+            if (s2 >= 4 && u < ntiles) issue_half(u, s2 & 1);
+        };
+        auto tail_odd = [&](int s2) __attribute__((always_inline)) {
+            const int tv = (s2 + 1) / 2;
+            if (tv >= NS && tv < ntiles) {
+                if (tv + 1 < ntiles) wait_vm<3>();
+                else wait_vm<1>();
+            } else if (tv == ntiles && ntiles > NS) {
+                wait_vm<0>();                         // V of the last tile
+            }
+            lds_barrier();
+        };
+        lds_barrier();
+        if (grp == 0) {
+            do_s(0);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) settle16(sacc[kb]);
+            lds_barrier();
+            softmax(0);
+            tail_odd(1);
+            for (int t = 1; t <= ntiles; ++t) {
+                head(2 * t);
+                gemm(t);
+                lds_barrier();
+                head(2 * t + 1);
+                softmax(t);
+                tail_odd(2 * t + 1);
+            }
+        } else {
+            lds_barrier();
+            do_s(0);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) settle16(sacc[kb]);
+            tail_odd(1);
+            for (int t = 1; t <= ntiles; ++t) {
+                head(2 * t);
+                softmax(t - 1);
+                lds_barrier();
+                head(2 * t + 1);
+                gemm(t);
+                tail_odd(2 * t + 1);
+            }
+        }
+
+        // ---- epilogue: O = s_V O_acc / l, LSE = ln2 (m + log2(l / 2^7))
+        const float ltot = pair_sum(lsum);
+        if (qrow < N) {
+            const float f = sv / ltot;
+            int le = lane;
+            asm volatile("" : "+v"(le));
+            uint16_t* Orow = O + (((int64_t)b * Hq + h) * N + qw + (le & 31)) * D + 4 * (le >> 5);
+#pragma unroll
+            for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(oacc[ct][4 * gq] * f, oacc[ct][4 * gq + 1] * f);
+                    w[1] = pack_bf16x2(oacc[ct][4 * gq + 2] * f, oacc[ct][4 * gq + 3] * f);
+                    *reinterpret_cast<u32x2*>(Orow + 32 * ct + 8 * gq) = w;
+                }
+            if (hh == 0) LSE[((int64_t)b * Hq + h) * N + qrow] = (m + log2f(ltot) - Cfg::kPLog2) * kLn2;
+        }
+    }
+}
+
+template <bool CAUSAL>
+static hipError_t launch_fp8_pp(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const float* descale, int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
+    using Cfg = FwdFp8Cfg<128>;
+    const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
+    static std::atomic<int> slots{0};
+    const int grid = persistent_grid((const void*)fwd_fp8_pp_kernel<128, CAUSAL>, Cfg::kThreads, nmb * Hq * B, slots);
+    hipLaunchKernelGGL((fwd_fp8_pp_kernel<128, CAUSAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
+                       (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (uint16_t*)o, lse, descale, B, Hq,
+                       Hkv, N, scale);
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd_fp8(int d, int causal, const void* q, const void* k, const void* v, void* o, float* lse,
                           const float* descale, int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
+    if (d == 128) return causal ? launch_fp8_pp<true>(q, k, v, o, lse, descale, B, Hq, Hkv, N, scale, st)
+                                : launch_fp8_pp<false>(q, k, v, o, lse, descale, B, Hq, Hkv, N, scale, st);
+    // d = 64: a row group of a 64-key tile is 16 rows of 64 bytes, fewer
+    // groups than the eight waves of the ping-pong kernel; the four-wave
+    // kernel above handles it
     const int nmb = (N + 127) / 128;
     const dim3 grid((unsigned)((int64_t)nmb * Hq * B)), block(256);
 #define FA_FP8_CASE(DD)                                                                                 \
@@ -312,7 +647,6 @@ hipError_t launch_fwd_fp8(int d, int causal, const void* q, const void* k, const
         return hipGetLastError();                                                                       \
     }
     FA_FP8_CASE(64)
-    FA_FP8_CASE(128)
 #undef FA_FP8_CASE
     return hipErrorInvalidValue;
 }
