@@ -116,41 +116,44 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         const int qt0 = CAUSAL ? k0 / BMQ : 0;          // earlier query blocks see none of these keys
         const int total = G * (nqt - qt0);              // steps: (head g*G + i / (nqt-qt0), block qt0 + i % (nqt-qt0))
 
-        // ---- direct loads of step u (issued in step order: one running position).
+        // ---- direct loads of step u, issued in step order.  The next step's
+        // rows are kept as running element offsets: one for Q and dO (the two
+        // share a layout) and one for the statistics rows; both move on by a
+        // block per step and to the next head of the group after the last block.
         // The per-lane offsets are recomputed at every issue from an opaque copy
         // of the lane index: kept live across the loop they would be spilled, and
         // a scratch reload is a vector-memory load whose wait would also drain
         // the tile loads in flight.
-        int ih = 0, iq = qt0;                           // head offset and query block of the next step to load
+        const int64_t bg0 = (int64_t)b * Hq + g * G;    // first query head of the group
+        int64_t qo = (bg0 * N + qt0 * BMQ) * D;
+        int64_t so = bg0 * Npad + qt0 * BMQ;
+        int qrem = N - qt0 * BMQ;                       // rows from the next step's first row to the head's end
+        // statistics: chunk c < BMQ/4 of a stage holds LSE*log2e rows 4c.., the
+        // rest -D rows; chunk c is loaded by wave c / kStatPerWave, so the first
+        // half of the waves loads LSE rows and the second half -D rows
+        const float* Sw = (wave < NW / 2 ? WSl : WSd) + 4 * Cfg::kStatPerWave * (wave % (NW / 2));
         int u_next = 0;
         auto issue = [&](int u) __attribute__((always_inline)) {
-            const int64_t bh = (int64_t)b * Hq + g * G + ih;
-            const int q0 = iq * BMQ;
             const uint32_t st = lds_addr(smem + (u % NS) * Cfg::kStageBytes);
-            const uint16_t* qb = Q + (bh * N + q0) * D;
-            const uint16_t* ob = dO + (bh * N + q0) * D;
-            const int rows_valid = N - q0;
             int ln = lane;
             asm volatile("" : "+v"(ln));
 #pragma unroll
             for (int i = 0; i < QT::kPerWave; ++i) {
                 const int row = (i * NW + wave) * QT::RG + ln % QT::RG;
-                const int grow = row < rows_valid ? row : rows_valid - 1;
+                const int grow = row < qrem ? row : qrem - 1;
                 const uint32_t off = (uint32_t)(grow * D + (ln / QT::RG) * 8) * 2u;
-                dma16s(qb, off, st + (i * NW + wave) * QT::RGS);
-                dma16s(ob, off, st + QT::kBytes + (i * NW + wave) * QT::RGS);
+                dma16s(Q + qo, off, st + (i * NW + wave) * QT::RGS);
+                dma16s(dO + qo, off, st + QT::kBytes + (i * NW + wave) * QT::RGS);
             }
-            // statistics: chunk c < BMQ/4 holds LSE*log2e rows q0+4c.., the rest D rows
-            const int c = wave * Cfg::kStatPerWave + lane;
-            if (lane < Cfg::kStatPerWave) {
-                const float* src = c < BMQ / 4 ? WSl + bh * Npad + q0 + 4 * c : WSd + bh * Npad + q0 + 4 * (c - BMQ / 4);
-                dma16(src, st + 2 * QT::kBytes + 16 * wave * Cfg::kStatPerWave);
+            if (ln < Cfg::kStatPerWave) dma16s(Sw + so, 16u * (uint32_t)ln, st + 2 * QT::kBytes + 16 * wave * Cfg::kStatPerWave);
+            qo += BMQ * D;
+            so += BMQ;
+            qrem -= BMQ;
+            if (qrem <= 0) {                            // past the head's last block: the next head, block qt0
+                qo += ((int64_t)N - (nqt - qt0) * BMQ) * D;
+                so += Npad - (nqt - qt0) * BMQ;
+                qrem = N - qt0 * BMQ;
             }
-            if (++iq == nqt) {
-                iq = qt0;
-                ++ih;
-            }
-            (void)u;
         };
         VT::load(Vg + (int64_t)k0 * D, N - k0, Vl, wave, lane);
 #pragma unroll
