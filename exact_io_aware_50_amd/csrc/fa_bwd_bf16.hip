@@ -245,10 +245,13 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
             // the read-ahead altogether)
             sched_dkdv_phase<D == 128 && CAUSAL ? 8 : 4, 4 * QB>();
         };
-        // X(i): step i's query block is xq
+        // X(i): step i's query block is xq.  `mid` (the phase's loads) is
+        // issued after the first query block's exponentials, whose results it
+        // waits for
         int xq = qt0;
-        auto softmax = [&](int i) __attribute__((always_inline)) {
+        auto softmax = [&](int i, auto&& mid) __attribute__((always_inline)) {
             if (i >= total) {
+                mid();
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) pb[qb][0] = pb[qb][1] = sb[qb][0] = sb[qb][1] = u32x4{};
                 return;
@@ -270,6 +273,10 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
                         const int r = 4 * gq + j;
                         sacc[qb][r] = fast_exp2(fmaf(sacc[qb][r], c2, -l4[j]));
                     }
+                }
+                if (qb == 0) {
+                    settle(sacc[qb]);                    // the exponentials stay above the loads
+                    mid();
                 }
                 if (need_mask) {
                     const int delta = krow - q0 - 32 * qb - 4 * hh;
@@ -300,9 +307,9 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         };
 
         // ---- phases (slot s ends with a barrier).  In loop round i both groups
-        // load step i+NS-2 (that stage held step i-2, last read in slot 2i-1) at
-        // the start of their vector phase (slot 2i+1 for the first group, 2i for
-        // the second); before the barrier ending odd slot s, step tv = (s+1)/2
+        // load step i+NS-2 (that stage held step i-2, last read in slot 2i-1) in
+        // their vector phase (slot 2i+1 for the first group, 2i for the
+        // second); before the barrier ending odd slot s, step tv = (s+1)/2
         // has landed, while up to NS-3 later steps may still be in flight.
         static_assert(NS >= 4 && (NS - 3) * kLoads <= 63, "vmcnt range");
         auto refill = [&](int i) __attribute__((always_inline)) {
@@ -325,13 +332,12 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
             init_dp(0);
             do_sdp(0);
             lds_barrier();
-            softmax(0);
+            softmax(0, [] {});
             tail_odd(1);
             for (int i = 1; i <= total; ++i) {
                 gemm(i);
                 lds_barrier();
-                refill(i);
-                softmax(i);
+                softmax(i, [&] { refill(i); });
                 tail_odd(2 * i + 1);
             }
         } else {
@@ -341,8 +347,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
             do_sdp(0);
             tail_odd(1);
             for (int i = 1; i <= total; ++i) {
-                refill(i);
-                softmax(i - 1);
+                softmax(i - 1, [&] { refill(i); });
                 lds_barrier();
                 gemm(i);
                 tail_odd(2 * i + 1);

@@ -382,6 +382,7 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
 // later pipelined loop, where they would also drain the asm-issued loads.
 __device__ __forceinline__ void settle(const u32x4& x) { asm volatile("" : : "v"(x)); }
 __device__ __forceinline__ void settle(float x) { asm volatile("" : : "v"(x)); }
+__device__ __forceinline__ void settle(const f32x16& x) { asm volatile("" : : "v"(x)); }
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
