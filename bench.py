@@ -127,6 +127,38 @@ def cpu_baseline(w, seconds):
                       f"{w.name.split(' ')[0]}; credited flops of those heads / compute time ({elapsed:.1f} s)"}
 
 
+def gemm_reference(torch, dev, stream, kern, n=8192, iters=15):
+    """Context for the TFLOP/s figures: the vendor library's bf16 GEMM (torch.matmul) on one
+    n x n x n product, with seeded N(0,1) operands and with all-zero operands.  The matrix cores
+    draw less power on zeros and the chip then holds a higher clock, so the gap between the two
+    shows how far the published peak is from what random data sustains.  Each kernel's TFLOP/s
+    is also given as a fraction of the N(0,1) rate."""
+    g = torch.Generator(device=dev).manual_seed(1234)
+    out = {"shape": [n, n, n], "dtype": "bf16"}
+    for kind in ("randn", "zeros"):
+        if kind == "randn":
+            a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+            b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+        else:
+            a = torch.zeros(n, n, device=dev, dtype=torch.bfloat16)
+            b = torch.zeros(n, n, device=dev, dtype=torch.bfloat16)
+        c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            torch.matmul(a, b, out=c)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        out[f"tflops_{kind}"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+        del a, b, c
+    out["kernel_frac_of_randn"] = {k: round(v["tflops"] / out["tflops_randn"], 3)
+                                   for k, v in kern.items() if "tflops" in v}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +168,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the vendor bf16 GEMM timed for context (practical MFMA rate on this data)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -271,6 +305,11 @@ def main():
                              "frac_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
                              "note": "E4M3 forward of the same shape, inputs quantised per tensor outside the timing"}
         log(f"fp8 forward {t8:.3f} ms ({tf8:.0f} TFLOP/s)")
+
+    if not args.no_gemm_reference and w.dtype == "bf16":
+        result["gemm_reference"] = gemm_reference(torch, dev, stream, kern)
+        log("vendor bf16 GEMM 8192^3: {} TFLOP/s on N(0,1) data, {} on zeros".format(
+            result["gemm_reference"]["tflops_randn"], result["gemm_reference"]["tflops_zeros"]))
 
     if args.copy_mib > 0:
         n = args.copy_mib * (1 << 20) // 4
