@@ -235,8 +235,16 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
                     for (int j = 0; j < 4; ++j) dpacc[qb][4 * gq + j] = d4[j];
                 }
         };
-        // G(i), i >= 1 (i == total: the products of the last step only)
+        // G(i), i >= 1 (i == total: the products of the last step only).  gb is
+        // the query block of step i.  Causal: the first nd blocks of each head
+        // lie wholly before this wave's keys (P = dS = 0); a phase whose two
+        // steps are both such blocks is void and skipped (the slot takes as
+        // long, but the matrix cores spend no power on it)
+        int gb = qt0;
+        const int nd = CAUSAL ? 32 * wave / BMQ : 0;
         auto gemm = [&](int i) __attribute__((always_inline)) {
+            if (++gb == nqt) gb = qt0;
+            if (gb > qt0 && gb - qt0 < nd) return;
             init_dp(i);
             do_dvdk(i - 1);
             do_sdp(i);

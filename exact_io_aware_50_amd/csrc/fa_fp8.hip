@@ -485,6 +485,9 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
         // them (and their completion) before the barrier.  The matrix phase is
         // much shorter than the vector phase here, so the wait costs nothing.
         auto gemm = [&](int t) __attribute__((always_inline)) {
+            // causal: past t = ntw the scores are unused and P is zero; the
+            // phase is skipped (no time saved in the slot, power saved)
+            if (CAUSAL && t > ntw) return;
             do_s(t);
             do_pv(t - 1);
             sched_fp8_phase();

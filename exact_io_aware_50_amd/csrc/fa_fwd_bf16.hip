@@ -189,8 +189,12 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
                         oacc[ct] = mma_bf16(KT::tr8(Vs, 32 * kb + 16 * t2, 32 * ct, lane), pf[kb][t2], oacc[ct]);
         };
         // G(t), t >= 1: scores of tile t (past this wave's last tile they are
-        // discarded) and the product of tile t-1 (P is zero past the last tile)
+        // discarded) and the product of tile t-1 (P is zero past the last
+        // tile).  Causal: past t = ntw both are void and the wave skips the
+        // phase; the slot takes as long, but the matrix cores spend no power
+        // on it.
         auto gemm = [&](int t) __attribute__((always_inline)) {
+            if (CAUSAL && t > ntw) return;
             do_s(t);
             do_pv(t - 1);
             sched_gemm_phase<D>();
