@@ -317,8 +317,11 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
 //    one column over eight keys, in the order its P bytes hold the keys.
 //  - P is scaled by 2^7 before its E4M3 rounding (exp2(c s - m + 7)), and the
 //    running max is moved when a row grows by more than a factor 2, so the
-//    scaled P stays at most 256, below the largest E4M3 value 448; l adds the
-//    unrounded scaled values and the scale leaves with it.
+//    scaled P stays at most 256, below the largest E4M3 value 448.
+//  - l is the sum of the rounded scaled P that the P V product weighs V with,
+//    formed on the matrix cores: one more fp8 product per tile, of a ones
+//    operand with P (every output row is the key sum of its query column),
+//    instead of 32 vector additions per lane.  The scale leaves with l.
 template <int D>
 struct FwdFp8Cfg {
     static constexpr int kWaves = 8;                  // two groups of four, one wave of each per SIMD
@@ -334,7 +337,7 @@ struct FwdFp8Cfg {
 
 // G phase order: the K fragments (two reads) of the score products, then the
 // V^T fragments (four reads) of the P V products, each read three products
-// ahead.
+// ahead; the row-sum product (no reads) while the first reads are in flight.
 __device__ __forceinline__ void sched_fp8_phase() {
     constexpr int NS_ = 4, NT = 8, A = 3;
 #pragma unroll
@@ -342,6 +345,7 @@ __device__ __forceinline__ void sched_fp8_phase() {
         if (f < NS_) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         else __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -437,7 +441,11 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
         f32x16 oacc[D / 32];
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
-        float m = kNegBig, lsum = 0.f;
+        float m = kNegBig;
+        f32x16 lacc = zero16();                           // row sums of the rounded scaled P (all rows alike)
+        u32x8 ones;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ones[i] = 0x38383838u;   // E4M3 1.0 in every byte
         f32x16 sacc[KB];
         u32x8 pf = {};
 #pragma unroll
@@ -480,6 +488,7 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
                 oacc[ct] = mma_fp8(a, pf, oacc[ct]);
             }
         };
+        auto do_rowsum = [&]() __attribute__((always_inline)) { lacc = mma_fp8(ones, pf, lacc); };
         // The scaled fp8 products are not held in their phase by the ordering
         // hints alone: consuming their results at the end of the phase keeps
         // them (and their completion) before the barrier.  The matrix phase is
@@ -488,6 +497,7 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
             // causal: past t = ntw the scores are unused and P is zero; the
             // phase is skipped (no time saved in the slot, power saved)
             if (CAUSAL && t > ntw) return;
+            do_rowsum();
             do_s(t);
             do_pv(t - 1);
             sched_fp8_phase();
@@ -495,6 +505,7 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
             for (int kb = 0; kb < KB; ++kb) settle16(sacc[kb]);
 #pragma unroll
             for (int ct = 0; ct < D / 32; ++ct) settle16(oacc[ct]);
+            settle16(lacc);
         };
         // X(t)
         auto softmax = [&](int t) __attribute__((always_inline)) {
@@ -524,27 +535,22 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
             if (__any(mnew > m + Cfg::kTau)) {
                 const float alpha = fast_exp2(m - mnew);
                 m = mnew;
-                lsum *= alpha;
+                lacc *= alpha;
 #pragma unroll
                 for (int ct = 0; ct < D / 32; ++ct) oacc[ct] *= alpha;
             }
             // P * 2^7 = exp2(c2 s - m + 7), packed to E4M3: byte e of pf is
             // register e % 16 of key block e / 16
             const float base = Cfg::kPLog2 - m;
-            float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
                 float p[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[i] = fast_exp2(fmaf(sacc[w >> 2][4 * (w & 3) + i], c2, base));
-                    rs[i] += p[i];
-                }
+                for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sacc[w >> 2][4 * (w & 3) + i], c2, base));
                 int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
                 pk = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], pk, true);
                 pf[w] = (uint32_t)pk;
             }
-            lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
             settle8(pf);
         };
 
@@ -597,7 +603,8 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
         }
 
         // ---- epilogue: O = s_V O_acc / l, LSE = ln2 (m + log2(l / 2^7))
-        const float ltot = pair_sum(lsum);
+        // (G(t) adds the row sums of P_{t-1}, so G(ntiles) added the last tile's)
+        const float ltot = lacc[0];
         if (qrow < N) {
             const float f = sv / ltot;
             int le = lane;
