@@ -89,6 +89,44 @@ def stored_traffic(kernel, workload):
     return float(rec["bytes_per_launch"])
 
 
+def decode_bytes(dw):
+    """Bytes a decode step must move: the K and V cache once, Q in, O and LSE out."""
+    return 2 * dw.B * dw.Hkv * dw.Nk * dw.d * 2 + 2 * dw.B * dw.Hq * dw.Nq * dw.d * 2 + 4 * dw.B * dw.Hq * dw.Nq
+
+
+def decode_leg(torch, fa, I, dev, stream, args):
+    """fa_decode (split over key chunks, then the merge) on the decode workload, HIP events on the launch stream.
+
+    The cache read bounds it: the roofline is HBM bandwidth over decode_bytes."""
+    dw = I.DECODE_WORKLOADS[args.decode_workload]
+    q, k, v = (I.decode_tensor(dw, t).to(dev) for t in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((dw.B, dw.Hq, dw.Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_decode_workspace_bytes(dw.B, dw.Hq, dw.Hkv, dw.Nq, dw.Nk, dw.d) // 4,
+                     dtype=torch.float32, device=dev)
+    sh = stream.cuda_stream
+
+    def run():
+        st = fa.fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), ws.data_ptr(),
+                          dw.B, dw.Hq, dw.Hkv, dw.Nq, dw.Nk, dw.d, dw.causal, dw.scale, fa.FA_DTYPE_BF16, sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_decode")
+
+    for _ in range(args.warmup):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = decode_bytes(dw) / (ms * 1e-3) / 1e9
+    return {"workload": args.decode_workload, "ms": round(ms, 4), "bytes": decode_bytes(dw),
+            "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bound": "hbm",
+            "note": "fa_decode: split kernel plus merge; bytes = K and V cache once + Q + O + LSE"}
+
+
 def cpu_baseline(w, seconds):
     """Time the float64 oracle (forward + backward, P materialised) on whole heads."""
     import numpy as np
@@ -170,6 +208,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-gemm-reference", action="store_true",
                     help="skip the vendor bf16 GEMM timed for context (practical MFMA rate on this data)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode (KV cache) leg")
+    ap.add_argument("--decode-workload", default="decode_gqa_bf16_n16384")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -305,6 +345,12 @@ def main():
                              "frac_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
                              "note": "E4M3 forward of the same shape, inputs quantised per tensor outside the timing"}
         log(f"fp8 forward {t8:.3f} ms ({tf8:.0f} TFLOP/s)")
+
+    if not args.no_decode:
+        result["decode"] = decode_leg(torch, fa, I, dev, stream, args)
+        log("decode {}: {} ms, {} GB/s ({:.1%} of HBM peak)".format(
+            result["decode"]["workload"], result["decode"]["ms"], result["decode"]["gbs"],
+            result["decode"]["frac_hbm"]))
 
     if not args.no_gemm_reference and w.dtype == "bf16":
         result["gemm_reference"] = gemm_reference(torch, dev, stream, kern)

@@ -145,6 +145,44 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
                                            stream));
 }
 
+// Shape checks of the decode entry points; sets *empty for an empty problem.
+static fa_status_t check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                                bool* empty) {
+    if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_UNSUPPORTED;
+    *empty = (B == 0 || Hq == 0 || Nq == 0);
+    if (*empty) return FA_OK;
+    if (Hkv == 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    // every query row must see at least one key
+    if (Nk == 0 || (causal && Nq > Nk)) return FA_ERR_SHAPE;
+    const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk);
+    const int64_t units = (int64_t)B * Hkv * p.nrb * p.nsplit;
+    const int64_t rows = (int64_t)B * Hq * Nq;
+    if (units / 4 + 1 > INT32_MAX || rows / 4 + 1 > INT32_MAX) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    bool empty = false;
+    if (check_decode(B, Hq, Hkv, Nq, Nk, d, 0, 1.0f, &empty) != FA_OK || empty) return 0;
+    return fa::decode_ws_bytes(fa::decode_plan(B, Hq, Hkv, Nq, Nk), B, Hq, Nq, d);
+}
+
+fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int B, int Hq,
+                      int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale, int dtype,
+                      hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_decode(B, Hq, Hkv, Nq, Nk, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    s = check_ptrs({q, k, v}, {}, {o, ws}, {lse});
+    if (s != FA_OK) return s;
+    return launch_status(fa::launch_decode(d, causal, q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, softmax_scale,
+                                           stream));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N) {
     if (B <= 0 || Hq <= 0 || N <= 0) return 0;
     return (size_t)8 * (size_t)B * (size_t)Hq * (size_t)fa::ws_rows(N);

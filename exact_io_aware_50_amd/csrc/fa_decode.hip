@@ -1,0 +1,259 @@
+// Attention of a few new query rows against a long key/value cache (decode),
+// split over the keys.
+//
+// "Paper digest: FlashAttention", section "Limits": attention at decode time
+// reads a large KV cache for few new queries and has a bottleneck of its own;
+// the self-hosted LLM glossary, entries "KV Cache" (the keys and values of all
+// earlier tokens, read again for every new token) and "Grouped-Query
+// Attention" (query heads in groups share one key/value head).  The result is
+// the same exact softmax attention: new query row i (of Nq) attends to every
+// cache key j <= Nk - Nq + i when causal (the new rows are the last Nq
+// positions of the sequence), to all Nk keys otherwise.
+//
+// What bounds it on gfx950 is the one pass over the cache at HBM bandwidth;
+// the products are small.  So:
+//  - the query rows of the G heads that share a K/V head are packed into the
+//    32 columns of one matrix-core block (packed row r = head-in-group * Nq +
+//    i), so K and V are read once per group, not once per query head;
+//  - the keys are cut into chunks; every wave takes one (batch, K/V head, row
+//    block, chunk) unit on its own, streams the chunk through a private
+//    two-stage LDS ring with direct global->LDS loads, and runs the forward
+//    pass's online softmax on it (S^T = K Q^T, P packed to bf16, O^T += V^T
+//    P^T with transposing LDS reads of V);
+//  - each unit writes its chunk's normalised O and log-sum-exp to a float32
+//    workspace, and a second kernel merges the chunks of every row with the
+//    rescale of the online softmax ("flash attention io aware", section
+//    "Online Softmax": partial results taken against different maxima are
+//    combined after scaling each by exp(m_s - m)).
+#include "fa_device.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+template <int D>
+struct DecCfg {
+    static constexpr int kWaves = 4;                  // independent waves per workgroup (one per SIMD)
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int BN = 32;                     // keys per tile
+    static constexpr int kStages = 2;
+    using KT = LdsTile<BN, D, 1>;                     // one wave fills a whole tile
+    static constexpr int kStage = 2 * KT::kElems;     // elements per stage (K then V)
+    static constexpr float kTau = 8.0f;               // log2 slack before the running max is moved
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    float* __restrict__ Wo, float* __restrict__ Wl, int B, int Hq, int Hkv, int Nq, int Nk, int chunk, int nsplit,
+    float c2) {
+    using Cfg = DecCfg<D>;
+    using KT = typename Cfg::KT;
+    constexpr int BN = Cfg::BN, kStage = Cfg::kStage, KP = KT::kPerWave;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[Cfg::kWaves * Cfg::kStages * kStage];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = Hq / Hkv, R = G * Nq, nrb = (R + 31) / 32;
+    const int64_t u = (int64_t)blockIdx.x * Cfg::kWaves + wave;    // this wave's unit
+    if (u >= (int64_t)B * Hkv * nrb * nsplit) return;               // wave-uniform; no barriers below
+    const int s = (int)(u % nsplit);
+    const int64_t rest = u / nsplit;
+    const int rb = (int)(rest % nrb);
+    const int g = (int)((rest / nrb) % Hkv), b = (int)(rest / nrb / Hkv);
+
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+    const int r = rb * 32 + l32;                      // this lane's packed query row
+    const bool rv = r < R;
+    const int hq = g * G + (rv ? r / Nq : 0), qi = rv ? r % Nq : 0;
+    const int lim = CAUSAL ? Nk - Nq + qi : Nk - 1;   // last key the row sees
+    const int kbeg = s * chunk, kend = min(Nk, kbeg + chunk);
+    const int nt = (kend - kbeg + BN - 1) / BN;
+
+    uint16_t* ring = smem + wave * Cfg::kStages * kStage;
+    const uint16_t* Kg = K + ((int64_t)b * Hkv + g) * Nk * D;
+    const uint16_t* Vg = V + ((int64_t)b * Hkv + g) * Nk * D;
+    // K and V rows of tile t into stage t % 2 (rows past the chunk re-read its last row)
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const uint16_t* st = ring + (t & 1) * kStage;
+        const int k0 = kbeg + t * BN;
+        KT::load(Kg + (int64_t)k0 * D, kend - k0, st, 0, lane);
+        KT::load(Vg + (int64_t)k0 * D, kend - k0, st + KT::kElems, 0, lane);
+    };
+    issue(0);
+    u32x4 qf[D / 16];                                 // this lane's query row as B operands
+    {
+        const uint16_t* qp = Q + (((int64_t)b * Hq + hq) * Nq + qi) * D + 8 * hh;
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+            u32x4 v = {};
+            if (rv) v = *reinterpret_cast<const u32x4*>(qp + 16 * j);
+            qf[j] = v;
+        }
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) settle(qf[j]);
+    }
+    wait_vm<0>();
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
+    float m = kNegBig, lsum = 0.f;
+    for (int t = 0; t < nt; ++t) {
+        // tile t has landed once at most the next tile's loads are outstanding;
+        // the next tile's stage held tile t-1, whose reads all fed products of
+        // the previous iteration
+        if (t + 1 < nt) {
+            issue(t + 1);
+            wait_vm<2 * KP>();
+        } else {
+            wait_vm<0>();
+        }
+        const uint16_t* Ks = ring + (t & 1) * kStage;
+        const uint16_t* Vs = Ks + KT::kElems;
+        // S^T = K_t Q^T: rows = 32 keys, columns = the packed query rows
+        f32x16 sacc = zero16();
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) sacc = mma_bf16(KT::row8(Ks, l32, 2 * j + hh), qf[j], sacc);
+        const int k0 = kbeg + t * BN;
+        if (k0 + BN > kend || (CAUSAL && k0 + BN - 1 > Nk - Nq)) {
+#pragma unroll
+            for (int r2 = 0; r2 < 16; ++r2) {
+                const int key = k0 + acc_row(r2, hh);
+                if (key >= kend || key > lim) sacc[r2] = -INFINITY;
+            }
+        }
+        // online softmax in base 2 (scale * log2 e in c2); the running max is
+        // moved only when some row of the wave grew by more than 2^tau
+        float x = -INFINITY;
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) x = fmaxf(x, sacc[r2]);
+        x = pair_max(x);
+        const float mnew = fmaxf(m, x * c2);
+        if (__any(mnew > m + Cfg::kTau)) {
+            const float alpha = fast_exp2(m - mnew);
+            m = mnew;
+            lsum *= alpha;
+#pragma unroll
+            for (int ct = 0; ct < D / 32; ++ct) oacc[ct] *= alpha;
+        }
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) sacc[r2] = fast_exp2(fmaf(sacc[r2], c2, -m));
+        u32x4 pf[2];
+        float rs[2] = {0.f, 0.f};
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+            pf[t2] = pack_bf16x8(sacc, 8 * t2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rs[i & 1] = dot2_bf16_sum(pf[t2][i], rs[i & 1]);
+        }
+        lsum += rs[0] + rs[1];
+        // O^T += V_t^T P^T
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int ct = 0; ct < D / 32; ++ct)
+                oacc[ct] = mma_bf16(KT::tr8(Vs, 16 * t2, 32 * ct, lane), pf[t2], oacc[ct]);
+    }
+
+    // this chunk's O (normalised) and log-sum-exp; a row that sees no key of
+    // the chunk gets weight zero (LSE = -inf, O = 0)
+    const float lt = pair_sum(lsum);
+    if (rv) {
+        const int64_t row = ((int64_t)b * Hq + hq) * Nq + qi;
+        float* wo = Wo + (row * nsplit + s) * D;
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+#pragma unroll
+        for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                f32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = oacc[ct][4 * gq + e] * inv;
+                *reinterpret_cast<f32x4*>(wo + 32 * ct + 8 * gq + 4 * hh) = w;
+            }
+        if (hh == 0) Wl[row * nsplit + s] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+    }
+}
+
+// One wave per query row: LSE = L + ln(sum_s exp(LSE_s - L)) with L the
+// largest chunk LSE, O = sum_s exp(LSE_s - LSE) O_s.
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ Wo,
+                                                           const float* __restrict__ Wl, uint16_t* __restrict__ O,
+                                                           float* __restrict__ LSE, int64_t rows, int nsplit) {
+    constexpr int PER = D / 64;                       // d values per lane
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const float* wl = Wl + row * nsplit;
+    float L = -INFINITY;
+    for (int s = lane; s < nsplit; s += 64) L = fmaxf(L, wl[s]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L = fmaxf(L, __shfl_xor(L, off));
+    float acc[PER], wsum = 0.f;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) acc[p] = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+        const float ls = wl[s];
+        const float w = ls == -INFINITY ? 0.f : fast_exp2((ls - L) * kLog2e);
+        wsum += w;
+        const float* wo = Wo + (row * nsplit + s) * D + lane * PER;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) acc[p] = fmaf(w, wo[p], acc[p]);
+    }
+    const float inv = 1.0f / wsum;
+    uint16_t* orow = O + row * D + lane * PER;
+    if constexpr (PER == 2) {
+        *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+        orow[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
+    }
+    if (lane == 0) LSE[row] = L + logf(wsum);
+}
+
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk) {
+    DecodePlan p;
+    const int G = Hq / Hkv;
+    p.nrb = (G * Nq + 31) / 32;
+    const int64_t base = (int64_t)B * Hkv * p.nrb;
+    // about 2048 wave units (eight per CU), chunks of at least 256 keys
+    const int64_t want = (2048 + base - 1) / base;
+    const int64_t most = ((int64_t)Nk + 255) / 256;
+    int64_t ns = want < most ? want : most;
+    if (ns < 1) ns = 1;
+    int64_t chunk = ((int64_t)Nk + ns - 1) / ns;
+    chunk = (chunk + 31) / 32 * 32;
+    p.chunk = (int)chunk;
+    p.nsplit = (int)(((int64_t)Nk + chunk - 1) / chunk);
+    return p;
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int B,
+                         int Hq, int Hkv, int Nq, int Nk, float scale, hipStream_t st) {
+    using Cfg = DecCfg<D>;
+    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk);
+    const int64_t rows = (int64_t)B * Hq * Nq;
+    float* wo = ws;
+    float* wl = ws + rows * p.nsplit * D;
+    const int64_t units = (int64_t)B * Hkv * p.nrb * p.nsplit;
+    const unsigned g1 = (unsigned)((units + Cfg::kWaves - 1) / Cfg::kWaves);
+    hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL>), dim3(g1), dim3(Cfg::kThreads), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, wo, wl, B, Hq, Hkv, Nq, Nk, p.chunk, p.nsplit,
+                       scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, wo, wl,
+                       (uint16_t*)o, lse, rows, p.nsplit);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(int d, int causal, const void* q, const void* k, const void* v, void* o, float* lse,
+                         float* ws, int B, int Hq, int Hkv, int Nq, int Nk, float scale, hipStream_t st) {
+    if (d == 64) return causal ? launch<64, true>(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, scale, st)
+                               : launch<64, false>(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, scale, st);
+    if (d == 128) return causal ? launch<128, true>(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, scale, st)
+                                : launch<128, false>(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, scale, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa

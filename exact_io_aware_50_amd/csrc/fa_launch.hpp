@@ -65,4 +65,20 @@ hipError_t launch_bwd_dq_bf16(int d, int causal, const void* q, const void* k, c
 
 hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
 
+// Decode split over the keys: nrb blocks of 32 packed query rows per K/V head,
+// nsplit chunks of `chunk` keys (a multiple of 32).
+struct DecodePlan {
+    int nrb, nsplit, chunk;
+};
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk);
+
+// Workspace of fa_decode: float32 O per (row, chunk) [rows][nsplit][d], then
+// the chunk LSEs [rows][nsplit], rows = B * Hq * Nq.
+inline size_t decode_ws_bytes(const DecodePlan& p, int B, int Hq, int Nq, int d) {
+    return (size_t)4 * (size_t)B * (size_t)Hq * (size_t)Nq * (size_t)p.nsplit * (size_t)(d + 1);
+}
+
+hipError_t launch_decode(int d, int causal, const void* q, const void* k, const void* v, void* o, float* lse,
+                         float* ws, int B, int Hq, int Hkv, int Nq, int Nk, float scale, hipStream_t st);
+
 }  // namespace fa

@@ -43,13 +43,17 @@ _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_quantize_fp8.argtypes = [_p, ctypes.c_size_t, _p, _p, _p]
 _lib.fa_quantize_fp8.restype = _i
+_lib.fa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p]
+_lib.fa_decode.restype = _i
+_lib.fa_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+_lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_status_string.argtypes = [_i]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_abi_version.argtypes = []
 _lib.fa_abi_version.restype = _i
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
-           "fa_quantize_fp8", "fa_status_string", "fa_abi_version")
+           "fa_quantize_fp8", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string", "fa_abi_version")
 
 
 class FAError(RuntimeError):
@@ -91,6 +95,15 @@ def fa_bwd_workspace_bytes(B, Hq, N) -> int:
 
 def fa_quantize_fp8(x_bf16, n, x_e4m3, descale, stream) -> int:
     return _lib.fa_quantize_fp8(x_bf16, n, x_e4m3, descale, stream)
+
+
+def fa_decode(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, d, causal, softmax_scale, dtype, stream) -> int:
+    return _lib.fa_decode(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, d, int(causal), float(softmax_scale), dtype,
+                          stream)
+
+
+def fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d) -> int:
+    return int(_lib.fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d))
 
 
 def fa_status_string(status: int) -> str:
@@ -173,6 +186,29 @@ def bwd(q, k, v, o, do, lse, causal: bool, scale: float, stream=None, workspace=
                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, d, causal,
                   scale, code, _stream_handle(stream)), "fa_bwd")
     return dq, dk, dv, workspace
+
+
+def decode(q, k, v, causal: bool, scale: float, stream=None, workspace=None):
+    """(o, lse) for new query rows q [B,Hq,Nq,d] against a bf16 cache k, v [B,Hkv,Nk,d].
+
+    Causal: the rows are the last Nq positions (row i sees keys j <= Nk - Nq + i)."""
+    torch = _torch()
+    for t in (q, k, v):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous [B, H, N, d] tensors")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if v.shape != k.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] with q's B and d")
+    code = _dtype_code(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d) // 4
+        workspace = torch.empty(max(n, 4), dtype=torch.float32, device=q.device)
+    _check(fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                     B, Hq, Hkv, Nq, Nk, d, causal, scale, code, _stream_handle(stream)), "fa_decode")
+    return o, lse
 
 
 def quantize_fp8(x, stream=None):

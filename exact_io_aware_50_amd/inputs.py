@@ -52,6 +52,47 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """New query rows [B, Hq, Nq, d] against a key/value cache [B, Hkv, Nk, d]."""
+    name: str
+    seed: int
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+
+# The grouped-query shape of the 16K-token workload as a serving step: one new
+# token (and a four-token chunk, causal) per sequence for a batch of 16 against
+# a 16384-token cache; the cache is 1 GiB of bf16.
+DECODE_WORKLOADS = {
+    "decode_gqa_bf16_n16384": DecodeWorkload(
+        "decode_gqa_bf16_n16384 (B=16 Hq=64 Hkv=8 Nq=1 Nk=16384 d=128, bf16)", 6, 16, 64, 8, 1, 16384, 128, False),
+    "decode_gqa_bf16_n16384_q4": DecodeWorkload(
+        "decode_gqa_bf16_n16384_q4 (B=16 Hq=64 Hkv=8 Nq=4 Nk=16384 d=128, causal, bf16)", 7, 16, 64, 8, 4, 16384,
+        128, True),
+}
+
+
+def decode_tensor(w: DecodeWorkload, tensor_id: int, device="cpu"):
+    """Q ([B, Hq, Nq, d]) or the K / V cache ([B, Hkv, Nk, d]) of a decode workload, bf16."""
+    import torch
+    heads, n = (w.Hq, w.Nq) if tensor_id == Q_ID else (w.Hkv, w.Nk)
+    out = torch.empty((w.B, heads, n, w.d), dtype=torch.bfloat16, device=device)
+    for b in range(w.B):
+        for h in range(heads):
+            out[b, h].copy_(torch.from_numpy(slice_normal(w.seed, tensor_id, b, h, n, w.d)).to(torch.bfloat16))
+    return out
+
+
 def slice_normal(seed: int, tensor_id: int, b: int, h: int, n: int, d: int,
                  sigma: float = 1.0) -> np.ndarray:
     """One [n, d] float32 slice of i.i.d. N(0, sigma^2) from its own stream."""

@@ -164,6 +164,40 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int N);
 fa_status_t fa_quantize_fp8(const void* x_bf16, size_t n, void* x_e4m3,
                             float* descale, hipStream_t stream);
 
+/*
+ * Decode: attention of Nq new query rows against a key/value cache of Nk
+ * rows.  "Paper digest: FlashAttention", section "Limits" (decode-time
+ * attention reads a large KV cache for few queries); self-hosted LLM
+ * glossary, entries "KV Cache" (the keys and values of all earlier tokens,
+ * read for every new token) and "Grouped-Query Attention".  Exact softmax
+ * attention as in fa_fwd; with causal = 1 the new rows are the last Nq
+ * positions: row i sees cache keys j <= Nk - Nq + i (so Nq <= Nk is
+ * required); with causal = 0 every row sees all Nk keys.
+ *   q    : [B,Hq,Nq,d] bf16        k, v : [B,Hkv,Nk,d] bf16 (the cache)
+ *   o    : output [B,Hq,Nq,d] bf16
+ *   lse  : output [B,Hq,Nq] float32, natural-log log-sum-exp of the scaled
+ *          scores of each row
+ *   ws   : caller-owned device workspace of fa_decode_workspace_bytes()
+ *          bytes, 16-byte aligned (per-chunk partial results; overwritten)
+ * Two kernels are enqueued: a split over key chunks (one wave per batch, K/V
+ * head, block of 32 packed query rows and chunk) and a merge of the chunks.
+ * dtype must be FA_DTYPE_BF16, d 64 or 128.  Nk == 0, or causal with
+ * Nq > Nk, returns FA_ERR_SHAPE (a row with no visible key); B, Hq or Nq == 0
+ * returns FA_OK and touches nothing.
+ */
+fa_status_t fa_decode(const void* q, const void* k, const void* v,
+                      void* o, float* lse, float* ws,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                      int causal, float softmax_scale, int dtype,
+                      hipStream_t stream);
+
+/*
+ * Bytes of the decode workspace for these sizes (0 for an empty or invalid
+ * problem): 4 * B * Hq * Nq * nsplit * (d + 1), nsplit being the number of
+ * key chunks the library chooses for the shape.
+ */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
 /* Static text for a status code ("unknown status" for other values). */
 const char* fa_status_string(fa_status_t s);
 

@@ -17,7 +17,8 @@ Pages cited throughout (by title and section):
               Bandwidth Bottleneck", "Flash Attention Algorithm", "Online
               Softmax", "Performance Impact" table, "Integration".
   [FA-LLM]    inferensys.com glossary "Flash Attention" (self-hosted LLMs):
-              opening paragraphs; entry "Grouped-Query Attention (GQA)".
+              opening paragraphs; entries "Grouped-Query Attention (GQA)"
+              and "KV Cache".
 
 Parity pins: every function here is pinned by a ``-m "not gpu"`` test against
 closed forms, invariants, finite differences, a library routine (torch CPU
@@ -27,6 +28,7 @@ No function is "parity unpinned".
 from .attention import (  # noqa: F401
     forward,
     forward_online,
+    decode_forward,
     backward,
     probabilities,
     head_rows_forward,

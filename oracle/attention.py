@@ -87,6 +87,41 @@ def forward(q, k, v, causal, scale):
     return O, L
 
 
+def decode_forward(q, k, v, causal, scale):
+    """New query rows against a key/value cache: O [B, Hq, Nq, d] and LSE [B, Hq, Nq].
+
+    q is [B, Hq, Nq, d]; k and v are the cache, [B, Hkv, Nk, d].  [FA-LLM],
+    entry "KV Cache": the keys and values of all earlier tokens are kept and
+    each new token attends to them; [Digest], "Limits": decode-time attention
+    over that cache.  The new rows are the last Nq positions of the sequence,
+    so with the causal mask row i sees cache keys j <= Nk - Nq + i; without
+    it every row sees all Nk keys.  Plain definition per (batch, head): S =
+    scale * q k^T over the visible keys, two-pass softmax, O = P v,
+    LSE = m + ln l.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Nq, _ = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    O = np.empty((B, Hq, Nq, v.shape[3]))
+    L = np.empty((B, Hq, Nq))
+    pos = np.arange(Nk - Nq, Nk)                      # positions of the new rows
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            S = scale * (q[b, h] @ k[b, g].T)
+            if causal:
+                S = np.where(np.arange(Nk)[None, :] <= pos[:, None], S, -np.inf)
+            m = S.max(axis=1)
+            E = np.exp(S - m[:, None])
+            l = E.sum(axis=1)
+            O[b, h] = (E / l[:, None]) @ v[b, g]
+            L[b, h] = m + np.log(l)
+    return O, L
+
+
 def forward_online(q, k, v, causal, scale, block_sizes):
     """Forward by the tiled online softmax, key blocks taken in order.
 

@@ -298,3 +298,63 @@ def test_quantize_per_tensor_scale_and_range():
     assert np.max(np.abs(oracle.e4m3_decode(codes))) == 448.0
     z, sz = oracle.quantize_per_tensor(np.zeros(8, np.float32))
     assert sz == np.float32(2.0 ** -120) / np.float32(448.0) and not z.any()
+
+
+# ---------------------------------------------------------------- decode against a KV cache
+
+DECODE_SHAPES = [  # B, Hq, Hkv, Nq, Nk, d
+    (1, 8, 1, 1, 40, 8),
+    (2, 4, 2, 3, 17, 4),
+    (1, 6, 3, 5, 5, 16),
+    (1, 2, 2, 7, 30, 8),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_matches_torch_cpu_float64_sdpa(shape, causal):
+    """New rows at the end of the sequence: torch SDPA with an explicit bottom-right mask, and torch.logsumexp."""
+    B, Hq, Hkv, Nq, Nk, d = shape
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = rnd(90, (B, Hq, Nq, d)), rnd(91, (B, Hkv, Nk, d)), rnd(92, (B, Hkv, Nk, d))
+    O, L = oracle.decode_forward(q, k, v, causal, scale)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64) for x in (q, k, v))
+    mask = None
+    if causal:
+        mask = torch.arange(Nk)[None, :] <= torch.arange(Nk - Nq, Nk)[:, None]
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale,
+                                                          enable_gqa=Hq != Hkv)
+    s = scale * (tq @ tk.repeat_interleave(Hq // Hkv, dim=1).transpose(-1, -2))
+    if causal:
+        s = s.masked_fill(~mask, float("-inf"))
+    tl = torch.logsumexp(s, dim=-1)
+    assert np.max(np.abs(O - to.numpy())) <= 1e-12
+    assert np.max(np.abs(L - tl.numpy())) <= 1e-12 * max(1.0, float(tl.abs().max()))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_equals_last_rows_of_full_attention(causal):
+    """Decoding the last Nq rows against the whole sequence's cache gives those rows of full attention."""
+    B, Hq, Hkv, N, d, Nq = 1, 4, 2, 23, 8, 6
+    q, k, v = rnd(95, (B, Hq, N, d)), rnd(96, (B, Hkv, N, d)), rnd(97, (B, Hkv, N, d))
+    O, L = oracle.forward(q, k, v, causal, 0.4)
+    Od, Ld = oracle.decode_forward(q[:, :, N - Nq:], k, v, causal, 0.4)
+    assert np.max(np.abs(Od - O[:, :, N - Nq:])) <= 1e-12
+    assert np.max(np.abs(Ld - L[:, :, N - Nq:])) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_identical_keys_and_single_key(causal):
+    """Identical cache keys: O_i = mean of the visible V rows, LSE_i = scale q_i.k + ln(count); one key returns V."""
+    Hq, Nq, Nk, d, scale = 3, 4, 11, 5, 0.7
+    q, v = rnd(98, (1, Hq, Nq, d)), rnd(99, (1, 1, Nk, d))
+    krow = rnd(100, (d,))
+    k = np.broadcast_to(krow, (1, 1, Nk, d)).copy()
+    O, L = oracle.decode_forward(q, k, v, causal, scale)
+    for i in range(Nq):
+        cnt = Nk - Nq + i + 1 if causal else Nk
+        assert np.max(np.abs(O[0, :, i] - v[0, 0, :cnt].mean(axis=0))) <= 1e-12
+        assert np.max(np.abs(L[0, :, i] - (scale * q[0, :, i] @ krow + np.log(cnt)))) <= 1e-12
+    O1, L1 = oracle.decode_forward(q[:, :, :1], k[:, :, :1], v[:, :, :1], causal, scale)
+    assert np.max(np.abs(O1[0, :, 0] - v[0, 0, 0])) <= 1e-15
+    assert np.max(np.abs(L1[0, :, 0] - scale * q[0, :, 0] @ krow)) <= 1e-12
