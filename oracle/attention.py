@@ -23,14 +23,26 @@ import numpy as np
 ROW_BLOCK = 256   # rows materialised at once; each block still holds full rows of S and P
 
 
-def _visible(rows: np.ndarray, n_keys: int, causal: bool) -> np.ndarray | None:
-    """Boolean mask [len(rows), n_keys] of visible keys, or None when all are."""
+def _visible(rows: np.ndarray, n_keys: int, causal: bool, window=None) -> np.ndarray | None:
+    """Boolean mask [len(rows), n_keys] of visible keys, or None when all are.
+
+    ``window`` (with the causal mask only) is the sliding window of local
+    attention ([FA-legal], entry "Block-sparse": sliding-window (local)
+    attention is one of the named sparsity patterns): key j is visible to
+    query i iff i - window < j <= i.
+    """
+    if window is not None and not causal:
+        raise ValueError("the sliding window is defined with the causal mask")
     if not causal:
         return None
-    return np.arange(n_keys)[None, :] <= rows[:, None]
+    keys = np.arange(n_keys)[None, :]
+    vis = keys <= rows[:, None]
+    if window is not None:
+        vis &= keys > rows[:, None] - int(window)
+    return vis
 
 
-def probabilities(qh, kg, scale, causal, rows=None):
+def probabilities(qh, kg, scale, causal, rows=None, window=None):
     """Rows of S and P = softmax(S), plus the row max m and row sum l.
 
     [IO-aware], "The Memory Bandwidth Bottleneck", steps 1-2: S = Q K^T, then
@@ -44,7 +56,7 @@ def probabilities(qh, kg, scale, causal, rows=None):
     n = kg.shape[0]
     rows = np.arange(qh.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
     S = scale * (qh[rows] @ kg.T)
-    vis = _visible(rows, n, causal)
+    vis = _visible(rows, n, causal, window)
     if vis is not None:
         S = np.where(vis, S, -np.inf)
     m = S.max(axis=1)
@@ -54,7 +66,7 @@ def probabilities(qh, kg, scale, causal, rows=None):
     return S, P, m, l
 
 
-def head_rows_forward(qh, kg, vg, rows, causal, scale):
+def head_rows_forward(qh, kg, vg, rows, causal, scale, window=None):
     """O and LSE for the given query rows of one head, in row blocks.
 
     [IO-aware], "The Memory Bandwidth Bottleneck", step 3: O = P V.
@@ -66,13 +78,13 @@ def head_rows_forward(qh, kg, vg, rows, causal, scale):
     L = np.empty(rows.size)
     for s in range(0, rows.size, ROW_BLOCK):
         r = rows[s:s + ROW_BLOCK]
-        _, P, m, l = probabilities(qh, kg, scale, causal, r)
+        _, P, m, l = probabilities(qh, kg, scale, causal, r, window)
         O[s:s + r.size] = P @ vg
         L[s:s + r.size] = m + np.log(l)
     return O, L
 
 
-def forward(q, k, v, causal, scale):
+def forward(q, k, v, causal, scale, window=None):
     """Full forward over [B, Hq, N, d]: returns O [B, Hq, N, d] and LSE [B, Hq, N]."""
     q = np.asarray(q, dtype=np.float64)
     B, Hq, N, d = q.shape
@@ -83,7 +95,7 @@ def forward(q, k, v, causal, scale):
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            O[b, h], L[b, h] = head_rows_forward(q[b, h], k[b, g], v[b, g], rows, causal, scale)
+            O[b, h], L[b, h] = head_rows_forward(q[b, h], k[b, g], v[b, g], rows, causal, scale, window)
     return O, L
 
 
@@ -171,7 +183,7 @@ def forward_online(q, k, v, causal, scale, block_sizes):
     return O, L
 
 
-def backward(q, k, v, do, causal, scale):
+def backward(q, k, v, do, causal, scale, window=None):
     """Gradients of O = softmax(scale Q K^T [+mask]) V for a loss with dL/dO = dO.
 
     The pages do not print the backward; [FA-legal] (backward paragraph and
@@ -196,7 +208,7 @@ def backward(q, k, v, do, causal, scale):
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            _, P, _, _ = probabilities(q[b, h], k[b, g], scale, causal)
+            _, P, _, _ = probabilities(q[b, h], k[b, g], scale, causal, window=window)
             O = P @ v[b, g]
             dv[b, g] += P.T @ do[b, h]
             dP = do[b, h] @ v[b, g].T
@@ -208,7 +220,7 @@ def backward(q, k, v, do, causal, scale):
     return dq, dk, dv, Dall
 
 
-def head_rows_backward_dq(qh, kg, vg, doh, rows, causal, scale):
+def head_rows_backward_dq(qh, kg, vg, doh, rows, causal, scale, window=None):
     """dQ rows of one head (and their O, LSE, D), from full rows of P.
 
     Same chain rule as ``backward`` restricted to the given query rows: D of
@@ -224,7 +236,7 @@ def head_rows_backward_dq(qh, kg, vg, doh, rows, causal, scale):
     Dr = np.empty(rows.size)
     for s in range(0, rows.size, ROW_BLOCK):
         r = rows[s:s + ROW_BLOCK]
-        _, P, m, l = probabilities(qh, kg, scale, causal, r)
+        _, P, m, l = probabilities(qh, kg, scale, causal, r, window)
         Or = P @ vg
         dP = doh[r] @ vg.T
         D = (doh[r] * Or).sum(axis=1)
@@ -236,15 +248,15 @@ def head_rows_backward_dq(qh, kg, vg, doh, rows, causal, scale):
     return dQ, O, L, Dr
 
 
-def head_full_stats(qh, kg, vg, doh, causal, scale):
+def head_full_stats(qh, kg, vg, doh, causal, scale, window=None):
     """LSE and D = rowsum(dO * O) for every row of one head (row blocks, full rows of P)."""
     n = np.asarray(qh).shape[0]
-    O, L = head_rows_forward(qh, kg, vg, np.arange(n), causal, scale)
+    O, L = head_rows_forward(qh, kg, vg, np.arange(n), causal, scale, window)
     D = (np.asarray(doh, dtype=np.float64) * O).sum(axis=1)
     return L, D
 
 
-def head_cols_backward_dkdv(q_heads, kg, vg, do_heads, stats, cols, causal, scale):
+def head_cols_backward_dkdv(q_heads, kg, vg, do_heads, stats, cols, causal, scale, window=None):
     """dK and dV rows (key positions ``cols``) of one key/value head.
 
     For each query head h of the group, with its full-row LSE and D
@@ -265,7 +277,10 @@ def head_cols_backward_dkdv(q_heads, kg, vg, do_heads, stats, cols, causal, scal
         doh = np.asarray(doh, dtype=np.float64)
         S = scale * (qh @ kg[cols].T)                      # [n, |cols|]
         if causal:
-            S = np.where(cols[None, :] <= rows[:, None], S, -np.inf)
+            vis = cols[None, :] <= rows[:, None]
+            if window is not None:
+                vis &= cols[None, :] > rows[:, None] - int(window)
+            S = np.where(vis, S, -np.inf)
         P = np.exp(S - np.asarray(L)[:, None])
         dP = doh @ vg[cols].T
         dS = P * (dP - np.asarray(D)[:, None])

@@ -358,3 +358,74 @@ def test_decode_identical_keys_and_single_key(causal):
     O1, L1 = oracle.decode_forward(q[:, :, :1], k[:, :, :1], v[:, :, :1], causal, scale)
     assert np.max(np.abs(O1[0, :, 0] - v[0, 0, 0])) <= 1e-15
     assert np.max(np.abs(L1[0, :, 0] - scale * q[0, :, 0] @ krow)) <= 1e-12
+
+
+# ---------------------------------------------------------------- sliding window (local attention)
+
+@pytest.mark.parametrize("window", [1, 3, 7, 19, 100])
+def test_local_matches_torch_cpu_float64_sdpa_with_band_mask(window):
+    """Causal sliding window: torch SDPA + autograd with an explicit band mask (i - W < j <= i)."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 19, 8
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, do = (rnd(110 + i, (B, H, N, d)) for i, H in enumerate((Hq, Hkv, Hkv, Hq)))
+    O, L = oracle.forward(q, k, v, True, scale, window=window)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, True, scale, window=window)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    i, j = torch.arange(N)[:, None], torch.arange(N)[None, :]
+    band = (j <= i) & (j > i - window)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=band, scale=scale, enable_gqa=True)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    s = scale * (tq.detach() @ tk.detach().repeat_interleave(Hq // Hkv, dim=1).transpose(-1, -2))
+    tl = torch.logsumexp(s.masked_fill(~band, float("-inf")), dim=-1)
+    for a, b in ((O, o.detach()), (L, tl), (dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.max(np.abs(a - b.numpy())) <= 1e-12 * max(1.0, float(b.abs().max()))
+
+
+def test_local_window_limits():
+    """W >= N is plain causal attention; W = 1 lets each row see itself only (O_i = V_i, LSE_i = scale q_i.k_i)."""
+    B, Hq, Hkv, N, d, scale = 1, 2, 1, 13, 6, 0.4
+    q, k, v, do = (rnd(120 + i, (B, H, N, d)) for i, H in enumerate((Hq, Hkv, Hkv, Hq)))
+    for W in (N, N + 5):
+        Ow, Lw = oracle.forward(q, k, v, True, scale, window=W)
+        Oc, Lc = oracle.forward(q, k, v, True, scale)
+        assert np.max(np.abs(Ow - Oc)) <= 1e-15 and np.max(np.abs(Lw - Lc)) <= 1e-15
+    O1, L1 = oracle.forward(q, k, v, True, scale, window=1)
+    for h in range(Hq):
+        assert np.max(np.abs(O1[0, h] - v[0, 0])) <= 1e-15
+        assert np.max(np.abs(L1[0, h] - scale * (q[0, h] * k[0, 0]).sum(axis=1))) <= 1e-12
+    dq1, dk1, dv1, _ = oracle.backward(q, k, v, do, True, scale, window=1)
+    # one visible key: the softmax is constant 1, so dQ = dK = 0 and dV_j = sum over heads of dO_j
+    assert np.max(np.abs(dq1)) <= 1e-15 and np.max(np.abs(dk1)) <= 1e-15
+    assert np.max(np.abs(dv1[0, 0] - do[0].sum(axis=0))) <= 1e-12
+
+
+def test_local_backward_matches_central_differences():
+    B, Hq, Hkv, N, d, scale, W = 1, 2, 1, 9, 4, 0.6, 4
+    q, k, v, do = (rnd(130 + i, (B, H, N, d)) for i, H in enumerate((Hq, Hkv, Hkv, Hq)))
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, True, scale, window=W)
+    loss = lambda q_, k_, v_: float((oracle.forward(q_, k_, v_, True, scale, window=W)[0] * do).sum())
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert np.linalg.norm(num - g) <= 1e-6 * np.linalg.norm(g)
+
+
+def test_local_sampled_rows_and_columns_match_full():
+    B, Hq, Hkv, N, d, scale, W = 1, 2, 1, 40, 8, 0.3, 11
+    q, k, v, do = (rnd(140 + i, (B, H, N, d)) for i, H in enumerate((Hq, Hkv, Hkv, Hq)))
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, True, scale, window=W)
+    O, L = oracle.forward(q, k, v, True, scale, window=W)
+    rows = np.array([0, 5, 10, 11, 39])
+    dQr, Or, Lr, _ = oracle.head_rows_backward_dq(q[0, 1], k[0, 0], v[0, 0], do[0, 1], rows, True, scale, window=W)
+    assert np.max(np.abs(dQr - dq[0, 1, rows])) <= 1e-12 and np.max(np.abs(Or - O[0, 1, rows])) <= 1e-12
+    stats = [oracle.head_full_stats(q[0, h], k[0, 0], v[0, 0], do[0, h], True, scale, window=W) for h in range(2)]
+    dKc, dVc = oracle.head_cols_backward_dkdv([q[0, 0], q[0, 1]], k[0, 0], v[0, 0], [do[0, 0], do[0, 1]], stats,
+                                             rows, True, scale, window=W)
+    assert np.max(np.abs(dKc - dk[0, 0, rows])) <= 1e-12 and np.max(np.abs(dVc - dv[0, 0, rows])) <= 1e-12
