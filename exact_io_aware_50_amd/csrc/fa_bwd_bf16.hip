@@ -69,12 +69,12 @@ __device__ __forceinline__ void sched_dkdv_phase() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOCAL = false>
 __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int n_rows, int Npad, float c2,
-    float scale) {
+    float scale, int W = 0) {
     using Cfg = KVBf16Cfg<D>;
     using QT = typename Cfg::QT;
     constexpr int NW = Cfg::kWaves, BNK = Cfg::BNK, BMQ = Cfg::BMQ, QB = Cfg::QB, NS = Cfg::kStages;
@@ -114,7 +114,9 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
 
         const int nqt = (N + BMQ - 1) / BMQ;
         const int qt0 = CAUSAL ? k0 / BMQ : 0;          // earlier query blocks see none of these keys
-        const int total = G * (nqt - qt0);              // steps: (head g*G + i / (nqt-qt0), block qt0 + i % (nqt-qt0))
+        // (local) later query blocks than qt1 - 1 see none of them either
+        const int qt1 = LOCAL ? min(nqt, (min(N, k0 + BNK) - 2 + W) / BMQ + 1) : nqt;
+        const int total = G * (qt1 - qt0);              // steps: (head g*G + i / (qt1-qt0), block qt0 + i % (qt1-qt0))
 
         // ---- direct loads of step u, issued in step order.  The next step's
         // rows are kept as running element offsets: one for Q and dO (the two
@@ -128,6 +130,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         int64_t qo = (bg0 * N + qt0 * BMQ) * D;
         int64_t so = bg0 * Npad + qt0 * BMQ;
         int qrem = N - qt0 * BMQ;                       // rows from the next step's first row to the head's end
+        int bq = qt0;                                   // (local) query block of the next step
         // statistics: chunk c < BMQ/4 of a stage holds LSE*log2e rows 4c.., the
         // rest -D rows; chunk c is loaded by wave c / kStatPerWave, so the first
         // half of the waves loads LSE rows and the second half -D rows
@@ -149,10 +152,11 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
             qo += BMQ * D;
             so += BMQ;
             qrem -= BMQ;
-            if (qrem <= 0) {                            // past the head's last block: the next head, block qt0
-                qo += ((int64_t)N - (nqt - qt0) * BMQ) * D;
-                so += Npad - (nqt - qt0) * BMQ;
+            if (LOCAL ? ++bq == qt1 : qrem <= 0) {     // past the head's last block: the next head, block qt0
+                qo += ((int64_t)N - (qt1 - qt0) * BMQ) * D;
+                so += Npad - (qt1 - qt0) * BMQ;
                 qrem = N - qt0 * BMQ;
+                if (LOCAL) bq = qt0;
             }
         };
         VT::load(Vg + (int64_t)k0 * D, N - k0, Vl, wave, lane);
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         int gb = qt0;
         const int nd = CAUSAL ? 32 * wave / BMQ : 0;
         auto gemm = [&](int i) __attribute__((always_inline)) {
-            if (++gb == nqt) gb = qt0;
+            if (++gb == qt1) gb = qt0;
             if (gb > qt0 && gb - qt0 < nd) return;
             init_dp(i);
             do_dvdk(i - 1);
@@ -265,12 +269,15 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
                 return;
             }
             const int q0 = xq * BMQ;
-            if (++xq == nqt) xq = qt0;
+            if (++xq == qt1) xq = qt0;
             const float* sl = (const float*)(smem + (i % NS) * Cfg::kStageBytes + 2 * QT::kBytes);
             // causal: key krow is hidden from query q0 + 32*qb + row(r) iff
             // delta > 8*(r/4) + r%4, delta = krow - q0 - 32*qb - 4*hh; steps whose
             // queries all follow this wave's keys skip the test (uniform branch)
             const bool need_mask = CAUSAL && kw + 31 > q0;
+            // local: query q0 + 32*qb + row(r) is past the window of key krow iff
+            // 8*(r/4) + r%4 + dw >= W, dw = q0 + 32*qb + 4*hh - krow
+            const bool need_wmask = LOCAL && q0 + BMQ - 1 >= kw + W;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -291,6 +298,12 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         if (delta > 8 * (r / 4) + r % 4) sacc[qb][r] = 0.f;
+                }
+                if (need_wmask) {
+                    const int dw = q0 + 32 * qb + 4 * hh - krow;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (dw + 8 * (r / 4) + r % 4 >= W) sacc[qb][r] = 0.f;
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dpacc[qb][r] = sacc[qb][r] * dpacc[qb][r];
@@ -428,11 +441,14 @@ __device__ __forceinline__ void sched_dq_phase() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, bool CAUSAL>
+// LOCAL (with CAUSAL): sliding window, key j visible to query i iff
+// i - W < j <= i; the key tiles of a query block start at the first one its
+// first row can see.
+template <int D, bool CAUSAL, bool LOCAL = false>
 __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
-    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int n_rows, int Npad, float c2, float scale) {
+    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int n_rows, int Npad, float c2, float scale, int W = 0) {
     using Cfg = QBf16Cfg<D>;
     using KT = typename Cfg::KT;
     constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BNK = Cfg::BNK, NS = Cfg::kStages, KB = BNK / 32;
@@ -466,17 +482,18 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
         const int qw = q0 + 32 * wave;
         const int qrow = qw + l32;
         const int kend = CAUSAL ? min(N, q0 + BM) : N;
-        const int ntiles = (kend + BNK - 1) / BNK;
-        const int ntw = qw >= N ? 0 : CAUSAL ? (min(N, qw + 32) + BNK - 1) / BNK : ntiles;
+        const int ts = LOCAL ? max(0, q0 - W + 1) / BNK : 0;   // first key tile (t is tile ts + t)
+        const int ntiles = (kend + BNK - 1) / BNK - ts;
+        const int ntw = qw >= N ? 0 : CAUSAL ? (min(N, qw + 32) + BNK - 1) / BNK - ts : ntiles;
 
         // direct loads of tile t; the per-lane offsets are recomputed at every
         // issue from an opaque copy of the lane index (kept live across the
         // loop they would take registers the products need)
         auto issue = [&](int t) __attribute__((always_inline)) {
             const uint32_t st = lds_addr(smem + (t % NS) * kStage);
-            const uint16_t* kb = Kg + (int64_t)t * BNK * D;
-            const uint16_t* vb = Vg + (int64_t)t * BNK * D;
-            const int rows_valid = N - t * BNK;
+            const uint16_t* kb = Kg + (int64_t)(t + ts) * BNK * D;
+            const uint16_t* vb = Vg + (int64_t)(t + ts) * BNK * D;
+            const int rows_valid = N - (t + ts) * BNK;
             int ln = lane;
             asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -566,12 +583,12 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
                 for (int kb = 0; kb < KB; ++kb) dsf[kb][0] = dsf[kb][1] = u32x4{};
                 return;
             }
-            const int k0 = t * BNK;
+            const int k0 = (t + ts) * BNK;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c2, -lse2));
-            if ((CAUSAL && k0 + BNK - 1 > qw) || (k0 + BNK > N)) {
+            if ((CAUSAL && k0 + BNK - 1 > qw) || (k0 + BNK > N) || (LOCAL && k0 < qw + 32 - W)) {
                 // row indices from an opaque copy of the lane half: hoisted
                 // out of the item loop, they and the masks derived from them
                 // would stay live in registers
@@ -582,7 +599,7 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = k0 + 32 * kb + acc_row(r, hm);
-                        if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r] = 0.f;
+                        if ((CAUSAL && key > qrow) || key >= N || (LOCAL && key <= qrow - W)) sacc[kb][r] = 0.f;
                     }
             }
 #pragma unroll
@@ -663,32 +680,35 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOCAL = false>
 static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* ws,
-                              void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
+                              void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, hipStream_t st,
+                              int W = 0) {
     using Cfg = KVBf16Cfg<D>;
     const int nkb = (N + Cfg::BNK - 1) / Cfg::BNK;
     const int Np = ws_rows(N);
     static std::atomic<int> slots{0};
-    const int grid = persistent_grid((const void*)bwd_dkdv_bf16_kernel<D, CAUSAL>, Cfg::kThreads, nkb * Hkv * B, slots);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
+    const int grid =
+        persistent_grid((const void*)bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL>, Cfg::kThreads, nkb * Hkv * B, slots);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
                        ws + (int64_t)B * Hq * Np, (uint16_t*)dk, (uint16_t*)dv, B, Hq, Hkv, N, Np, scale * kLog2e,
-                       scale);
+                       scale, W);
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOCAL = false>
 static hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dq,
-                            int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
+                            int B, int Hq, int Hkv, int N, float scale, hipStream_t st, int W = 0) {
     using Cfg = QBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
     const int Np = ws_rows(N);
     static std::atomic<int> slots{0};
-    const int grid = persistent_grid((const void*)bwd_dq_bf16_kernel<D, CAUSAL>, Cfg::kThreads, nmb * Hq * B, slots);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
+    const int grid =
+        persistent_grid((const void*)bwd_dq_bf16_kernel<D, CAUSAL, LOCAL>, Cfg::kThreads, nmb * Hq * B, slots);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, LOCAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
-                       ws + (int64_t)B * Hq * Np, (uint16_t*)dq, B, Hq, Hkv, N, Np, scale * kLog2e, scale);
+                       ws + (int64_t)B * Hq * Np, (uint16_t*)dq, B, Hq, Hkv, N, Np, scale * kLog2e, scale, W);
     return hipGetLastError();
 }
 
@@ -708,6 +728,22 @@ hipError_t launch_bwd_dq_bf16(int d, int causal, const void* q, const void* k, c
     if (d == 64) return causal ? launch_dq<64, true>(ARGS) : launch_dq<64, false>(ARGS);
     if (d == 128) return causal ? launch_dq<128, true>(ARGS) : launch_dq<128, false>(ARGS);
 #undef ARGS
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dkdv_bf16_local(int d, const void* q, const void* k, const void* v, const void* dO,
+                                      const float* ws, void* dk, void* dv, int B, int Hq, int Hkv, int N, int W,
+                                      float scale, hipStream_t st) {
+    if (d == 64) return launch_dkdv<64, true, true>(q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st, W);
+    if (d == 128) return launch_dkdv<128, true, true>(q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st, W);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_bf16_local(int d, const void* q, const void* k, const void* v, const void* dO,
+                                    const float* ws, void* dq, int B, int Hq, int Hkv, int N, int W, float scale,
+                                    hipStream_t st) {
+    if (d == 64) return launch_dq<64, true, true>(q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st, W);
+    if (d == 128) return launch_dq<128, true, true>(q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st, W);
     return hipErrorInvalidValue;
 }
 

@@ -17,7 +17,7 @@
 //    i), so K and V are read once per group, not once per query head;
 //  - the keys are cut into chunks; every wave takes one (batch, K/V head, row
 //    block, chunk) unit on its own, streams the chunk through a private
-//    two-stage LDS ring with direct global->LDS loads, and runs the forward
+//    four-stage LDS ring with direct global->LDS loads, and runs the forward
 //    pass's online softmax on it (S^T = K Q^T, P packed to bf16, O^T += V^T
 //    P^T with transposing LDS reads of V);
 //  - each unit writes its chunk's normalised O and log-sum-exp to a float32
@@ -32,10 +32,13 @@ namespace fa {
 
 template <int D>
 struct DecCfg {
-    static constexpr int kWaves = 4;                  // independent waves per workgroup (one per SIMD)
+    // Independent waves per workgroup: one workgroup fills the LDS (136 KiB),
+    // so these are the waves of a CU.  The cache read needs bytes in flight
+    // more than it needs waves: each wave keeps kStages - 1 tiles in flight.
+    static constexpr int kWaves = D == 128 ? 2 : 4;
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int BN = 32;                     // keys per tile
-    static constexpr int kStages = 2;
+    static constexpr int kStages = 4;
     using KT = LdsTile<BN, D, 1>;                     // one wave fills a whole tile
     static constexpr int kStage = 2 * KT::kElems;     // elements per stage (K then V)
     static constexpr float kTau = 8.0f;               // log2 slack before the running max is moved
@@ -48,7 +51,7 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     float c2) {
     using Cfg = DecCfg<D>;
     using KT = typename Cfg::KT;
-    constexpr int BN = Cfg::BN, kStage = Cfg::kStage, KP = KT::kPerWave;
+    constexpr int BN = Cfg::BN, kStage = Cfg::kStage, KP = KT::kPerWave, NS = Cfg::kStages;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[Cfg::kWaves * Cfg::kStages * kStage];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -71,14 +74,16 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     uint16_t* ring = smem + wave * Cfg::kStages * kStage;
     const uint16_t* Kg = K + ((int64_t)b * Hkv + g) * Nk * D;
     const uint16_t* Vg = V + ((int64_t)b * Hkv + g) * Nk * D;
-    // K and V rows of tile t into stage t % 2 (rows past the chunk re-read its last row)
+    // K and V rows of tile t into stage t % NS (rows past the chunk re-read its last row)
     auto issue = [&](int t) __attribute__((always_inline)) {
-        const uint16_t* st = ring + (t & 1) * kStage;
+        const uint16_t* st = ring + (t % NS) * kStage;
         const int k0 = kbeg + t * BN;
         KT::load(Kg + (int64_t)k0 * D, kend - k0, st, 0, lane);
         KT::load(Vg + (int64_t)k0 * D, kend - k0, st + KT::kElems, 0, lane);
     };
-    issue(0);
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+        if (t < nt) issue(t);
     u32x4 qf[D / 16];                                 // this lane's query row as B operands
     {
         const uint16_t* qp = Q + (((int64_t)b * Hq + hq) * Nq + qi) * D + 8 * hh;
@@ -98,16 +103,12 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
     float m = kNegBig, lsum = 0.f;
     for (int t = 0; t < nt; ++t) {
-        // tile t has landed once at most the next tile's loads are outstanding;
-        // the next tile's stage held tile t-1, whose reads all fed products of
-        // the previous iteration
-        if (t + 1 < nt) {
-            issue(t + 1);
-            wait_vm<2 * KP>();
-        } else {
-            wait_vm<0>();
-        }
-        const uint16_t* Ks = ring + (t & 1) * kStage;
+        // tile t + NS - 1 goes into the stage of tile t - 1, whose reads all
+        // fed products of the previous iteration; tile t has landed once at
+        // most the loads of the tiles issued after it are outstanding
+        if (t + NS - 1 < nt) issue(t + NS - 1);
+        wait_vm_dyn<2 * KP, NS - 1>(min(NS - 1, nt - 1 - t));
+        const uint16_t* Ks = ring + (t % NS) * kStage;
         const uint16_t* Vs = Ks + KT::kElems;
         // S^T = K_t Q^T: rows = 32 keys, columns = the packed query rows
         f32x16 sacc = zero16();

@@ -63,6 +63,17 @@ hipError_t launch_bwd_dkdv_bf16(int d, int causal, const void* q, const void* k,
 hipError_t launch_bwd_dq_bf16(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
                               const float* ws, void* dq, int B, int Hq, int Hkv, int N, float scale, hipStream_t st);
 
+// Causal sliding-window (local) attention, bf16: key j visible to query i iff
+// i - W < j <= i.
+hipError_t launch_fwd_bf16_local(int d, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                 int Hq, int Hkv, int N, int W, float scale, hipStream_t st);
+hipError_t launch_bwd_dkdv_bf16_local(int d, const void* q, const void* k, const void* v, const void* dO,
+                                      const float* ws, void* dk, void* dv, int B, int Hq, int Hkv, int N, int W,
+                                      float scale, hipStream_t st);
+hipError_t launch_bwd_dq_bf16_local(int d, const void* q, const void* k, const void* v, const void* dO,
+                                    const float* ws, void* dq, int B, int Hq, int Hkv, int N, int W, float scale,
+                                    hipStream_t st);
+
 hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
 
 // Decode split over the keys: nrb blocks of 32 packed query rows per K/V head,

@@ -43,6 +43,10 @@ _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_quantize_fp8.argtypes = [_p, ctypes.c_size_t, _p, _p, _p]
 _lib.fa_quantize_fp8.restype = _i
+_lib.fa_fwd_local.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
+_lib.fa_fwd_local.restype = _i
+_lib.fa_bwd_local.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
+_lib.fa_bwd_local.restype = _i
 _lib.fa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_decode.restype = _i
 _lib.fa_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
@@ -53,7 +57,8 @@ _lib.fa_abi_version.argtypes = []
 _lib.fa_abi_version.restype = _i
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
-           "fa_quantize_fp8", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string", "fa_abi_version")
+           "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_decode", "fa_decode_workspace_bytes",
+           "fa_status_string", "fa_abi_version")
 
 
 class FAError(RuntimeError):
@@ -95,6 +100,16 @@ def fa_bwd_workspace_bytes(B, Hq, N) -> int:
 
 def fa_quantize_fp8(x_bf16, n, x_e4m3, descale, stream) -> int:
     return _lib.fa_quantize_fp8(x_bf16, n, x_e4m3, descale, stream)
+
+
+def fa_fwd_local(q, k, v, o, lse, B, Hq, Hkv, N, d, window, softmax_scale, dtype, stream) -> int:
+    return _lib.fa_fwd_local(q, k, v, o, lse, B, Hq, Hkv, N, d, window, float(softmax_scale), dtype, stream)
+
+
+def fa_bwd_local(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, window, softmax_scale, dtype,
+                 stream) -> int:
+    return _lib.fa_bwd_local(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, window,
+                             float(softmax_scale), dtype, stream)
 
 
 def fa_decode(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, d, causal, softmax_scale, dtype, stream) -> int:
@@ -185,6 +200,30 @@ def bwd(q, k, v, o, do, lse, causal: bool, scale: float, stream=None, workspace=
     _check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, d, causal,
                   scale, code, _stream_handle(stream)), "fa_bwd")
+    return dq, dk, dv, workspace
+
+
+def fwd_local(q, k, v, window: int, scale: float, stream=None):
+    """(o, lse) of causal sliding-window attention (key j visible to query i iff i - window < j <= i), bf16."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
+                        window, scale, _dtype_code(q), _stream_handle(stream)), "fa_fwd_local")
+    return o, lse
+
+
+def bwd_local(q, k, v, o, do, lse, window: int, scale: float, stream=None, workspace=None):
+    """(dq, dk, dv, workspace) of causal sliding-window attention."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_bytes(B, Hq, N) // 4, dtype=torch.float32, device=q.device)
+    _check(fa_bwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, d, window,
+                        scale, _dtype_code(q), _stream_handle(stream)), "fa_bwd_local")
     return dq, dk, dv, workspace
 
 

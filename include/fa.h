@@ -165,6 +165,30 @@ fa_status_t fa_quantize_fp8(const void* x_bf16, size_t n, void* x_e4m3,
                             float* descale, hipStream_t stream);
 
 /*
+ * Causal sliding-window (local) attention: key j is visible to query i iff
+ * i - window < j <= i.  The FlashAttention legal glossary, entry
+ * "Block-sparse": a sparsity mask picks the blocks of the attention matrix
+ * worth computing, sliding-window (local) attention being a common pattern,
+ * and whole tiles outside it are skipped.  Same arguments, layouts and
+ * outputs as fa_fwd / fa_bwd with causal = 1, plus `window` (>= 1; a window
+ * of N or more is plain causal attention); bf16 only.  The backward reads
+ * the LSE of fa_fwd_local with the same window.
+ */
+fa_status_t fa_fwd_local(const void* q, const void* k, const void* v,
+                         void* o, float* lse,
+                         int B, int Hq, int Hkv, int N, int d,
+                         int window, float softmax_scale, int dtype,
+                         hipStream_t stream);
+
+fa_status_t fa_bwd_local(const void* q, const void* k, const void* v,
+                         const void* o, const void* dO, const float* lse,
+                         void* dq, void* dk, void* dv,
+                         float* delta_ws,
+                         int B, int Hq, int Hkv, int N, int d,
+                         int window, float softmax_scale, int dtype,
+                         hipStream_t stream);
+
+/*
  * Decode: attention of Nq new query rows against a key/value cache of Nk
  * rows.  "Paper digest: FlashAttention", section "Limits" (decode-time
  * attention reads a large KV cache for few queries); self-hosted LLM

@@ -29,7 +29,8 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(fa.LIB_PATH)
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
-                          "fa_bwd_workspace_bytes", "fa_quantize_fp8", "fa_decode", "fa_decode_workspace_bytes",
+                          "fa_bwd_workspace_bytes", "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_decode",
+                          "fa_decode_workspace_bytes",
                           "fa_status_string", "fa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -178,3 +179,23 @@ def test_decode_empty_and_workspace():
     assert fa.fa_decode_workspace_bytes(0, 8, 2, 1, 100, 128) == 0
     assert fa.fa_decode_workspace_bytes(1, 8, 2, 1, 0, 128) == 0
     assert fa.fa_decode_workspace_bytes(1, 8, 2, 1, 100, 96) == 0
+
+
+def test_local_validation():
+    from exact_io_aware_50_amd import fa
+    f = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, Hq=2, Hkv=2, N=256, d=128, window=64,
+             softmax_scale=0.1, dtype=1, stream=None)
+    assert fa.fa_fwd_local(**{**f, "window": 0}) == 3
+    assert fa.fa_fwd_local(**{**f, "dtype": 0}) == 3
+    assert fa.fa_fwd_local(**{**f, "d": 32}) == 3
+    assert fa.fa_fwd_local(**{**f, "q": None}) == 1
+    assert fa.fa_fwd_local(**{**f, "o": A[0]}) == 6
+    assert fa.fa_fwd_local(**{**f, "lse": A[4] + 2}) == 4
+    assert fa.fa_fwd_local(**{**f, "N": 0}) == 0
+    bw = dict(q=A[0], k=A[1], v=A[2], o=A[3], dO=A[4], lse=A[5], dq=A[6], dk=A[7], dv=A[8], delta_ws=A[9],
+              B=1, Hq=2, Hkv=2, N=256, d=128, window=64, softmax_scale=0.1, dtype=1, stream=None)
+    assert fa.fa_bwd_local(**{**bw, "window": -1}) == 3
+    assert fa.fa_bwd_local(**{**bw, "delta_ws": None}) == 1
+    assert fa.fa_bwd_local(**{**bw, "dk": A[8]}) == 6
+    assert fa.fa_bwd_local(**{**bw, "Hq": 3}) == 2
+    assert fa.fa_bwd_local(**{**bw, "B": 0}) == 0
