@@ -89,6 +89,64 @@ def stored_traffic(kernel, workload):
     return float(rec["bytes_per_launch"])
 
 
+def local_pairs(N, W):
+    """Visible (query, key) pairs of causal sliding-window attention: row i sees min(i + 1, W) keys."""
+    W = min(W, N)
+    return W * (W + 1) // 2 + (N - W) * W
+
+
+def local_leg(torch, fa, I, dev, stream, args):
+    """fa_fwd_local and fa_bwd_local on the local workload, HIP events on the launch stream.
+
+    Credited flops: 4 d per visible (query, key) pair and query head forward, 2.5x that backward."""
+    w, W = I.LOCAL_WORKLOADS[args.local_workload]
+    q, k, v, do = (I.full_tensor(w, t).to(dev) for t in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.N) // 4, dtype=torch.float32, device=dev)
+    sh = stream.cuda_stream
+    code = fa.FA_DTYPE_BF16
+
+    def fwd():
+        st = fa.fa_fwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq,
+                             w.Hkv, w.N, w.d, W, w.scale, code, sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_fwd_local")
+
+    def bwd():
+        st = fa.fa_bwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d,
+                             W, w.scale, code, sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_bwd_local")
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tf = tb = 0.0
+    for _ in range(args.steps):
+        ev[0].record(stream)
+        fwd()
+        ev[1].record(stream)
+        bwd()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        tf += ev[0].elapsed_time(ev[1])
+        tb += ev[1].elapsed_time(ev[2])
+    tf /= args.steps
+    tb /= args.steps
+    fl = 4.0 * w.B * w.Hq * w.d * local_pairs(w.N, W)
+    fwd_tf = fl / (tf * 1e-3) / 1e12
+    fb_tf = 3.5 * fl / ((tf + tb) * 1e-3) / 1e12
+    return {"workload": args.local_workload, "window": W, "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4),
+            "fwd_bwd_ms": round(tf + tb, 4), "fwd_tflops": round(fwd_tf, 1),
+            "fwd_frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4), "fwd_bwd_tflops": round(fb_tf, 1),
+            "fwd_bwd_frac_peak": round(fb_tf / PEAK_BF16_TFLOPS, 4),
+            "note": "causal sliding window; credited 4 d flops per visible pair forward, 2.5x backward"}
+
+
 def decode_bytes(dw):
     """Bytes a decode step must move: the K and V cache once, Q in, O and LSE out."""
     return 2 * dw.B * dw.Hkv * dw.Nk * dw.d * 2 + 2 * dw.B * dw.Hq * dw.Nq * dw.d * 2 + 4 * dw.B * dw.Hq * dw.Nq
@@ -209,6 +267,8 @@ def main():
     ap.add_argument("--no-gemm-reference", action="store_true",
                     help="skip the vendor bf16 GEMM timed for context (practical MFMA rate on this data)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode (KV cache) leg")
+    ap.add_argument("--no-local", action="store_true", help="skip the sliding-window (local) attention leg")
+    ap.add_argument("--local-workload", default="local_bf16_n65536_w4096")
     ap.add_argument("--decode-workload", default="decode_gqa_bf16_n16384")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (calibrates HBM byte counters)")
@@ -345,6 +405,12 @@ def main():
                              "frac_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
                              "note": "E4M3 forward of the same shape, inputs quantised per tensor outside the timing"}
         log(f"fp8 forward {t8:.3f} ms ({tf8:.0f} TFLOP/s)")
+
+    if not args.no_local:
+        result["local"] = local_leg(torch, fa, I, dev, stream, args)
+        log("local {}: fwd {} ms ({} TFLOP/s), fwd+bwd {} ms ({} TFLOP/s)".format(
+            result["local"]["workload"], result["local"]["fwd_ms"], result["local"]["fwd_tflops"],
+            result["local"]["fwd_bwd_ms"], result["local"]["fwd_bwd_tflops"]))
 
     if not args.no_decode:
         result["decode"] = decode_leg(torch, fa, I, dev, stream, args)

@@ -82,6 +82,13 @@ DECODE_WORKLOADS = {
 }
 
 
+# Sliding-window (local) attention at the 64K-token shape: a 4096-key causal
+# window, inputs as the long-context workload (Q, K with sigma 3).
+LOCAL_WORKLOADS = {
+    "local_bf16_n65536_w4096": (WORKLOADS["long_bf16_n65536"], 4096),
+}
+
+
 def decode_tensor(w: DecodeWorkload, tensor_id: int, device="cpu"):
     """Q ([B, Hq, Nq, d]) or the K / V cache ([B, Hkv, Nk, d]) of a decode workload, bf16."""
     import torch
