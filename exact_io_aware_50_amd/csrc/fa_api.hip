@@ -193,7 +193,7 @@ static fa_status_t check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, i
     if (Hkv == 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
     // every query row must see at least one key
     if (Nk == 0 || (causal && Nq > Nk)) return FA_ERR_SHAPE;
-    const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk);
+    const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d);
     const int64_t units = (int64_t)B * Hkv * p.nrb * p.nsplit;
     const int64_t rows = (int64_t)B * Hq * Nq;
     if (units / 4 + 1 > INT32_MAX || rows / 4 + 1 > INT32_MAX) return FA_ERR_SHAPE;
@@ -203,7 +203,7 @@ static fa_status_t check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, i
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     bool empty = false;
     if (check_decode(B, Hq, Hkv, Nq, Nk, d, 0, 1.0f, &empty) != FA_OK || empty) return 0;
-    return fa::decode_ws_bytes(fa::decode_plan(B, Hq, Hkv, Nq, Nk), B, Hq, Nq, d);
+    return fa::decode_ws_bytes(fa::decode_plan(B, Hq, Hkv, Nq, Nk, d), B, Hq, Nq, d);
 }
 
 fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int B, int Hq,

@@ -193,6 +193,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     float acc[PER], wsum = 0.f;
 #pragma unroll
     for (int p = 0; p < PER; ++p) acc[p] = 0.f;
+#pragma unroll 4
     for (int s = 0; s < nsplit; ++s) {
         const float ls = wl[s];
         const float w = ls == -INFINITY ? 0.f : fast_exp2((ls - L) * kLog2e);
@@ -211,13 +212,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     if (lane == 0) LSE[row] = L + logf(wsum);
 }
 
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk) {
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     DecodePlan p;
     const int G = Hq / Hkv;
     p.nrb = (G * Nq + 31) / 32;
     const int64_t base = (int64_t)B * Hkv * p.nrb;
-    // about 2048 wave units (eight per CU), chunks of at least 256 keys
-    const int64_t want = (2048 + base - 1) / base;
+    // one wave unit per resident wave of the 256 CUs (each unit streams its
+    // chunk with its own ring, so fewer, longer units pay the ring's start-up
+    // latency less often), chunks of at least 256 keys
+    const int64_t slots = 256 * (d == 128 ? DecCfg<128>::kWaves : DecCfg<64>::kWaves);
+    const int64_t want = (slots + base - 1) / base;
     const int64_t most = ((int64_t)Nk + 255) / 256;
     int64_t ns = want < most ? want : most;
     if (ns < 1) ns = 1;
@@ -232,7 +236,7 @@ template <int D, bool CAUSAL>
 static hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int B,
                          int Hq, int Hkv, int Nq, int Nk, float scale, hipStream_t st) {
     using Cfg = DecCfg<D>;
-    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk);
+    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk, D);
     const int64_t rows = (int64_t)B * Hq * Nq;
     float* wo = ws;
     float* wl = ws + rows * p.nsplit * D;

@@ -81,7 +81,7 @@ hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descal
 struct DecodePlan {
     int nrb, nsplit, chunk;
 };
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk);
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
 // Workspace of fa_decode: float32 O per (row, chunk) [rows][nsplit][d], then
 // the chunk LSEs [rows][nsplit], rows = B * Hq * Nq.
