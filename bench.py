@@ -180,9 +180,49 @@ def decode_leg(torch, fa, I, dev, stream, args):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     gbs = decode_bytes(dw) / (ms * 1e-3) / 1e9
-    return {"workload": args.decode_workload, "ms": round(ms, 4), "bytes": decode_bytes(dw),
-            "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bound": "hbm",
-            "note": "fa_decode: split kernel plus merge; bytes = K and V cache once + Q + O + LSE"}
+    res = {"workload": args.decode_workload, "ms": round(ms, 4), "bytes": decode_bytes(dw),
+           "gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bound": "hbm",
+           "note": "fa_decode: split kernel plus merge; bytes = K and V cache once + Q + O + LSE"}
+
+    # the same cache as a pool of 256-key blocks in shuffled order, with
+    # per-sequence lengths drawn from [Nk/4, Nk] (a batch of mixed lengths)
+    bs = 256
+    maxb = dw.Nk // bs
+    g = torch.Generator().manual_seed(dw.seed)
+    perm = torch.randperm(dw.B * maxb, generator=g)
+    lens = torch.randint(dw.Nk // 4, dw.Nk + 1, (dw.B,), generator=g, dtype=torch.int32)
+    blk = lambda t: t.view(dw.B, dw.Hkv, maxb, bs, dw.d).permute(0, 2, 1, 3, 4).reshape(dw.B * maxb, dw.Hkv, bs, dw.d)
+    kc, vc = torch.empty_like(blk(k)), torch.empty_like(blk(v))
+    pd = perm.to(dev)
+    kc[pd] = blk(k)
+    vc[pd] = blk(v)
+    del k, v
+    table = perm.view(dw.B, maxb).to(torch.int32).to(dev)
+    ld = lens.to(dev)
+    ws2 = torch.empty(fa.fa_decode_paged_workspace_bytes(dw.B, dw.Hq, dw.Hkv, dw.Nq, maxb, bs, dw.d) // 4,
+                      dtype=torch.float32, device=dev)
+
+    def run_paged():
+        st = fa.fa_decode_paged(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), table.data_ptr(), ld.data_ptr(),
+                                o.data_ptr(), lse.data_ptr(), ws2.data_ptr(), dw.B, dw.Hq, dw.Hkv, dw.Nq, maxb, bs,
+                                dw.B * maxb, dw.d, dw.causal, dw.scale, fa.FA_DTYPE_BF16, sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_decode_paged")
+
+    for _ in range(args.warmup):
+        run_paged()
+    e0.record(stream)
+    for _ in range(args.steps):
+        run_paged()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    msp = e0.elapsed_time(e1) / args.steps
+    pbytes = 2 * dw.Hkv * dw.d * 2 * int(lens.sum()) + 2 * dw.B * dw.Hq * dw.Nq * dw.d * 2 + 4 * dw.B * dw.Hq * dw.Nq
+    res["paged"] = {"ms": round(msp, 4), "block_size": bs, "lens_min": int(lens.min()), "lens_max": int(lens.max()),
+                    "bytes": pbytes, "gbs": round(pbytes / (msp * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(pbytes / (msp * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "note": "fa_decode_paged: shuffled 256-key blocks, per-sequence lengths in [Nk/4, Nk]"}
+    return res
 
 
 def cpu_baseline(w, seconds):

@@ -193,7 +193,7 @@ static fa_status_t check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, i
     if (Hkv == 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
     // every query row must see at least one key
     if (Nk == 0 || (causal && Nq > Nk)) return FA_ERR_SHAPE;
-    const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d);
+    const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d, fa::kPagedUnitsPerSlot);
     const int64_t units = (int64_t)B * Hkv * p.nrb * p.nsplit;
     const int64_t rows = (int64_t)B * Hq * Nq;
     if (units / 4 + 1 > INT32_MAX || rows / 4 + 1 > INT32_MAX) return FA_ERR_SHAPE;
@@ -203,7 +203,7 @@ static fa_status_t check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, i
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     bool empty = false;
     if (check_decode(B, Hq, Hkv, Nq, Nk, d, 0, 1.0f, &empty) != FA_OK || empty) return 0;
-    return fa::decode_ws_bytes(fa::decode_plan(B, Hq, Hkv, Nq, Nk, d), B, Hq, Nq, d);
+    return fa::decode_ws_bytes(fa::decode_plan(B, Hq, Hkv, Nq, Nk, d, 1), B, Hq, Nq, d);
 }
 
 fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int B, int Hq,
@@ -217,6 +217,42 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, floa
     if (s != FA_OK) return s;
     return launch_status(fa::launch_decode(d, causal, q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, softmax_scale,
                                            stream));
+}
+
+// Paged decode: the host checks the pool and table shapes; the sequence
+// lengths and block ids live on the device and are clamped by the kernel.
+static fa_status_t check_paged(int B, int Hq, int Hkv, int Nq, int maxb, int bs, int nblk, int d, int causal,
+                               float scale, bool* empty) {
+    if (maxb < 0 || bs < 0 || nblk < 0) return FA_ERR_SHAPE;
+    if (bs == 0 || bs % 32 != 0) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)maxb * bs > INT32_MAX / 2) return FA_ERR_SHAPE;
+    fa_status_t s = check_decode(B, Hq, Hkv, Nq, maxb * bs, d, 0, scale, empty);
+    if (s != FA_OK || *empty) return s;
+    if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+    if (nblk == 0) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int Nq, int max_blocks, int block_size, int d) {
+    bool empty = false;
+    if (check_paged(B, Hq, Hkv, Nq, max_blocks, block_size, 1, d, 0, 1.0f, &empty) != FA_OK || empty) return 0;
+    const int Nk = max_blocks * block_size;
+    return fa::decode_ws_bytes(fa::decode_plan(B, Hq, Hkv, Nq, Nk, d, fa::kPagedUnitsPerSlot), B, Hq, Nq, d);
+}
+
+fa_status_t fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                            const int* seq_lens, void* o, float* lse, float* ws, int B, int Hq, int Hkv, int Nq,
+                            int max_blocks, int block_size, int num_blocks, int d, int causal, float softmax_scale,
+                            int dtype, hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_paged(B, Hq, Hkv, Nq, max_blocks, block_size, num_blocks, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    s = check_ptrs({q, k_cache, v_cache}, {block_table, seq_lens}, {o, ws}, {lse});
+    if (s != FA_OK) return s;
+    return launch_status(fa::launch_decode_paged(d, causal, q, k_cache, v_cache, block_table, seq_lens, o, lse, ws,
+                                                 B, Hq, Hkv, Nq, max_blocks, block_size, num_blocks, softmax_scale,
+                                                 stream));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N) {

@@ -44,11 +44,19 @@ struct DecCfg {
     static constexpr float kTau = 8.0f;               // log2 slack before the running max is moved
 };
 
-template <int D, bool CAUSAL>
+// PAGED: the cache is a pool of blocks [nblk][Hkv][bs][D] and sequence b's
+// key j sits in block table[b][j / bs], row j % bs; sequence b has lens[b]
+// keys (the self-hosted LLM glossary, entry "PagedAttention": the KV cache in
+// fixed-size, non-contiguous blocks; the digest's "Limits": batch-varying
+// lengths at decode time).  bs is a multiple of the 32-key tile, so a tile
+// never straddles two blocks.  Lengths are clamped to [0, maxb * bs] and
+// block ids to [0, nblk): a bad table reads wrong rows, never outside the pool.
+template <int D, bool CAUSAL, bool PAGED = false>
 __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     float* __restrict__ Wo, float* __restrict__ Wl, int B, int Hq, int Hkv, int Nq, int Nk, int chunk, int nsplit,
-    float c2) {
+    float c2, const int* __restrict__ table = nullptr, const int* __restrict__ lens = nullptr, int maxb = 0,
+    int bs = 0, int nblk = 0) {
     using Cfg = DecCfg<D>;
     using KT = typename Cfg::KT;
     constexpr int BN = Cfg::BN, kStage = Cfg::kStage, KP = KT::kPerWave, NS = Cfg::kStages;
@@ -67,9 +75,10 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     const int r = rb * 32 + l32;                      // this lane's packed query row
     const bool rv = r < R;
     const int hq = g * G + (rv ? r / Nq : 0), qi = rv ? r % Nq : 0;
-    const int lim = CAUSAL ? Nk - Nq + qi : Nk - 1;   // last key the row sees
-    const int kbeg = s * chunk, kend = min(Nk, kbeg + chunk);
-    const int nt = (kend - kbeg + BN - 1) / BN;
+    const int Nb = PAGED ? min(max(lens[b], 0), maxb * bs) : Nk;   // this sequence's keys
+    const int lim = CAUSAL ? Nb - Nq + qi : Nb - 1;   // last key the row sees
+    const int kbeg = s * chunk, kend = min(Nb, kbeg + chunk);
+    const int nt = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
 
     uint16_t* ring = smem + wave * Cfg::kStages * kStage;
     const uint16_t* Kg = K + ((int64_t)b * Hkv + g) * Nk * D;
@@ -78,8 +87,15 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     auto issue = [&](int t) __attribute__((always_inline)) {
         const uint16_t* st = ring + (t % NS) * kStage;
         const int k0 = kbeg + t * BN;
-        KT::load(Kg + (int64_t)k0 * D, kend - k0, st, 0, lane);
-        KT::load(Vg + (int64_t)k0 * D, kend - k0, st + KT::kElems, 0, lane);
+        const uint16_t *ks = Kg + (int64_t)k0 * D, *vs = Vg + (int64_t)k0 * D;
+        if constexpr (PAGED) {
+            const int blk = min(max(table[(int64_t)b * maxb + k0 / bs], 0), nblk - 1);
+            const int64_t off = (((int64_t)blk * Hkv + g) * bs + k0 % bs) * D;
+            ks = K + off;
+            vs = V + off;
+        }
+        KT::load(ks, kend - k0, st, 0, lane);
+        KT::load(vs, kend - k0, st + KT::kElems, 0, lane);
     };
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t)
@@ -115,7 +131,7 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) sacc = mma_bf16(KT::row8(Ks, l32, 2 * j + hh), qf[j], sacc);
         const int k0 = kbeg + t * BN;
-        if (k0 + BN > kend || (CAUSAL && k0 + BN - 1 > Nk - Nq)) {
+        if (k0 + BN > kend || (CAUSAL && k0 + BN - 1 > Nb - Nq)) {
 #pragma unroll
             for (int r2 = 0; r2 < 16; ++r2) {
                 const int key = k0 + acc_row(r2, hh);
@@ -202,25 +218,27 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 #pragma unroll
         for (int p = 0; p < PER; ++p) acc[p] = fmaf(w, wo[p], acc[p]);
     }
-    const float inv = 1.0f / wsum;
+    // a row that sees no key at all (paged: an empty sequence, or a causal
+    // row before its sequence's first key) gets O = 0 and LSE = -inf
+    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
     uint16_t* orow = O + row * D + lane * PER;
     if constexpr (PER == 2) {
         *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
     } else {
         orow[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
     }
-    if (lane == 0) LSE[row] = L + logf(wsum);
+    if (lane == 0) LSE[row] = wsum > 0.f ? L + logf(wsum) : -INFINITY;
 }
 
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int per_slot) {
     DecodePlan p;
     const int G = Hq / Hkv;
     p.nrb = (G * Nq + 31) / 32;
     const int64_t base = (int64_t)B * Hkv * p.nrb;
-    // one wave unit per resident wave of the 256 CUs (each unit streams its
-    // chunk with its own ring, so fewer, longer units pay the ring's start-up
-    // latency less often), chunks of at least 256 keys
-    const int64_t slots = 256 * (d == 128 ? DecCfg<128>::kWaves : DecCfg<64>::kWaves);
+    // per_slot wave units per resident wave of the 256 CUs (each unit streams
+    // its chunk with its own ring, so fewer, longer units pay the ring's
+    // start-up latency less often); chunks of at least 256 keys
+    const int64_t slots = (int64_t)per_slot * 256 * (d == 128 ? DecCfg<128>::kWaves : DecCfg<64>::kWaves);
     const int64_t want = (slots + base - 1) / base;
     const int64_t most = ((int64_t)Nk + 255) / 256;
     int64_t ns = want < most ? want : most;
@@ -232,19 +250,20 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     return p;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED = false>
 static hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int B,
-                         int Hq, int Hkv, int Nq, int Nk, float scale, hipStream_t st) {
+                         int Hq, int Hkv, int Nq, int Nk, float scale, hipStream_t st, const int* table = nullptr,
+                         const int* lens = nullptr, int maxb = 0, int bs = 0, int nblk = 0) {
     using Cfg = DecCfg<D>;
-    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk, D);
+    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk, D, PAGED ? kPagedUnitsPerSlot : 1);
     const int64_t rows = (int64_t)B * Hq * Nq;
     float* wo = ws;
     float* wl = ws + rows * p.nsplit * D;
     const int64_t units = (int64_t)B * Hkv * p.nrb * p.nsplit;
     const unsigned g1 = (unsigned)((units + Cfg::kWaves - 1) / Cfg::kWaves);
-    hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL>), dim3(g1), dim3(Cfg::kThreads), 0, st, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, wo, wl, B, Hq, Hkv, Nq, Nk, p.chunk, p.nsplit,
-                       scale * kLog2e);
+    hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, PAGED>), dim3(g1), dim3(Cfg::kThreads), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wo, wl, B, Hq, Hkv, Nq, Nk, p.chunk,
+                       p.nsplit, scale * kLog2e, table, lens, maxb, bs, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, wo, wl,
@@ -258,6 +277,17 @@ hipError_t launch_decode(int d, int causal, const void* q, const void* k, const 
                                : launch<64, false>(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, scale, st);
     if (d == 128) return causal ? launch<128, true>(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, scale, st)
                                 : launch<128, false>(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, scale, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_paged(int d, int causal, const void* q, const void* kc, const void* vc, const int* table,
+                               const int* lens, void* o, float* lse, float* ws, int B, int Hq, int Hkv, int Nq,
+                               int maxb, int bs, int nblk, float scale, hipStream_t st) {
+    const int Nk = maxb * bs;                         // the longest a sequence can be
+#define PARGS q, kc, vc, o, lse, ws, B, Hq, Hkv, Nq, Nk, scale, st, table, lens, maxb, bs, nblk
+    if (d == 64) return causal ? launch<64, true, true>(PARGS) : launch<64, false, true>(PARGS);
+    if (d == 128) return causal ? launch<128, true, true>(PARGS) : launch<128, false, true>(PARGS);
+#undef PARGS
     return hipErrorInvalidValue;
 }
 

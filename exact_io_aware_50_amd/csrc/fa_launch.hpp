@@ -81,13 +81,24 @@ hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descal
 struct DecodePlan {
     int nrb, nsplit, chunk;
 };
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int per_slot);
+// wave units per resident wave for the paged cache.  Its lengths vary, but
+// four units per wave (finer chunks, so that slots freed by short sequences
+// take more work) measured slower than one on the 16-sequence 16K workload
+// with lengths in [4K, 16K]: 0.162 against 0.144 ms, the extra unit start-ups
+// costing more than the better balance gains.
+constexpr int kPagedUnitsPerSlot = 1;
 
 // Workspace of fa_decode: float32 O per (row, chunk) [rows][nsplit][d], then
 // the chunk LSEs [rows][nsplit], rows = B * Hq * Nq.
 inline size_t decode_ws_bytes(const DecodePlan& p, int B, int Hq, int Nq, int d) {
     return (size_t)4 * (size_t)B * (size_t)Hq * (size_t)Nq * (size_t)p.nsplit * (size_t)(d + 1);
 }
+
+// Paged cache [nblk][Hkv][bs][d], block table [B][maxb], lengths [B] (device).
+hipError_t launch_decode_paged(int d, int causal, const void* q, const void* kc, const void* vc, const int* table,
+                               const int* lens, void* o, float* lse, float* ws, int B, int Hq, int Hkv, int Nq,
+                               int maxb, int bs, int nblk, float scale, hipStream_t st);
 
 hipError_t launch_decode(int d, int causal, const void* q, const void* k, const void* v, void* o, float* lse,
                          float* ws, int B, int Hq, int Hkv, int Nq, int Nk, float scale, hipStream_t st);

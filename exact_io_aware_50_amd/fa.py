@@ -51,6 +51,10 @@ _lib.fa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _
 _lib.fa_decode.restype = _i
 _lib.fa_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.fa_decode_paged.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p] + [_i] * 9 + [_f, _i, _p]
+_lib.fa_decode_paged.restype = _i
+_lib.fa_decode_paged_workspace_bytes.argtypes = [_i] * 7
+_lib.fa_decode_paged_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_status_string.argtypes = [_i]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_abi_version.argtypes = []
@@ -58,7 +62,7 @@ _lib.fa_abi_version.restype = _i
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
            "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_decode", "fa_decode_workspace_bytes",
-           "fa_status_string", "fa_abi_version")
+           "fa_decode_paged", "fa_decode_paged_workspace_bytes", "fa_status_string", "fa_abi_version")
 
 
 class FAError(RuntimeError):
@@ -119,6 +123,16 @@ def fa_decode(q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, d, causal, softmax_scale,
 
 def fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d) -> int:
     return int(_lib.fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d))
+
+
+def fa_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, ws, B, Hq, Hkv, Nq, max_blocks, block_size,
+                    num_blocks, d, causal, softmax_scale, dtype, stream) -> int:
+    return _lib.fa_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, ws, B, Hq, Hkv, Nq, max_blocks,
+                                block_size, num_blocks, d, int(causal), float(softmax_scale), dtype, stream)
+
+
+def fa_decode_paged_workspace_bytes(B, Hq, Hkv, Nq, max_blocks, block_size, d) -> int:
+    return int(_lib.fa_decode_paged_workspace_bytes(B, Hq, Hkv, Nq, max_blocks, block_size, d))
 
 
 def fa_status_string(status: int) -> str:
@@ -247,6 +261,29 @@ def decode(q, k, v, causal: bool, scale: float, stream=None, workspace=None):
         workspace = torch.empty(max(n, 4), dtype=torch.float32, device=q.device)
     _check(fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
                      B, Hq, Hkv, Nq, Nk, d, causal, scale, code, _stream_handle(stream)), "fa_decode")
+    return o, lse
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, causal: bool, scale: float, stream=None, workspace=None):
+    """(o, lse) for q [B,Hq,Nq,d] against a paged bf16 cache [num_blocks,Hkv,block_size,d].
+
+    block_table: int32 [B, max_blocks]; seq_lens: int32 [B] (both on the device)."""
+    torch = _torch()
+    B, Hq, Nq, d = q.shape
+    nblk, Hkv, bs = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    maxb = block_table.shape[1]
+    for t in (block_table, seq_lens):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("block_table and seq_lens must be contiguous int32 tensors")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = fa_decode_paged_workspace_bytes(B, Hq, Hkv, Nq, maxb, bs, d) // 4
+        workspace = torch.empty(max(n, 4), dtype=torch.float32, device=q.device)
+    _check(fa_decode_paged(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                           seq_lens.data_ptr(), o.data_ptr(), lse.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, Nq,
+                           maxb, bs, nblk, d, causal, scale, _dtype_code(q), _stream_handle(stream)),
+           "fa_decode_paged")
     return o, lse
 
 

@@ -222,6 +222,37 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v,
  */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
+/*
+ * Decode against a paged KV cache with per-sequence lengths.  Self-hosted LLM
+ * glossary, entry "PagedAttention" (the KV cache split into fixed-size,
+ * non-contiguous blocks, like pages of virtual memory); "Paper digest:
+ * FlashAttention", section "Limits" (decode-time attention over batch-varying
+ * lengths).  Same attention as fa_decode, per sequence b of seq_lens[b] keys.
+ *   k_cache, v_cache : the block pool, [num_blocks, Hkv, block_size, d] bf16
+ *   block_table      : device int32 [B, max_blocks]; key j of sequence b is
+ *                      row j % block_size of block block_table[b][j / block_size]
+ *   seq_lens         : device int32 [B]
+ *   q, o, lse        : as fa_decode ([B,Hq,Nq,d], [B,Hq,Nq,d], [B,Hq,Nq])
+ *   ws               : fa_decode_paged_workspace_bytes() bytes, 16-byte aligned
+ * block_size must be a positive multiple of 32.  The lengths and block ids are
+ * read on the device: lengths are clamped to [0, max_blocks * block_size] and
+ * block ids to [0, num_blocks), so a bad table reads wrong rows but never
+ * outside the pool.  A row that sees no key (an empty sequence, or with
+ * causal = 1 a row i with seq_lens[b] - Nq + i < 0) gets O = 0 and
+ * LSE = -infinity.
+ */
+fa_status_t fa_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                            const int* block_table, const int* seq_lens,
+                            void* o, float* lse, float* ws,
+                            int B, int Hq, int Hkv, int Nq,
+                            int max_blocks, int block_size, int num_blocks, int d,
+                            int causal, float softmax_scale, int dtype,
+                            hipStream_t stream);
+
+/* Bytes of the paged decode workspace (0 for an empty or invalid problem). */
+size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int Nq,
+                                       int max_blocks, int block_size, int d);
+
 /* Static text for a status code ("unknown status" for other values). */
 const char* fa_status_string(fa_status_t s);
 

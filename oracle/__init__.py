@@ -17,8 +17,8 @@ Pages cited throughout (by title and section):
               Bandwidth Bottleneck", "Flash Attention Algorithm", "Online
               Softmax", "Performance Impact" table, "Integration".
   [FA-LLM]    inferensys.com glossary "Flash Attention" (self-hosted LLMs):
-              opening paragraphs; entries "Grouped-Query Attention (GQA)"
-              and "KV Cache".
+              opening paragraphs; entries "Grouped-Query Attention (GQA)",
+              "KV Cache" and "PagedAttention".
 
 Parity pins: every function here is pinned by a ``-m "not gpu"`` test against
 closed forms, invariants, finite differences, a library routine (torch CPU
@@ -29,6 +29,7 @@ from .attention import (  # noqa: F401
     forward,
     forward_online,
     decode_forward,
+    decode_paged_forward,
     backward,
     probabilities,
     head_rows_forward,

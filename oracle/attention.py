@@ -134,6 +134,44 @@ def decode_forward(q, k, v, causal, scale):
     return O, L
 
 
+def decode_paged_forward(q, k_cache, v_cache, block_table, seq_lens, causal, scale):
+    """Decode against a paged cache: O [B, Hq, Nq, d] and LSE [B, Hq, Nq].
+
+    [FA-LLM], entry "PagedAttention": the KV cache is kept in fixed-size,
+    non-contiguous blocks; sequence b's key j is row j % bs of block
+    block_table[b][j // bs] of the pool k_cache / v_cache [nblk, Hkv, bs, d],
+    and it has seq_lens[b] keys ([Digest], "Limits": batch-varying lengths).
+    Per sequence the keys are gathered in order, then the plain definition as
+    in ``decode_forward``: causal row i sees keys j <= n - Nq + i.  A row that
+    sees no key gets O = 0 and LSE = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, Nq, _ = q.shape
+    Hkv, bs = k_cache.shape[1], k_cache.shape[2]
+    G = Hq // Hkv
+    O = np.zeros((B, Hq, Nq, v_cache.shape[3]))
+    L = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n == 0:
+            continue
+        blocks = [int(x) for x in block_table[b][:(n + bs - 1) // bs]]
+        kb = np.concatenate([np.asarray(k_cache[x], dtype=np.float64) for x in blocks], axis=1)[:, :n]
+        vb = np.concatenate([np.asarray(v_cache[x], dtype=np.float64) for x in blocks], axis=1)[:, :n]
+        vis = np.ones((Nq, n), dtype=bool)
+        if causal:
+            vis = np.arange(n)[None, :] <= (n - Nq + np.arange(Nq))[:, None]
+        rows = vis.any(axis=1)
+        for h in range(Hq):
+            S = np.where(vis, scale * (q[b, h] @ kb[h // G].T), -np.inf)[rows]
+            m = S.max(axis=1)
+            E = np.exp(S - m[:, None])
+            l = E.sum(axis=1)
+            O[b, h, rows] = (E / l[:, None]) @ vb[h // G]
+            L[b, h, rows] = m + np.log(l)
+    return O, L
+
+
 def forward_online(q, k, v, causal, scale, block_sizes):
     """Forward by the tiled online softmax, key blocks taken in order.
 

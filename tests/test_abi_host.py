@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_bwd_workspace_bytes", "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_decode",
-                          "fa_decode_workspace_bytes",
+                          "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
                           "fa_status_string", "fa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -199,3 +199,24 @@ def test_local_validation():
     assert fa.fa_bwd_local(**{**bw, "dk": A[8]}) == 6
     assert fa.fa_bwd_local(**{**bw, "Hq": 3}) == 2
     assert fa.fa_bwd_local(**{**bw, "B": 0}) == 0
+
+
+def test_decode_paged_validation():
+    from exact_io_aware_50_amd import fa
+    a = dict(q=A[0], k_cache=A[1], v_cache=A[2], block_table=A[3], seq_lens=A[4], o=A[5], lse=A[6], ws=A[7], B=2,
+             Hq=8, Hkv=2, Nq=1, max_blocks=8, block_size=64, num_blocks=16, d=128, causal=0, softmax_scale=0.1,
+             dtype=1, stream=None)
+    assert fa.fa_decode_paged(**{**a, "block_size": 48}) == 3          # not a multiple of 32
+    assert fa.fa_decode_paged(**{**a, "block_size": 0}) == 3
+    assert fa.fa_decode_paged(**{**a, "num_blocks": 0}) == 2
+    assert fa.fa_decode_paged(**{**a, "max_blocks": 0}) == 2           # no key position at all
+    assert fa.fa_decode_paged(**{**a, "dtype": 0}) == 3
+    assert fa.fa_decode_paged(**{**a, "block_table": None}) == 1
+    assert fa.fa_decode_paged(**{**a, "seq_lens": A[4] + 2}) == 4
+    assert fa.fa_decode_paged(**{**a, "ws": A[1]}) == 6
+    assert fa.fa_decode_paged(**{**a, "o": A[3]}) == 6
+    assert fa.fa_decode_paged(**{**a, "Nq": 0}) == 0
+    n = fa.fa_decode_paged_workspace_bytes(2, 8, 2, 1, 8, 64, 128)
+    # float32 O and LSE per (row, key chunk); the paged plan cuts finer chunks
+    assert n >= fa.fa_decode_workspace_bytes(2, 8, 2, 1, 8 * 64, 128) > 0 and n % (4 * 2 * 8 * 1 * 129) == 0
+    assert fa.fa_decode_paged_workspace_bytes(2, 8, 2, 1, 8, 40, 128) == 0

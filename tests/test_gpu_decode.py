@@ -35,8 +35,9 @@ def f64(t):
 
 
 def check(o, lse, O, L, tag):
-    eo = float(np.max(np.abs(f64(o) - O)))
-    el = float(np.max(np.abs(f64(lse) - L)))
+    o, lse = (f64(x) if isinstance(x, torch.Tensor) else x for x in (o, lse))
+    eo = float(np.max(np.abs(o - O)))
+    el = float(np.max(np.abs(lse - L)))
     print(f"[{tag}] O max|err| {eo:.3e}  LSE max|err| {el:.3e}", flush=True)
     assert eo <= O_TOL and el <= LSE_TOL, (tag, eo, el)
 
@@ -103,4 +104,75 @@ def test_decode_workload_every_row(fa, dev, name):
         eo = max(eo, float(np.max(np.abs(f64(o[b:b + 1]) - O))))
         el = max(el, float(np.max(np.abs(f64(lse[b:b + 1]) - L))))
     print(f"[{name}] every row: O max|err| {eo:.3e}  LSE max|err| {el:.3e}", flush=True)
+    assert eo <= O_TOL and el <= LSE_TOL
+
+
+# ---------------------------------------------------------------- paged cache, per-sequence lengths
+
+def paged_case(seed, B, Hq, Hkv, Nq, lens, d, bs, spare=3):
+    """A shuffled block pool holding each sequence's keys, its block table and lengths (CPU tensors)."""
+    maxb = max((n + bs - 1) // bs for n in lens) if max(lens) > 0 else 1
+    nblk = B * maxb + spare
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 99])))
+    perm = rng.permutation(nblk)
+    kc = I.random_tensor(seed, (nblk, Hkv, bs, d), "bf16", tensor_id=1)
+    vc = I.random_tensor(seed, (nblk, Hkv, bs, d), "bf16", tensor_id=2)
+    table = torch.tensor(perm[:B * maxb].reshape(B, maxb), dtype=torch.int32)
+    q = I.random_tensor(seed, (B, Hq, Nq, d), "bf16", tensor_id=0)
+    return q, kc, vc, table, torch.tensor(lens, dtype=torch.int32)
+
+
+PAGED = [
+    # B, Hq, Hkv, Nq, lens, d, block size, causal
+    (3, 8, 1, 1, [1, 100, 257], 128, 32, False),
+    (2, 16, 2, 4, [1000, 64], 128, 64, True),
+    (4, 8, 8, 1, [33, 0, 500, 2048], 64, 256, False),
+    (2, 64, 8, 2, [3000, 1], 128, 128, True),
+    (2, 4, 2, 5, [3, 70], 64, 32, True),            # causal rows before sequence 0's first key
+]
+
+
+@pytest.mark.parametrize("case", PAGED, ids=lambda c: "B{}H{}x{}q{}d{}bs{}{}".format(*c[:4], *c[5:7], "c" if c[7] else ""))
+def test_decode_paged(fa, dev, case):
+    B, Hq, Hkv, Nq, lens, d, bs, causal = case
+    scale = 1.0 / np.sqrt(d)
+    q, kc, vc, table, sl = paged_case(4000 + sum(lens), B, Hq, Hkv, Nq, lens, d, bs)
+    print(f"case {case}", flush=True)
+    o, lse = fa.decode_paged(q.to(dev), kc.to(dev), vc.to(dev), table.to(dev), sl.to(dev), causal, scale)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_paged_forward(f64(q), f64(kc), f64(vc), table.numpy(), lens, causal, scale)
+    none = np.isneginf(L)                                    # rows that see no key: O = 0, LSE = -inf exactly
+    assert np.array_equal(np.isneginf(f64(lse)), none) and np.all(f64(o)[none] == 0)
+    keep = ~none
+    check(f64(o)[keep], f64(lse)[keep], O[keep], L[keep], str(case))
+
+
+@pytest.mark.timeout(300)
+def test_decode_paged_workload_mixed_lengths(fa, dev):
+    """The 16-sequence 16K-token cache as shuffled 256-key blocks, lengths in [Nk/4, Nk]: every row against the oracle."""
+    w = I.DECODE_WORKLOADS["decode_gqa_bf16_n16384"]
+    q, k, v = (I.decode_tensor(w, t) for t in range(3))
+    bs = 256
+    maxb = w.Nk // bs
+    g = torch.Generator().manual_seed(5)
+    perm = torch.randperm(w.B * maxb, generator=g)
+    lens = torch.randint(w.Nk // 4, w.Nk + 1, (w.B,), generator=g, dtype=torch.int32)
+    table = perm.view(w.B, maxb).to(torch.int32)
+    blk = lambda t: t.view(w.B, w.Hkv, maxb, bs, w.d).permute(0, 2, 1, 3, 4).reshape(w.B * maxb, w.Hkv, bs, w.d)
+    kc, vc = torch.empty_like(blk(k)), torch.empty_like(blk(v))
+    kc[perm] = blk(k)
+    vc[perm] = blk(v)
+    o, lse = fa.decode_paged(q.to(dev), kc.to(dev), vc.to(dev), table.to(dev), lens.to(dev), w.causal, w.scale)
+    o2, lse2 = fa.decode_paged(q.to(dev), kc.to(dev), vc.to(dev), table.to(dev), lens.to(dev), w.causal, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    o, lse = o.cpu(), lse.cpu()
+    eo = el = 0.0
+    for b in range(w.B):
+        n = int(lens[b])
+        O, L = oracle.decode_forward(f64(q[b:b + 1]), f64(k[b:b + 1, :, :n]), f64(v[b:b + 1, :, :n]), w.causal,
+                                     w.scale)
+        eo = max(eo, float(np.max(np.abs(f64(o[b:b + 1]) - O))))
+        el = max(el, float(np.max(np.abs(f64(lse[b:b + 1]) - L))))
+    print(f"[paged 16K mixed lengths] every row: O max|err| {eo:.3e}  LSE max|err| {el:.3e}", flush=True)
     assert eo <= O_TOL and el <= LSE_TOL

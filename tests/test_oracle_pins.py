@@ -429,3 +429,40 @@ def test_local_sampled_rows_and_columns_match_full():
     dKc, dVc = oracle.head_cols_backward_dkdv([q[0, 0], q[0, 1]], k[0, 0], v[0, 0], [do[0, 0], do[0, 1]], stats,
                                              rows, True, scale, window=W)
     assert np.max(np.abs(dKc - dk[0, 0, rows])) <= 1e-12 and np.max(np.abs(dVc - dv[0, 0, rows])) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_paged_equals_contiguous_decode(causal):
+    """A shuffled block pool read through its table gives the contiguous decode of each sequence's keys."""
+    B, Hq, Hkv, Nq, d, bs = 3, 4, 2, 3, 8, 4
+    lens = [9, 4, 12]
+    maxb = 3
+    rng = np.random.default_rng(150)
+    q = rnd(151, (B, Hq, Nq, d))
+    kfull, vfull = rnd(152, (B, Hkv, maxb * bs, d)), rnd(153, (B, Hkv, maxb * bs, d))
+    perm = rng.permutation(B * maxb)                    # block (b, i) is stored at pool slot perm[b*maxb + i]
+    kc, vc = np.zeros((B * maxb, Hkv, bs, d)), np.zeros((B * maxb, Hkv, bs, d))
+    table = np.zeros((B, maxb), dtype=np.int64)
+    for b in range(B):
+        for i in range(maxb):
+            slot = perm[b * maxb + i]
+            table[b, i] = slot
+            kc[slot] = kfull[b, :, i * bs:(i + 1) * bs]
+            vc[slot] = vfull[b, :, i * bs:(i + 1) * bs]
+    O, L = oracle.decode_paged_forward(q, kc, vc, table, lens, causal, 0.35)
+    for b in range(B):
+        n = lens[b]
+        Ob, Lb = oracle.decode_forward(q[b:b + 1], kfull[b:b + 1, :, :n], vfull[b:b + 1, :, :n], causal, 0.35)
+        assert np.max(np.abs(O[b] - Ob[0])) <= 1e-12 and np.max(np.abs(L[b] - Lb[0])) <= 1e-12
+
+
+def test_decode_paged_rows_without_keys():
+    """An empty sequence, and causal rows before a short sequence's first key: O = 0, LSE = -inf."""
+    q = rnd(160, (2, 2, 3, 4))
+    kc, vc = rnd(161, (2, 1, 4, 4)), rnd(162, (2, 1, 4, 4))
+    table = np.array([[0], [1]])
+    O, L = oracle.decode_paged_forward(q, kc, vc, table, [0, 2], True, 0.5)
+    assert np.all(O[0] == 0) and np.all(L[0] == -np.inf)
+    assert np.all(O[1, :, 0] == 0) and np.all(L[1, :, 0] == -np.inf)      # row 0 of 3 would sit at position -1
+    Ob, Lb = oracle.decode_forward(q[1:2, :, 1:], kc[1:2, :, :2], vc[1:2, :, :2], True, 0.5)
+    assert np.max(np.abs(O[1, :, 1:] - Ob[0])) <= 1e-12 and np.max(np.abs(L[1, :, 1:] - Lb[0])) <= 1e-12
