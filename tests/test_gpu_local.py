@@ -139,3 +139,35 @@ def test_local_gqa_4096_sampled(fa, dev):
     G_, R_ = c(got), c(ref)
     check(G_["O"], G_["L"], [G_["dQ"], G_["dK"], G_["dV"]], R_["O"], R_["L"], [R_["dQ"], R_["dK"], R_["dV"]],
           "N4096 W1024")
+
+
+@pytest.mark.timeout(600)
+def test_local_long_context_workload_sampled(fa, dev):
+    """The 64K-token sliding-window workload bench.py times (window 4096, Q and K with sigma 3): sampled rows of
+    two heads and the key columns of one K/V head against the oracle."""
+    w, W = I.LOCAL_WORKLOADS["local_bf16_n65536_w4096"]
+    q, k, v, do = (I.full_tensor(w, t) for t in range(4))
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.fwd_local(qd, kd, vd, W, w.scale)
+    dq, dk, dv, _ = fa.bwd_local(qd, kd, vd, o, dod, lse, W, w.scale)
+    torch.cuda.synchronize()
+    print("gpu done", flush=True)
+    rows = I.sample_rows(w.N)
+    got = {n: [] for n in ("O", "L", "dQ", "dK", "dV")}
+    ref = {n: [] for n in got}
+    for h in (0, w.Hq - 1):
+        dQr, Or, Lr, _ = oracle.head_rows_backward_dq(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), f64(do[0, h]), rows,
+                                                      True, w.scale, window=W)
+        got["O"].append(f64(o[0, h, rows])); ref["O"].append(Or)
+        got["L"].append(f64(lse[0, h, rows])); ref["L"].append(Lr)
+        got["dQ"].append(f64(dq[0, h, rows])); ref["dQ"].append(dQr)
+    g = w.Hkv - 1
+    stats = [oracle.head_full_stats(f64(q[0, g]), f64(k[0, g]), f64(v[0, g]), f64(do[0, g]), True, w.scale, window=W)]
+    dKc, dVc = oracle.head_cols_backward_dkdv([f64(q[0, g])], f64(k[0, g]), f64(v[0, g]), [f64(do[0, g])], stats, rows,
+                                             True, w.scale, window=W)
+    got["dK"].append(f64(dk[0, g, rows])); ref["dK"].append(dKc)
+    got["dV"].append(f64(dv[0, g, rows])); ref["dV"].append(dVc)
+    c = lambda d_: {n: np.concatenate(x) for n, x in d_.items()}
+    G_, R_ = c(got), c(ref)
+    check(G_["O"], G_["L"], [G_["dQ"], G_["dK"], G_["dV"]], R_["O"], R_["L"], [R_["dQ"], R_["dK"], R_["dV"]],
+          "N65536 W4096")
