@@ -23,13 +23,28 @@ import numpy as np
 ROW_BLOCK = 256   # rows materialised at once; each block still holds full rows of S and P
 
 
+def _band(window):
+    """(W, S) of a ``window`` argument: an int W, or a pair (W, S)."""
+    if isinstance(window, (tuple, list)):
+        return int(window[0]), int(window[1])
+    return int(window), 0
+
+
+def _band_visible(keys, rows, window):
+    """Sliding window with global tokens: j > i - W, or j < S (causal part applied by the caller)."""
+    W, S = _band(window)
+    return (keys > rows - W) | (keys < S)
+
+
 def _visible(rows: np.ndarray, n_keys: int, causal: bool, window=None) -> np.ndarray | None:
     """Boolean mask [len(rows), n_keys] of visible keys, or None when all are.
 
     ``window`` (with the causal mask only) is the sliding window of local
-    attention ([FA-legal], entry "Block-sparse": sliding-window (local)
-    attention is one of the named sparsity patterns): key j is visible to
-    query i iff i - window < j <= i.
+    attention, optionally with global tokens ([FA-legal], entry
+    "Block-sparse": sliding-window (local) attention and global tokens are
+    named sparsity patterns): an int W, or a pair (W, S).  Key j is visible to
+    query i iff j <= i and (i - W < j or j < S): the S leading tokens are
+    seen by every later query.
     """
     if window is not None and not causal:
         raise ValueError("the sliding window is defined with the causal mask")
@@ -38,7 +53,7 @@ def _visible(rows: np.ndarray, n_keys: int, causal: bool, window=None) -> np.nda
     keys = np.arange(n_keys)[None, :]
     vis = keys <= rows[:, None]
     if window is not None:
-        vis &= keys > rows[:, None] - int(window)
+        vis &= _band_visible(keys, rows[:, None], window)
     return vis
 
 
@@ -317,7 +332,7 @@ def head_cols_backward_dkdv(q_heads, kg, vg, do_heads, stats, cols, causal, scal
         if causal:
             vis = cols[None, :] <= rows[:, None]
             if window is not None:
-                vis &= cols[None, :] > rows[:, None] - int(window)
+                vis &= _band_visible(cols[None, :], rows[:, None], window)
             S = np.where(vis, S, -np.inf)
         P = np.exp(S - np.asarray(L)[:, None])
         dP = doh @ vg[cols].T

@@ -466,3 +466,28 @@ def test_decode_paged_rows_without_keys():
     assert np.all(O[1, :, 0] == 0) and np.all(L[1, :, 0] == -np.inf)      # row 0 of 3 would sit at position -1
     Ob, Lb = oracle.decode_forward(q[1:2, :, 1:], kc[1:2, :, :2], vc[1:2, :, :2], True, 0.5)
     assert np.max(np.abs(O[1, :, 1:] - Ob[0])) <= 1e-12 and np.max(np.abs(L[1, :, 1:] - Lb[0])) <= 1e-12
+
+
+@pytest.mark.parametrize("window,sink", [(3, 1), (5, 4), (1, 7), (8, 19)])
+def test_local_with_global_tokens_matches_torch_sdpa(window, sink):
+    """Window plus S leading global tokens: torch SDPA + autograd with the explicit mask (j <= i and (i - W < j or j < S))."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 17, 8
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, do = (rnd(170 + i, (B, H, N, d)) for i, H in enumerate((Hq, Hkv, Hkv, Hq)))
+    O, L = oracle.forward(q, k, v, True, scale, window=(window, sink))
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, True, scale, window=(window, sink))
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    i, j = torch.arange(N)[:, None], torch.arange(N)[None, :]
+    mask = (j <= i) & ((j > i - window) | (j < sink))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale, enable_gqa=True)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    s = scale * (tq.detach() @ tk.detach().repeat_interleave(Hq // Hkv, dim=1).transpose(-1, -2))
+    tl = torch.logsumexp(s.masked_fill(~mask, float("-inf")), dim=-1)
+    for a, b in ((O, o.detach()), (L, tl), (dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.max(np.abs(a - b.numpy())) <= 1e-12 * max(1.0, float(b.abs().max()))
+    # S = 0 is the plain window; S >= N sees every earlier key (causal)
+    O0, _ = oracle.forward(q, k, v, True, scale, window=(window, 0))
+    Ow, _ = oracle.forward(q, k, v, True, scale, window=window)
+    Oc, _ = oracle.forward(q, k, v, True, scale)
+    On, _ = oracle.forward(q, k, v, True, scale, window=(window, N))
+    assert np.max(np.abs(O0 - Ow)) <= 1e-15 and np.max(np.abs(On - Oc)) <= 1e-15
