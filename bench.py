@@ -110,14 +110,14 @@ def local_leg(torch, fa, I, dev, stream, args):
 
     def fwd():
         st = fa.fa_fwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq,
-                             w.Hkv, w.N, w.d, W, w.scale, code, sh)
+                             w.Hkv, w.N, w.d, W, 0, w.scale, code, sh)
         if st != fa.FA_OK:
             raise fa.FAError(st, "fa_fwd_local")
 
     def bwd():
         st = fa.fa_bwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d,
-                             W, w.scale, code, sh)
+                             W, 0, w.scale, code, sh)
         if st != fa.FA_OK:
             raise fa.FAError(st, "fa_bwd_local")
 

@@ -145,39 +145,42 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
                                            stream));
 }
 
-// Sliding window: W >= N sees exactly the causal keys, so the causal kernels run.
+// Sliding window: W >= N, or S >= N, sees exactly the causal keys, so the
+// causal kernels run.
 fa_status_t fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                         int N, int d, int window, float softmax_scale, int dtype, hipStream_t stream) {
+                         int N, int d, int window, int sink, float softmax_scale, int dtype, hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
-    if (window < 1) return FA_ERR_UNSUPPORTED;
+    if (window < 1 || sink < 0) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, 1, softmax_scale, &empty);
     if (s != FA_OK || empty) return s;
     s = check_ptrs({q, k, v}, {}, {o}, {lse});
     if (s != FA_OK) return s;
-    if (window >= N)
+    if (window >= N || sink >= N)
         return launch_status(fa::launch_fwd(dtype, d, 1, q, k, v, o, lse, B, Hq, Hkv, N, softmax_scale, stream));
-    return launch_status(fa::launch_fwd_bf16_local(d, q, k, v, o, lse, B, Hq, Hkv, N, window, softmax_scale, stream));
+    return launch_status(
+        fa::launch_fwd_bf16_local(d, q, k, v, o, lse, B, Hq, Hkv, N, window, sink, softmax_scale, stream));
 }
 
 fa_status_t fa_bwd_local(const void* q, const void* k, const void* v, const void* o, const void* dO,
                          const float* lse, void* dq, void* dk, void* dv, float* delta_ws, int B, int Hq, int Hkv,
-                         int N, int d, int window, float softmax_scale, int dtype, hipStream_t stream) {
+                         int N, int d, int window, int sink, float softmax_scale, int dtype, hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
-    if (window < 1) return FA_ERR_UNSUPPORTED;
+    if (window < 1 || sink < 0) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, 1, softmax_scale, &empty);
     if (s != FA_OK || empty) return s;
     s = check_ptrs({q, k, v, o, dO, delta_ws}, {lse}, {dq, dk, dv}, {});
     if (s != FA_OK) return s;
-    if (window >= N)
+    if (window >= N || sink >= N)
         return fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, 1, softmax_scale, dtype, stream);
     hipError_t e = fa::launch_bwd_delta(dtype, d, o, dO, lse, delta_ws, B, Hq, N, stream);
     if (e == hipSuccess)
-        e = fa::launch_bwd_dkdv_bf16_local(d, q, k, v, dO, delta_ws, dk, dv, B, Hq, Hkv, N, window, softmax_scale,
-                                           stream);
+        e = fa::launch_bwd_dkdv_bf16_local(d, q, k, v, dO, delta_ws, dk, dv, B, Hq, Hkv, N, window, sink,
+                                           softmax_scale, stream);
     if (e == hipSuccess)
-        e = fa::launch_bwd_dq_bf16_local(d, q, k, v, dO, delta_ws, dq, B, Hq, Hkv, N, window, softmax_scale, stream);
+        e = fa::launch_bwd_dq_bf16_local(d, q, k, v, dO, delta_ws, dq, B, Hq, Hkv, N, window, sink, softmax_scale,
+                                         stream);
     return launch_status(e);
 }
 

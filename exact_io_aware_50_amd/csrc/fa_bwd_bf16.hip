@@ -69,12 +69,16 @@ __device__ __forceinline__ void sched_dkdv_phase() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// LOCAL (with CAUSAL): sliding window with S global tokens, key j visible to
+// query i iff j <= i and (i - W < j or j < S); a key block's steps end at the
+// last query block that sees one of its keys (every later one when the block
+// holds global tokens).
 template <int D, bool CAUSAL, bool LOCAL = false>
 __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int n_rows, int Npad, float c2,
-    float scale, int W = 0) {
+    float scale, int W = 0, int S = 0) {
     using Cfg = KVBf16Cfg<D>;
     using QT = typename Cfg::QT;
     constexpr int NW = Cfg::kWaves, BNK = Cfg::BNK, BMQ = Cfg::BMQ, QB = Cfg::QB, NS = Cfg::kStages;
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         const int nqt = (N + BMQ - 1) / BMQ;
         const int qt0 = CAUSAL ? k0 / BMQ : 0;          // earlier query blocks see none of these keys
         // (local) later query blocks than qt1 - 1 see none of them either
-        const int qt1 = LOCAL ? min(nqt, (min(N, k0 + BNK) - 2 + W) / BMQ + 1) : nqt;
+        const int qt1 = LOCAL && k0 >= S ? min(nqt, (min(N, k0 + BNK) - 2 + W) / BMQ + 1) : nqt;
         const int total = G * (qt1 - qt0);              // steps: (head g*G + i / (qt1-qt0), block qt0 + i % (qt1-qt0))
 
         // ---- direct loads of step u, issued in step order.  The next step's
@@ -276,7 +280,8 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
             // queries all follow this wave's keys skip the test (uniform branch)
             const bool need_mask = CAUSAL && kw + 31 > q0;
             // local: query q0 + 32*qb + row(r) is past the window of key krow iff
-            // 8*(r/4) + r%4 + dw >= W, dw = q0 + 32*qb + 4*hh - krow
+            // 8*(r/4) + r%4 + dw >= W, dw = q0 + 32*qb + 4*hh - krow, unless the
+            // key is a global token
             const bool need_wmask = LOCAL && q0 + BMQ - 1 >= kw + W;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
@@ -300,7 +305,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
                         if (delta > 8 * (r / 4) + r % 4) sacc[qb][r] = 0.f;
                 }
                 if (need_wmask) {
-                    const int dw = q0 + 32 * qb + 4 * hh - krow;
+                    const int dw = krow >= S ? q0 + 32 * qb + 4 * hh - krow : -(1 << 30);
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         if (dw + 8 * (r / 4) + r % 4 >= W) sacc[qb][r] = 0.f;
@@ -441,14 +446,16 @@ __device__ __forceinline__ void sched_dq_phase() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// LOCAL (with CAUSAL): sliding window, key j visible to query i iff
-// i - W < j <= i; the key tiles of a query block start at the first one its
-// first row can see.
+// LOCAL (with CAUSAL): sliding window with S global tokens, key j visible to
+// query i iff j <= i and (i - W < j or j < S); a query block's key tiles are
+// the ns tiles holding global tokens left of its window, then the tiles from
+// the first one its first row can see.
 template <int D, bool CAUSAL, bool LOCAL = false>
 __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
-    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int n_rows, int Npad, float c2, float scale, int W = 0) {
+    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int n_rows, int Npad, float c2, float scale, int W = 0,
+    int S = 0) {
     using Cfg = QBf16Cfg<D>;
     using KT = typename Cfg::KT;
     constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BNK = Cfg::BNK, NS = Cfg::kStages, KB = BNK / 32;
@@ -482,18 +489,20 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
         const int qw = q0 + 32 * wave;
         const int qrow = qw + l32;
         const int kend = CAUSAL ? min(N, q0 + BM) : N;
-        const int ts = LOCAL ? max(0, q0 - W + 1) / BNK : 0;   // first key tile (t is tile ts + t)
-        const int ntiles = (kend + BNK - 1) / BNK - ts;
-        const int ntw = qw >= N ? 0 : CAUSAL ? (min(N, qw + 32) + BNK - 1) / BNK - ts : ntiles;
+        const int ts = LOCAL ? max(0, q0 - W + 1) / BNK : 0;   // first window key tile
+        const int ns = LOCAL ? min((S + BNK - 1) / BNK, ts) : 0;  // global-token tiles before it
+        auto tile_of = [&](int t) __attribute__((always_inline)) { return LOCAL ? (t < ns ? t : t - ns + ts) : t; };
+        const int ntiles = ns + (kend + BNK - 1) / BNK - ts;
+        const int ntw = qw >= N ? 0 : CAUSAL ? ns + (min(N, qw + 32) + BNK - 1) / BNK - ts : ntiles;
 
         // direct loads of tile t; the per-lane offsets are recomputed at every
         // issue from an opaque copy of the lane index (kept live across the
         // loop they would take registers the products need)
         auto issue = [&](int t) __attribute__((always_inline)) {
             const uint32_t st = lds_addr(smem + (t % NS) * kStage);
-            const uint16_t* kb = Kg + (int64_t)(t + ts) * BNK * D;
-            const uint16_t* vb = Vg + (int64_t)(t + ts) * BNK * D;
-            const int rows_valid = N - (t + ts) * BNK;
+            const uint16_t* kb = Kg + (int64_t)tile_of(t) * BNK * D;
+            const uint16_t* vb = Vg + (int64_t)tile_of(t) * BNK * D;
+            const int rows_valid = N - tile_of(t) * BNK;
             int ln = lane;
             asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -583,12 +592,12 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
                 for (int kb = 0; kb < KB; ++kb) dsf[kb][0] = dsf[kb][1] = u32x4{};
                 return;
             }
-            const int k0 = (t + ts) * BNK;
+            const int k0 = tile_of(t) * BNK;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c2, -lse2));
-            if ((CAUSAL && k0 + BNK - 1 > qw) || (k0 + BNK > N) || (LOCAL && k0 < qw + 32 - W)) {
+            if ((CAUSAL && k0 + BNK - 1 > qw) || (k0 + BNK > N) || (LOCAL && k0 < qw + 32 - W && k0 + BNK > S)) {
                 // row indices from an opaque copy of the lane half: hoisted
                 // out of the item loop, they and the masks derived from them
                 // would stay live in registers
@@ -599,7 +608,8 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = k0 + 32 * kb + acc_row(r, hm);
-                        if ((CAUSAL && key > qrow) || key >= N || (LOCAL && key <= qrow - W)) sacc[kb][r] = 0.f;
+                        if ((CAUSAL && key > qrow) || key >= N || (LOCAL && key <= qrow - W && key >= S))
+                            sacc[kb][r] = 0.f;
                     }
             }
 #pragma unroll
@@ -683,7 +693,7 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
 template <int D, bool CAUSAL, bool LOCAL = false>
 static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* ws,
                               void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, hipStream_t st,
-                              int W = 0) {
+                              int W = 0, int S = 0) {
     using Cfg = KVBf16Cfg<D>;
     const int nkb = (N + Cfg::BNK - 1) / Cfg::BNK;
     const int Np = ws_rows(N);
@@ -693,13 +703,13 @@ static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
                        ws + (int64_t)B * Hq * Np, (uint16_t*)dk, (uint16_t*)dv, B, Hq, Hkv, N, Np, scale * kLog2e,
-                       scale, W);
+                       scale, W, S);
     return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool LOCAL = false>
 static hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dq,
-                            int B, int Hq, int Hkv, int N, float scale, hipStream_t st, int W = 0) {
+                            int B, int Hq, int Hkv, int N, float scale, hipStream_t st, int W = 0, int S = 0) {
     using Cfg = QBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
     const int Np = ws_rows(N);
@@ -708,7 +718,7 @@ static hipError_t launch_dq(const void* q, const void* k, const void* v, const v
         persistent_grid((const void*)bwd_dq_bf16_kernel<D, CAUSAL, LOCAL>, Cfg::kThreads, nmb * Hq * B, slots);
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, LOCAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
-                       ws + (int64_t)B * Hq * Np, (uint16_t*)dq, B, Hq, Hkv, N, Np, scale * kLog2e, scale, W);
+                       ws + (int64_t)B * Hq * Np, (uint16_t*)dq, B, Hq, Hkv, N, Np, scale * kLog2e, scale, W, S);
     return hipGetLastError();
 }
 
@@ -733,17 +743,17 @@ hipError_t launch_bwd_dq_bf16(int d, int causal, const void* q, const void* k, c
 
 hipError_t launch_bwd_dkdv_bf16_local(int d, const void* q, const void* k, const void* v, const void* dO,
                                       const float* ws, void* dk, void* dv, int B, int Hq, int Hkv, int N, int W,
-                                      float scale, hipStream_t st) {
-    if (d == 64) return launch_dkdv<64, true, true>(q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st, W);
-    if (d == 128) return launch_dkdv<128, true, true>(q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st, W);
+                                      int S, float scale, hipStream_t st) {
+    if (d == 64) return launch_dkdv<64, true, true>(q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st, W, S);
+    if (d == 128) return launch_dkdv<128, true, true>(q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st, W, S);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq_bf16_local(int d, const void* q, const void* k, const void* v, const void* dO,
-                                    const float* ws, void* dq, int B, int Hq, int Hkv, int N, int W, float scale,
-                                    hipStream_t st) {
-    if (d == 64) return launch_dq<64, true, true>(q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st, W);
-    if (d == 128) return launch_dq<128, true, true>(q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st, W);
+                                    const float* ws, void* dq, int B, int Hq, int Hkv, int N, int W, int S,
+                                    float scale, hipStream_t st) {
+    if (d == 64) return launch_dq<64, true, true>(q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st, W, S);
+    if (d == 128) return launch_dq<128, true, true>(q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st, W, S);
     return hipErrorInvalidValue;
 }
 

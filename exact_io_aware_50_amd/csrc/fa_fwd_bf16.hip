@@ -74,16 +74,18 @@ __device__ __forceinline__ void sched_gemm_phase() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// LOCAL (with CAUSAL): sliding-window attention, key j visible to query i iff
-// i - W < j <= i (the FlashAttention legal glossary, entry "Block-sparse":
-// sliding-window local attention, whole tiles outside the pattern skipped).
-// A workgroup's tiles then start at tile ts, the first one holding a key its
-// first query row can see; keys left of a row's window are masked like those
-// past the diagonal.
+// LOCAL (with CAUSAL): sliding-window attention with S global tokens, key j
+// visible to query i iff j <= i and (i - W < j or j < S) (the FlashAttention
+// legal glossary, entry "Block-sparse": sliding-window local attention and
+// global tokens, whole tiles outside the pattern skipped).  A workgroup's
+// tiles are the ns tiles holding global tokens left of its window, then the
+// tiles from ts, the first one holding a key its first query row can see;
+// other keys left of a row's window are masked like those past the diagonal.
 template <int D, bool CAUSAL, bool LOCAL = false>
 __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int N, float c2, int W = 0) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int N, float c2, int W = 0,
+    int S = 0) {
     using Cfg = FwdBf16Cfg<D>;
     using KT = typename Cfg::KT;
     constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::kStages, KB = BN / 32;
@@ -112,9 +114,12 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
         const int qw = q0 + 32 * wave;                    // first query row of this wave
         const int qrow = qw + l32;                        // this lane's query row
         const int kend = CAUSAL ? min(N, q0 + BM) : N;
-        const int ts = LOCAL ? max(0, q0 - W + 1) / BN : 0;   // first tile of the workgroup
-        const int ntiles = (kend + BN - 1) / BN - ts;     // tiles of the workgroup (t is tile ts + t)
-        const int ntw = qw >= N ? 0 : CAUSAL ? (min(N, qw + 32) + BN - 1) / BN - ts : ntiles;   // tiles of this wave
+        const int ts = LOCAL ? max(0, q0 - W + 1) / BN : 0;   // first window tile of the workgroup
+        const int ns = LOCAL ? min((S + BN - 1) / BN, ts) : 0;    // global-token tiles before it
+        // the workgroup's t-th tile: tiles 0 .. ns-1, then ts, ts+1, ...
+        auto tile_of = [&](int t) __attribute__((always_inline)) { return LOCAL ? (t < ns ? t : t - ns + ts) : t; };
+        const int ntiles = ns + (kend + BN - 1) / BN - ts;    // tiles of the workgroup
+        const int ntw = qw >= N ? 0 : CAUSAL ? ns + (min(N, qw + 32) + BN - 1) / BN - ts : ntiles;   // tiles of this wave
 
         // ---- direct loads: this wave's row groups of a K/V tile, as byte offsets
         // from the tile's first row (rows past the end re-read the last row)
@@ -127,8 +132,8 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
         // half = 0: the K rows of tile t, 1: its V rows
         auto issue_half = [&](int t, const int half) __attribute__((always_inline)) {
             const uint32_t st = lds_addr(smem + (t % NS) * kStage) + half * KT::kBytes;
-            const uint16_t* src = (half ? Vh : Kh) + (int64_t)(t + ts) * BN * D;
-            const int rows_valid = N - (t + ts) * BN;
+            const uint16_t* src = (half ? Vh : Kh) + (int64_t)tile_of(t) * BN * D;
+            const int rows_valid = N - tile_of(t) * BN;
             if (rows_valid >= BN) {
 #pragma unroll
                 for (int i = 0; i < KT::kPerWave; ++i) dma16s(src, voff[i], st + (i * NW + wave) * KT::RGS);
@@ -213,10 +218,10 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
                 for (int kb = 0; kb < KB; ++kb) pf[kb][0] = pf[kb][1] = u32x4{};
                 return;
             }
-            const int k0 = (t + ts) * BN;
+            const int k0 = tile_of(t) * BN;
             // ---- keys past the diagonal (causal), past the end, or (local)
-            // left of some row's window
-            if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N || (LOCAL && k0 < qw + 32 - W)) {
+            // left of some row's window and not global
+            if ((CAUSAL && k0 + BN - 1 > qw) || k0 + BN > N || (LOCAL && k0 < qw + 32 - W && k0 + BN > S)) {
                 // row indices from an opaque copy of the lane half: hoisted
                 // out of the item loop, they and the masks derived from them
                 // would stay live in registers
@@ -227,7 +232,8 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = k0 + 32 * kb + acc_row(r, hm);
-                        if ((CAUSAL && key > qrow) || key >= N || (LOCAL && key <= qrow - W)) sacc[kb][r] = -INFINITY;
+                        if ((CAUSAL && key > qrow) || key >= N || (LOCAL && key <= qrow - W && key >= S))
+                            sacc[kb][r] = -INFINITY;
                     }
             }
             // ---- running max (base 2, scale*log2(e) in c2); moved only when some
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
 
 template <int D, bool CAUSAL, bool LOCAL = false>
 static hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                         int N, float scale, hipStream_t st, int W = 0) {
+                         int N, float scale, hipStream_t st, int W = 0, int S = 0) {
     using Cfg = FwdBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
     static std::atomic<int> slots{0};
@@ -349,7 +355,7 @@ static hipError_t launch(const void* q, const void* k, const void* v, void* o, f
         persistent_grid((const void*)fwd_bf16_kernel<D, CAUSAL, LOCAL>, Cfg::kThreads, nmb * Hq * B, slots);
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, LOCAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, B, Hq, Hkv, N,
-                       scale * kLog2e, W);
+                       scale * kLog2e, W, S);
     return hipGetLastError();
 }
 
@@ -363,9 +369,9 @@ hipError_t launch_fwd_bf16(int d, int causal, const void* q, const void* k, cons
 }
 
 hipError_t launch_fwd_bf16_local(int d, const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                                 int Hq, int Hkv, int N, int W, float scale, hipStream_t st) {
-    if (d == 64) return launch<64, true, true>(q, k, v, o, lse, B, Hq, Hkv, N, scale, st, W);
-    if (d == 128) return launch<128, true, true>(q, k, v, o, lse, B, Hq, Hkv, N, scale, st, W);
+                                 int Hq, int Hkv, int N, int W, int S, float scale, hipStream_t st) {
+    if (d == 64) return launch<64, true, true>(q, k, v, o, lse, B, Hq, Hkv, N, scale, st, W, S);
+    if (d == 128) return launch<128, true, true>(q, k, v, o, lse, B, Hq, Hkv, N, scale, st, W, S);
     return hipErrorInvalidValue;
 }
 

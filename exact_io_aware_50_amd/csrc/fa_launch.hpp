@@ -63,16 +63,16 @@ hipError_t launch_bwd_dkdv_bf16(int d, int causal, const void* q, const void* k,
 hipError_t launch_bwd_dq_bf16(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
                               const float* ws, void* dq, int B, int Hq, int Hkv, int N, float scale, hipStream_t st);
 
-// Causal sliding-window (local) attention, bf16: key j visible to query i iff
-// i - W < j <= i.
+// Causal sliding-window (local) attention with S global tokens, bf16: key j
+// visible to query i iff j <= i and (i - W < j or j < S).
 hipError_t launch_fwd_bf16_local(int d, const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                                 int Hq, int Hkv, int N, int W, float scale, hipStream_t st);
+                                 int Hq, int Hkv, int N, int W, int S, float scale, hipStream_t st);
 hipError_t launch_bwd_dkdv_bf16_local(int d, const void* q, const void* k, const void* v, const void* dO,
                                       const float* ws, void* dk, void* dv, int B, int Hq, int Hkv, int N, int W,
-                                      float scale, hipStream_t st);
+                                      int S, float scale, hipStream_t st);
 hipError_t launch_bwd_dq_bf16_local(int d, const void* q, const void* k, const void* v, const void* dO,
-                                    const float* ws, void* dq, int B, int Hq, int Hkv, int N, int W, float scale,
-                                    hipStream_t st);
+                                    const float* ws, void* dq, int B, int Hq, int Hkv, int N, int W, int S,
+                                    float scale, hipStream_t st);
 
 hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
 

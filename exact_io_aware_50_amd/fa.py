@@ -43,9 +43,9 @@ _lib.fa_bwd_workspace_bytes.argtypes = [_i, _i, _i]
 _lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.fa_quantize_fp8.argtypes = [_p, ctypes.c_size_t, _p, _p, _p]
 _lib.fa_quantize_fp8.restype = _i
-_lib.fa_fwd_local.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
+_lib.fa_fwd_local.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_fwd_local.restype = _i
-_lib.fa_bwd_local.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
+_lib.fa_bwd_local.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_bwd_local.restype = _i
 _lib.fa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_decode.restype = _i
@@ -106,13 +106,13 @@ def fa_quantize_fp8(x_bf16, n, x_e4m3, descale, stream) -> int:
     return _lib.fa_quantize_fp8(x_bf16, n, x_e4m3, descale, stream)
 
 
-def fa_fwd_local(q, k, v, o, lse, B, Hq, Hkv, N, d, window, softmax_scale, dtype, stream) -> int:
-    return _lib.fa_fwd_local(q, k, v, o, lse, B, Hq, Hkv, N, d, window, float(softmax_scale), dtype, stream)
+def fa_fwd_local(q, k, v, o, lse, B, Hq, Hkv, N, d, window, sink, softmax_scale, dtype, stream) -> int:
+    return _lib.fa_fwd_local(q, k, v, o, lse, B, Hq, Hkv, N, d, window, sink, float(softmax_scale), dtype, stream)
 
 
-def fa_bwd_local(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, window, softmax_scale, dtype,
+def fa_bwd_local(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, window, sink, softmax_scale, dtype,
                  stream) -> int:
-    return _lib.fa_bwd_local(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, window,
+    return _lib.fa_bwd_local(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, window, sink,
                              float(softmax_scale), dtype, stream)
 
 
@@ -217,19 +217,21 @@ def bwd(q, k, v, o, do, lse, causal: bool, scale: float, stream=None, workspace=
     return dq, dk, dv, workspace
 
 
-def fwd_local(q, k, v, window: int, scale: float, stream=None):
-    """(o, lse) of causal sliding-window attention (key j visible to query i iff i - window < j <= i), bf16."""
+def fwd_local(q, k, v, window: int, scale: float, stream=None, sink: int = 0):
+    """(o, lse) of causal sliding-window attention with `sink` global tokens, bf16.
+
+    Key j is visible to query i iff j <= i and (i - window < j or j < sink)."""
     torch = _torch()
     B, Hq, Hkv, N, d = _shape(q, k)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     _check(fa_fwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
-                        window, scale, _dtype_code(q), _stream_handle(stream)), "fa_fwd_local")
+                        window, sink, scale, _dtype_code(q), _stream_handle(stream)), "fa_fwd_local")
     return o, lse
 
 
-def bwd_local(q, k, v, o, do, lse, window: int, scale: float, stream=None, workspace=None):
-    """(dq, dk, dv, workspace) of causal sliding-window attention."""
+def bwd_local(q, k, v, o, do, lse, window: int, scale: float, stream=None, workspace=None, sink: int = 0):
+    """(dq, dk, dv, workspace) of causal sliding-window attention with `sink` global tokens."""
     torch = _torch()
     B, Hq, Hkv, N, d = _shape(q, k)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -237,7 +239,7 @@ def bwd_local(q, k, v, o, do, lse, window: int, scale: float, stream=None, works
         workspace = torch.empty(fa_bwd_workspace_bytes(B, Hq, N) // 4, dtype=torch.float32, device=q.device)
     _check(fa_bwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, d, window,
-                        scale, _dtype_code(q), _stream_handle(stream)), "fa_bwd_local")
+                        sink, scale, _dtype_code(q), _stream_handle(stream)), "fa_bwd_local")
     return dq, dk, dv, workspace
 
 

@@ -165,19 +165,21 @@ fa_status_t fa_quantize_fp8(const void* x_bf16, size_t n, void* x_e4m3,
                             float* descale, hipStream_t stream);
 
 /*
- * Causal sliding-window (local) attention: key j is visible to query i iff
- * i - window < j <= i.  The FlashAttention legal glossary, entry
- * "Block-sparse": a sparsity mask picks the blocks of the attention matrix
- * worth computing, sliding-window (local) attention being a common pattern,
- * and whole tiles outside it are skipped.  Same arguments, layouts and
- * outputs as fa_fwd / fa_bwd with causal = 1, plus `window` (>= 1; a window
- * of N or more is plain causal attention); bf16 only.  The backward reads
- * the LSE of fa_fwd_local with the same window.
+ * Causal sliding-window (local) attention with global tokens: key j is
+ * visible to query i iff j <= i and (i - window < j or j < sink).  The
+ * FlashAttention legal glossary, entry "Block-sparse": a sparsity mask picks
+ * the blocks of the attention matrix worth computing, sliding-window (local)
+ * attention and global tokens being common patterns, and whole tiles outside
+ * it are skipped.  Same arguments, layouts and outputs as fa_fwd / fa_bwd with
+ * causal = 1, plus `window` (>= 1) and `sink` (>= 0, the number of leading
+ * tokens every later query sees; 0 for none).  A window or sink of N or more
+ * is plain causal attention.  bf16 only.  The backward reads the LSE of
+ * fa_fwd_local with the same window and sink.
  */
 fa_status_t fa_fwd_local(const void* q, const void* k, const void* v,
                          void* o, float* lse,
                          int B, int Hq, int Hkv, int N, int d,
-                         int window, float softmax_scale, int dtype,
+                         int window, int sink, float softmax_scale, int dtype,
                          hipStream_t stream);
 
 fa_status_t fa_bwd_local(const void* q, const void* k, const void* v,
@@ -185,7 +187,7 @@ fa_status_t fa_bwd_local(const void* q, const void* k, const void* v,
                          void* dq, void* dk, void* dv,
                          float* delta_ws,
                          int B, int Hq, int Hkv, int N, int d,
-                         int window, float softmax_scale, int dtype,
+                         int window, int sink, float softmax_scale, int dtype,
                          hipStream_t stream);
 
 /*

@@ -183,9 +183,10 @@ def test_decode_empty_and_workspace():
 
 def test_local_validation():
     from exact_io_aware_50_amd import fa
-    f = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, Hq=2, Hkv=2, N=256, d=128, window=64,
+    f = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, Hq=2, Hkv=2, N=256, d=128, window=64, sink=0,
              softmax_scale=0.1, dtype=1, stream=None)
     assert fa.fa_fwd_local(**{**f, "window": 0}) == 3
+    assert fa.fa_fwd_local(**{**f, "sink": -1}) == 3
     assert fa.fa_fwd_local(**{**f, "dtype": 0}) == 3
     assert fa.fa_fwd_local(**{**f, "d": 32}) == 3
     assert fa.fa_fwd_local(**{**f, "q": None}) == 1
@@ -193,7 +194,7 @@ def test_local_validation():
     assert fa.fa_fwd_local(**{**f, "lse": A[4] + 2}) == 4
     assert fa.fa_fwd_local(**{**f, "N": 0}) == 0
     bw = dict(q=A[0], k=A[1], v=A[2], o=A[3], dO=A[4], lse=A[5], dq=A[6], dk=A[7], dv=A[8], delta_ws=A[9],
-              B=1, Hq=2, Hkv=2, N=256, d=128, window=64, softmax_scale=0.1, dtype=1, stream=None)
+              B=1, Hq=2, Hkv=2, N=256, d=128, window=64, sink=4, softmax_scale=0.1, dtype=1, stream=None)
     assert fa.fa_bwd_local(**{**bw, "window": -1}) == 3
     assert fa.fa_bwd_local(**{**bw, "delta_ws": None}) == 1
     assert fa.fa_bwd_local(**{**bw, "dk": A[8]}) == 6

@@ -1,6 +1,7 @@
 """GPU parity of causal sliding-window (local) attention (fa_fwd_local / fa_bwd_local) with the float64 oracle.
 
-Key j is visible to query i iff i - W < j <= i.  Tolerances are the bf16 ones:
+Key j is visible to query i iff j <= i and (i - W < j or j < S), S leading
+global tokens (0 for the plain window).  Tolerances are the bf16 ones:
 max |err| <= 2e-2 on O, <= 1e-2 on LSE, relative L2 <= 2e-2 on dQ, dK, dV.
 Small shapes (ragged lengths, windows from one key to nearly the whole
 sequence, grouped heads, d = 64 and 128) are compared element by element; a
@@ -55,8 +56,13 @@ def check(o, lse, grads, O, L, ref_grads, tag):
 
 
 SMALL = [
-    # B, Hq, Hkv, N, d, W
+    # B, Hq, Hkv, N, d, W  (S global tokens: a pair (W, S))
     (1, 2, 2, 300, 64, 1),
+    (1, 4, 2, 1000, 128, (100, 4)),
+    (1, 2, 2, 513, 128, (37, 64)),
+    (1, 3, 3, 777, 64, (100, 1)),
+    (1, 2, 1, 600, 128, (64, 300)),
+    (2, 2, 2, 2000, 64, (300, 130)),
     (1, 4, 2, 513, 128, 37),
     (2, 2, 1, 1000, 128, 256),
     (1, 3, 3, 777, 64, 100),
@@ -68,9 +74,10 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}H{}x{}N{}d{}W{}".format(*s))
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}H{}x{}N{}d{}W{}".format(*s[:5], str(s[5]).replace(" ", "")))
 def test_local_small_shapes(fa, dev, shape):
     B, Hq, Hkv, N, d, W = shape
+    W, S = W if isinstance(W, tuple) else (W, 0)
     scale = 1.0 / np.sqrt(d)
     seed = 5000 + N + W
     q = I.random_tensor(seed, (B, Hq, N, d), "bf16", tensor_id=0)
@@ -79,12 +86,12 @@ def test_local_small_shapes(fa, dev, shape):
     do = I.random_tensor(seed, (B, Hq, N, d), "bf16", tensor_id=3)
     print(f"case {shape}", flush=True)
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
-    o, lse = fa.fwd_local(qd, kd, vd, W, scale)
-    dq, dk, dv, _ = fa.bwd_local(qd, kd, vd, o, dod, lse, W, scale)
+    o, lse = fa.fwd_local(qd, kd, vd, W, scale, sink=S)
+    dq, dk, dv, _ = fa.bwd_local(qd, kd, vd, o, dod, lse, W, scale, sink=S)
     torch.cuda.synchronize()
     Q, K, V, dO = (f64(t) for t in (q, k, v, do))
-    O, L = oracle.forward(Q, K, V, True, scale, window=W)
-    rq, rk, rv, _ = oracle.backward(Q, K, V, dO, True, scale, window=W)
+    O, L = oracle.forward(Q, K, V, True, scale, window=(W, S))
+    rq, rk, rv, _ = oracle.backward(Q, K, V, dO, True, scale, window=(W, S))
     check(f64(o), f64(lse), [f64(x) for x in (dq, dk, dv)], O, L, [rq, rk, rv], str(shape))
 
 
@@ -94,11 +101,13 @@ def test_local_window_covering_the_sequence_is_causal(fa, dev):
     q, k, v, do = (I.random_tensor(77, (B, H, N, d), "bf16", tensor_id=t).to(dev)
                    for t, H in enumerate((Hq, Hkv, Hkv, Hq)))
     o, lse = fa.fwd_local(q, k, v, N, 0.1)
+    o_s, lse_s = fa.fwd_local(q, k, v, 10, 0.1, sink=N)
     oc, lc = fa.fwd(q, k, v, True, 0.1)
     g = fa.bwd_local(q, k, v, o, do, lse, N + 9, 0.1)[:3]
     gc = fa.bwd(q, k, v, oc, do, lc, True, 0.1)[:3]
     torch.cuda.synchronize()
     assert torch.equal(o, oc) and torch.equal(lse, lc)
+    assert torch.equal(o_s, oc) and torch.equal(lse_s, lc)
     for a, b in zip(g, gc):
         assert torch.equal(a, b)
 
