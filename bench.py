@@ -372,8 +372,9 @@ def main():
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {name: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
-           for i, (name, _) in enumerate(calls)}
+    samples = {name: sorted(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps))
+               for i, (name, _) in enumerate(calls)}
+    per = {name: sum(v) / len(v) for name, v in samples.items()}
     gpu_ms = sum(evs[s][0].elapsed_time(evs[s][-1]) for s in range(args.steps)) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step wall, {gpu_ms:.3f} ms/step on events; "
@@ -385,7 +386,9 @@ def main():
     kfl = kernel_flops(w)
     kern = {}
     for n, t in per.items():
-        ent = {"ms": round(t, 4)}
+        v = samples[n]
+        ent = {"ms": round(t, 4), "median_ms": round(v[len(v) // 2], 4), "min_ms": round(v[0], 4),
+               "max_ms": round(v[-1], 4)}
         if n in kfl:
             tf = kfl[n] / (t * 1e-3) / 1e12
             ent.update(tflops=round(tf, 1), frac_peak=round(tf / PEAK_BF16_TFLOPS, 4))
