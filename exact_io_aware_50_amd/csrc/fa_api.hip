@@ -196,7 +196,7 @@ static fa_status_t check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, i
     if (Hkv == 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
     // every query row must see at least one key
     if (Nk == 0 || (causal && Nq > Nk)) return FA_ERR_SHAPE;
-    const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d, fa::kPagedUnitsPerSlot);
+    const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d, 1);
     const int64_t units = (int64_t)B * Hkv * p.nrb * p.nsplit;
     const int64_t rows = (int64_t)B * Hq * Nq;
     if (units / 4 + 1 > INT32_MAX || rows / 4 + 1 > INT32_MAX) return FA_ERR_SHAPE;
@@ -233,14 +233,15 @@ static fa_status_t check_paged(int B, int Hq, int Hkv, int Nq, int maxb, int bs,
     if (s != FA_OK || *empty) return s;
     if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
     if (nblk == 0) return FA_ERR_SHAPE;
+    const int64_t units = (int64_t)fa::paged_chunks(B, Hq, Hkv, Nq, d) * Hkv * ((Hq / Hkv * (int64_t)Nq + 31) / 32);
+    if (units / 4 + 1 > INT32_MAX) return FA_ERR_SHAPE;
     return FA_OK;
 }
 
 size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int Nq, int max_blocks, int block_size, int d) {
     bool empty = false;
     if (check_paged(B, Hq, Hkv, Nq, max_blocks, block_size, 1, d, 0, 1.0f, &empty) != FA_OK || empty) return 0;
-    const int Nk = max_blocks * block_size;
-    return fa::decode_ws_bytes(fa::decode_plan(B, Hq, Hkv, Nq, Nk, d, fa::kPagedUnitsPerSlot), B, Hq, Nq, d);
+    return fa::paged_ws_bytes(B, Hq, Hkv, Nq, d);
 }
 
 fa_status_t fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,

@@ -44,6 +44,76 @@ struct DecCfg {
     static constexpr float kTau = 8.0f;               // log2 slack before the running max is moved
 };
 
+// Paged cache: the pool [nblk][Hkv][bs][D], the block table [B][maxb], and the
+// chunk plan written on the device by decode_plan_kernel from the lengths:
+// seq[b] = (first chunk, chunk count, chunk size, length), unit[c] = (batch,
+// first key, end key) of chunk c < T, batch -1 for an unused chunk.
+struct PagedArgs {
+    const int* table;
+    const int* seq;
+    const int* unit;
+    int maxb, bs, nblk, T;
+};
+
+// The chunks of a paged decode, from the sequence lengths: a nonempty sequence
+// of n keys (clamped to [0, maxb * bs]) gets 1 + floor(n (T - B) / L) chunks
+// of equal size rounded up to 32 keys, L being the total length, so that
+// every chunk slot holds about the same number of keys whatever the lengths
+// (T >= 2B makes the counts add up to at most T).  One workgroup.
+__global__ __launch_bounds__(256) void decode_plan_kernel(const int* __restrict__ lens, int B, int maxb, int bs,
+                                                          int T, int* __restrict__ seq, int* __restrict__ unit) {
+    __shared__ long long red[256];
+    __shared__ int scan[256];
+    const int tid = threadIdx.x;
+    const int cap = maxb * bs;
+    long long sum = 0;
+    for (int b = tid; b < B; b += 256) sum += min(max(lens[b], 0), cap);
+    red[tid] = sum;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    const long long L = red[0] > 0 ? red[0] : 1;
+    int base = 0;                                     // chunks of the sequences before this pass
+    for (int b0 = 0; b0 < B; b0 += 256) {
+        const int b = b0 + tid;
+        int n = 0, c = 0, cs = 0;
+        if (b < B) {
+            n = min(max(lens[b], 0), cap);
+            if (n > 0) {
+                c = 1 + (int)((long long)n * (T - B) / L);
+                cs = ((n + c - 1) / c + 31) / 32 * 32;
+                c = (n + cs - 1) / cs;
+            }
+        }
+        // inclusive scan of the counts over this pass
+        scan[tid] = c;
+        __syncthreads();
+        for (int w = 1; w < 256; w <<= 1) {
+            const int x = tid >= w ? scan[tid - w] : 0;
+            __syncthreads();
+            scan[tid] += x;
+            __syncthreads();
+        }
+        const int off = base + scan[tid] - c;
+        if (b < B) {
+            seq[4 * b] = off;
+            seq[4 * b + 1] = c;
+            seq[4 * b + 2] = cs;
+            seq[4 * b + 3] = n;
+            for (int j = 0; j < c; ++j) {
+                unit[3 * (off + j)] = b;
+                unit[3 * (off + j) + 1] = j * cs;
+                unit[3 * (off + j) + 2] = min(n, (j + 1) * cs);
+            }
+        }
+        base += scan[255];
+        __syncthreads();
+    }
+    for (int cid = base + tid; cid < T; cid += 256) unit[3 * cid] = -1;
+}
+
 // PAGED: the cache is a pool of blocks [nblk][Hkv][bs][D] and sequence b's
 // key j sits in block table[b][j / bs], row j % bs; sequence b has lens[b]
 // keys (the self-hosted LLM glossary, entry "PagedAttention": the KV cache in
@@ -51,12 +121,13 @@ struct DecCfg {
 // lengths at decode time).  bs is a multiple of the 32-key tile, so a tile
 // never straddles two blocks.  Lengths are clamped to [0, maxb * bs] and
 // block ids to [0, nblk): a bad table reads wrong rows, never outside the pool.
+// A wave's unit is (chunk of the plan, K/V head, row block); the chunk's
+// partial result for query row (h, i) goes to slot (chunk * Hq + h) * Nq + i.
 template <int D, bool CAUSAL, bool PAGED = false>
 __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     float* __restrict__ Wo, float* __restrict__ Wl, int B, int Hq, int Hkv, int Nq, int Nk, int chunk, int nsplit,
-    float c2, const int* __restrict__ table = nullptr, const int* __restrict__ lens = nullptr, int maxb = 0,
-    int bs = 0, int nblk = 0) {
+    float c2, PagedArgs pg = PagedArgs{}) {
     using Cfg = DecCfg<D>;
     using KT = typename Cfg::KT;
     constexpr int BN = Cfg::BN, kStage = Cfg::kStage, KP = KT::kPerWave, NS = Cfg::kStages;
@@ -65,19 +136,32 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = Hq / Hkv, R = G * Nq, nrb = (R + 31) / 32;
     const int64_t u = (int64_t)blockIdx.x * Cfg::kWaves + wave;    // this wave's unit
-    if (u >= (int64_t)B * Hkv * nrb * nsplit) return;               // wave-uniform; no barriers below
-    const int s = (int)(u % nsplit);
-    const int64_t rest = u / nsplit;
-    const int rb = (int)(rest % nrb);
-    const int g = (int)((rest / nrb) % Hkv), b = (int)(rest / nrb / Hkv);
+    int s, rb, g, b, cid = 0;
+    if constexpr (PAGED) {
+        if (u >= (int64_t)pg.T * Hkv * nrb) return;                 // wave-uniform; no barriers below
+        rb = (int)(u % nrb);
+        g = (int)((u / nrb) % Hkv);
+        cid = (int)(u / nrb / Hkv);
+        b = pg.unit[3 * cid];
+        if (b < 0) return;                                           // an unused chunk slot
+        s = 0;
+    } else {
+        if (u >= (int64_t)B * Hkv * nrb * nsplit) return;
+        s = (int)(u % nsplit);
+        const int64_t rest = u / nsplit;
+        rb = (int)(rest % nrb);
+        g = (int)((rest / nrb) % Hkv);
+        b = (int)(rest / nrb / Hkv);
+    }
 
     const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
     const int r = rb * 32 + l32;                      // this lane's packed query row
     const bool rv = r < R;
     const int hq = g * G + (rv ? r / Nq : 0), qi = rv ? r % Nq : 0;
-    const int Nb = PAGED ? min(max(lens[b], 0), maxb * bs) : Nk;   // this sequence's keys
+    const int Nb = PAGED ? pg.seq[4 * b + 3] : Nk;    // this sequence's keys
     const int lim = CAUSAL ? Nb - Nq + qi : Nb - 1;   // last key the row sees
-    const int kbeg = s * chunk, kend = min(Nb, kbeg + chunk);
+    const int kbeg = PAGED ? pg.unit[3 * cid + 1] : s * chunk;
+    const int kend = PAGED ? pg.unit[3 * cid + 2] : min(Nb, kbeg + chunk);
     const int nt = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
 
     uint16_t* ring = smem + wave * Cfg::kStages * kStage;
@@ -89,8 +173,8 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
         const int k0 = kbeg + t * BN;
         const uint16_t *ks = Kg + (int64_t)k0 * D, *vs = Vg + (int64_t)k0 * D;
         if constexpr (PAGED) {
-            const int blk = min(max(table[(int64_t)b * maxb + k0 / bs], 0), nblk - 1);
-            const int64_t off = (((int64_t)blk * Hkv + g) * bs + k0 % bs) * D;
+            const int blk = min(max(pg.table[(int64_t)b * pg.maxb + k0 / pg.bs], 0), pg.nblk - 1);
+            const int64_t off = (((int64_t)blk * Hkv + g) * pg.bs + k0 % pg.bs) * D;
             ks = K + off;
             vs = V + off;
         }
@@ -176,7 +260,8 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     const float lt = pair_sum(lsum);
     if (rv) {
         const int64_t row = ((int64_t)b * Hq + hq) * Nq + qi;
-        float* wo = Wo + (row * nsplit + s) * D;
+        const int64_t slot = PAGED ? ((int64_t)cid * Hq + hq) * Nq + qi : row * nsplit + s;
+        float* wo = Wo + slot * D;
         const float inv = lt > 0.f ? 1.0f / lt : 0.f;
 #pragma unroll
         for (int ct = 0; ct < D / 32; ++ct)
@@ -187,34 +272,44 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
                 for (int e = 0; e < 4; ++e) w[e] = oacc[ct][4 * gq + e] * inv;
                 *reinterpret_cast<f32x4*>(wo + 32 * ct + 8 * gq + 4 * hh) = w;
             }
-        if (hh == 0) Wl[row * nsplit + s] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+        if (hh == 0) Wl[slot] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
     }
 }
 
 // One wave per query row: LSE = L + ln(sum_s exp(LSE_s - L)) with L the
-// largest chunk LSE, O = sum_s exp(LSE_s - LSE) O_s.
+// largest chunk LSE, O = sum_s exp(LSE_s - LSE) O_s.  The chunks of row r are
+// slots r * nsplit + s (contiguous cache) or, with a paged plan `seq`, slots
+// (first + j) * HqNq + r % HqNq for the row's sequence's chunks j.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ Wo,
                                                            const float* __restrict__ Wl, uint16_t* __restrict__ O,
-                                                           float* __restrict__ LSE, int64_t rows, int nsplit) {
+                                                           float* __restrict__ LSE, int64_t rows, int nsplit,
+                                                           const int* __restrict__ seq = nullptr, int HqNq = 0) {
     constexpr int PER = D / 64;                       // d values per lane
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const int lane = threadIdx.x & 63;
-    const float* wl = Wl + row * nsplit;
+    int64_t first = row * nsplit, stride = 1;
+    int cnt = nsplit;
+    if (seq) {
+        const int b = (int)(row / HqNq);
+        first = (int64_t)seq[4 * b] * HqNq + row % HqNq;
+        stride = HqNq;
+        cnt = seq[4 * b + 1];
+    }
     float L = -INFINITY;
-    for (int s = lane; s < nsplit; s += 64) L = fmaxf(L, wl[s]);
+    for (int s = lane; s < cnt; s += 64) L = fmaxf(L, Wl[first + s * stride]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) L = fmaxf(L, __shfl_xor(L, off));
     float acc[PER], wsum = 0.f;
 #pragma unroll
     for (int p = 0; p < PER; ++p) acc[p] = 0.f;
 #pragma unroll 4
-    for (int s = 0; s < nsplit; ++s) {
-        const float ls = wl[s];
+    for (int s = 0; s < cnt; ++s) {
+        const float ls = Wl[first + s * stride];
         const float w = ls == -INFINITY ? 0.f : fast_exp2((ls - L) * kLog2e);
         wsum += w;
-        const float* wo = Wo + (row * nsplit + s) * D + lane * PER;
+        const float* wo = Wo + (first + s * stride) * D + lane * PER;
 #pragma unroll
         for (int p = 0; p < PER; ++p) acc[p] = fmaf(w, wo[p], acc[p]);
     }
@@ -250,24 +345,68 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int per_sl
     return p;
 }
 
-template <int D, bool CAUSAL, bool PAGED = false>
+template <int D, bool CAUSAL>
 static hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int B,
-                         int Hq, int Hkv, int Nq, int Nk, float scale, hipStream_t st, const int* table = nullptr,
-                         const int* lens = nullptr, int maxb = 0, int bs = 0, int nblk = 0) {
+                         int Hq, int Hkv, int Nq, int Nk, float scale, hipStream_t st) {
     using Cfg = DecCfg<D>;
-    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk, D, PAGED ? kPagedUnitsPerSlot : 1);
+    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk, D, 1);
     const int64_t rows = (int64_t)B * Hq * Nq;
     float* wo = ws;
     float* wl = ws + rows * p.nsplit * D;
     const int64_t units = (int64_t)B * Hkv * p.nrb * p.nsplit;
     const unsigned g1 = (unsigned)((units + Cfg::kWaves - 1) / Cfg::kWaves);
-    hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, PAGED>), dim3(g1), dim3(Cfg::kThreads), 0, st,
+    hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, false>), dim3(g1), dim3(Cfg::kThreads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, wo, wl, B, Hq, Hkv, Nq, Nk, p.chunk,
-                       p.nsplit, scale * kLog2e, table, lens, maxb, bs, nblk);
+                       p.nsplit, scale * kLog2e, PagedArgs{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, wo, wl,
-                       (uint16_t*)o, lse, rows, p.nsplit);
+                       (uint16_t*)o, lse, rows, p.nsplit, (const int*)nullptr, 0);
+    return hipGetLastError();
+}
+
+int paged_chunks(int B, int Hq, int Hkv, int Nq, int d) {
+    // about one wave unit (chunk x K/V head x row block) per resident wave of
+    // the 256 CUs, and at least two chunk slots per sequence
+    const int nrb = (Hq / Hkv * Nq + 31) / 32;
+    const int64_t slots = 256 * (int64_t)(d == 128 ? DecCfg<128>::kWaves : DecCfg<64>::kWaves);
+    const int64_t per = (int64_t)Hkv * nrb;
+    const int64_t T = (slots + per - 1) / per;
+    return (int)(T > 2 * (int64_t)B ? T : 2 * (int64_t)B);
+}
+
+size_t paged_ws_bytes(int B, int Hq, int Hkv, int Nq, int d) {
+    const int64_t T = paged_chunks(B, Hq, Hkv, Nq, d);
+    const int64_t ints = ((4 * (int64_t)B + 3 * T) * 4 + 15) / 16 * 16;
+    return (size_t)(ints + 4 * T * Hq * Nq * (int64_t)(d + 1));
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_paged(const void* q, const void* kc, const void* vc, const int* table, const int* lens,
+                               void* o, float* lse, float* ws, int B, int Hq, int Hkv, int Nq, int maxb, int bs,
+                               int nblk, float scale, hipStream_t st) {
+    using Cfg = DecCfg<D>;
+    const int T = paged_chunks(B, Hq, Hkv, Nq, D);
+    const int nrb = (Hq / Hkv * Nq + 31) / 32;
+    int* seq = reinterpret_cast<int*>(ws);
+    int* unit = seq + 4 * (int64_t)B;
+    const int64_t ints = ((4 * (int64_t)B + 3 * (int64_t)T) * 4 + 15) / 16 * 16;
+    float* wo = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ints);
+    float* wl = wo + (int64_t)T * Hq * Nq * D;
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(256), 0, st, lens, B, maxb, bs, T, seq, unit);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const PagedArgs pg{table, seq, unit, maxb, bs, nblk, T};
+    const int64_t units = (int64_t)T * Hkv * nrb;
+    const unsigned g1 = (unsigned)((units + Cfg::kWaves - 1) / Cfg::kWaves);
+    hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, true>), dim3(g1), dim3(Cfg::kThreads), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, wo, wl, B, Hq, Hkv, Nq,
+                       maxb * bs, 0, 0, scale * kLog2e, pg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = (int64_t)B * Hq * Nq;
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, wo, wl,
+                       (uint16_t*)o, lse, rows, 0, (const int*)seq, Hq * Nq);
     return hipGetLastError();
 }
 
@@ -283,10 +422,9 @@ hipError_t launch_decode(int d, int causal, const void* q, const void* k, const 
 hipError_t launch_decode_paged(int d, int causal, const void* q, const void* kc, const void* vc, const int* table,
                                const int* lens, void* o, float* lse, float* ws, int B, int Hq, int Hkv, int Nq,
                                int maxb, int bs, int nblk, float scale, hipStream_t st) {
-    const int Nk = maxb * bs;                         // the longest a sequence can be
-#define PARGS q, kc, vc, o, lse, ws, B, Hq, Hkv, Nq, Nk, scale, st, table, lens, maxb, bs, nblk
-    if (d == 64) return causal ? launch<64, true, true>(PARGS) : launch<64, false, true>(PARGS);
-    if (d == 128) return causal ? launch<128, true, true>(PARGS) : launch<128, false, true>(PARGS);
+#define PARGS q, kc, vc, table, lens, o, lse, ws, B, Hq, Hkv, Nq, maxb, bs, nblk, scale, st
+    if (d == 64) return causal ? launch_paged<64, true>(PARGS) : launch_paged<64, false>(PARGS);
+    if (d == 128) return causal ? launch_paged<128, true>(PARGS) : launch_paged<128, false>(PARGS);
 #undef PARGS
     return hipErrorInvalidValue;
 }

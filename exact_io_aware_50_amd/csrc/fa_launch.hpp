@@ -82,12 +82,11 @@ struct DecodePlan {
     int nrb, nsplit, chunk;
 };
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int per_slot);
-// wave units per resident wave for the paged cache.  Its lengths vary, but
-// four units per wave (finer chunks, so that slots freed by short sequences
-// take more work) measured slower than one on the 16-sequence 16K workload
-// with lengths in [4K, 16K]: 0.162 against 0.144 ms, the extra unit start-ups
-// costing more than the better balance gains.
-constexpr int kPagedUnitsPerSlot = 1;
+// Paged decode: chunk slots of the device-side plan, and the workspace
+// (plan ints [B][4] + [T][3], 16-byte aligned, then float32 O [T][Hq][Nq][d]
+// and LSE [T][Hq][Nq]).
+int paged_chunks(int B, int Hq, int Hkv, int Nq, int d);
+size_t paged_ws_bytes(int B, int Hq, int Hkv, int Nq, int d);
 
 // Workspace of fa_decode: float32 O per (row, chunk) [rows][nsplit][d], then
 // the chunk LSEs [rows][nsplit], rows = B * Hq * Nq.
