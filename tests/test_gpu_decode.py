@@ -129,22 +129,26 @@ PAGED = [
     (4, 8, 8, 1, [33, 0, 500, 2048], 64, 256, False),
     (2, 64, 8, 2, [3000, 1], 128, 128, True),
     (2, 4, 2, 5, [3, 70], 64, 32, True),            # causal rows before sequence 0's first key
+    # more sequences than the plan kernel's 256 threads: its scan runs in two passes
+    (300, 2, 1, 1, [int(x) for x in np.random.Generator(np.random.PCG64(31)).integers(0, 200, 300)], 64, 32, False),
 ]
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("case", PAGED, ids=lambda c: "B{}H{}x{}q{}d{}bs{}{}".format(*c[:4], *c[5:7], "c" if c[7] else ""))
 def test_decode_paged(fa, dev, case):
     B, Hq, Hkv, Nq, lens, d, bs, causal = case
     scale = 1.0 / np.sqrt(d)
     q, kc, vc, table, sl = paged_case(4000 + sum(lens), B, Hq, Hkv, Nq, lens, d, bs)
-    print(f"case {case}", flush=True)
+    tag = f"B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} lens[{len(lens)}] max {max(lens)} d={d} bs={bs} causal={causal}"
+    print(f"case {tag}", flush=True)
     o, lse = fa.decode_paged(q.to(dev), kc.to(dev), vc.to(dev), table.to(dev), sl.to(dev), causal, scale)
     torch.cuda.synchronize()
     O, L = oracle.decode_paged_forward(f64(q), f64(kc), f64(vc), table.numpy(), lens, causal, scale)
     none = np.isneginf(L)                                    # rows that see no key: O = 0, LSE = -inf exactly
     assert np.array_equal(np.isneginf(f64(lse)), none) and np.all(f64(o)[none] == 0)
     keep = ~none
-    check(f64(o)[keep], f64(lse)[keep], O[keep], L[keep], str(case))
+    check(f64(o)[keep], f64(lse)[keep], O[keep], L[keep], tag)
 
 
 @pytest.mark.timeout(300)
