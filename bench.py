@@ -386,9 +386,9 @@ def main():
     kfl = kernel_flops(w)
     kern = {}
     for n, t in per.items():
-        v = samples[n]
-        ent = {"ms": round(t, 4), "median_ms": round(v[len(v) // 2], 4), "min_ms": round(v[0], 4),
-               "max_ms": round(v[-1], 4)}
+        ts = samples[n]
+        ent = {"ms": round(t, 4), "median_ms": round(ts[len(ts) // 2], 4), "min_ms": round(ts[0], 4),
+               "max_ms": round(ts[-1], 4)}
         if n in kfl:
             tf = kfl[n] / (t * 1e-3) / 1e12
             ent.update(tflops=round(tf, 1), frac_peak=round(tf / PEAK_BF16_TFLOPS, 4))
