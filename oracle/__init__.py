@@ -26,6 +26,7 @@ float64 scaled_dot_product_attention) or the pages' printed memory arithmetic.
 No function is "parity unpinned".
 """
 from .attention import (  # noqa: F401
+    BlockMask,
     forward,
     forward_online,
     decode_forward,

@@ -23,6 +23,25 @@ import numpy as np
 ROW_BLOCK = 256   # rows materialised at once; each block still holds full rows of S and P
 
 
+def _log(x):
+    """Natural log with log(0) = -inf and no warning (a row that sees no key has LSE = -inf)."""
+    with np.errstate(divide="ignore"):
+        return np.log(x)
+
+
+class BlockMask:
+    """A block-sparse pattern: key j is visible to query i iff mask[i // bs, j // bs].
+
+    [FA-legal], entry "Block-sparse": a sparsity mask over the blocks of the
+    attention matrix says which blocks are computed.  Used as the ``window``
+    argument; with the causal mask both conditions apply.
+    """
+
+    def __init__(self, mask, bs):
+        self.mask = np.asarray(mask, dtype=bool)
+        self.bs = int(bs)
+
+
 def _band(window):
     """(W, S) of a ``window`` argument: an int W, or a pair (W, S)."""
     if isinstance(window, (tuple, list)):
@@ -31,7 +50,9 @@ def _band(window):
 
 
 def _band_visible(keys, rows, window):
-    """Sliding window with global tokens: j > i - W, or j < S (causal part applied by the caller)."""
+    """Sliding window with global tokens: j > i - W, or j < S; or a block mask (causal part applied by the caller)."""
+    if isinstance(window, BlockMask):
+        return window.mask[rows // window.bs, keys // window.bs]
     W, S = _band(window)
     return (keys > rows - W) | (keys < S)
 
@@ -46,17 +67,18 @@ def _visible(rows: np.ndarray, n_keys: int, causal: bool, window=None) -> np.nda
     query i iff j <= i and (i - W < j or j < S): the S leading tokens are
     seen by every later query.
     """
-    if window is not None and not causal:
+    if window is not None and not causal and not isinstance(window, BlockMask):
         raise ValueError("the sliding window is defined with the causal mask")
-    if not causal:
-        return None
     keys = np.arange(n_keys)[None, :]
+    if not causal:
+        return None if window is None else _band_visible(keys, rows[:, None], window)
     vis = keys <= rows[:, None]
     if window is not None:
         vis &= _band_visible(keys, rows[:, None], window)
     return vis
 
 
+@np.errstate(divide="ignore")
 def probabilities(qh, kg, scale, causal, rows=None, window=None):
     """Rows of S and P = softmax(S), plus the row max m and row sum l.
 
@@ -75,9 +97,10 @@ def probabilities(qh, kg, scale, causal, rows=None, window=None):
     if vis is not None:
         S = np.where(vis, S, -np.inf)
     m = S.max(axis=1)
-    E = np.exp(S - m[:, None])
+    seen = np.isfinite(m)                               # rows that see at least one key
+    E = np.exp(S - np.where(seen, m, 0.0)[:, None])
     l = E.sum(axis=1)
-    P = E / l[:, None]
+    P = E / np.where(seen, l, 1.0)[:, None]
     return S, P, m, l
 
 
@@ -95,7 +118,7 @@ def head_rows_forward(qh, kg, vg, rows, causal, scale, window=None):
         r = rows[s:s + ROW_BLOCK]
         _, P, m, l = probabilities(qh, kg, scale, causal, r, window)
         O[s:s + r.size] = P @ vg
-        L[s:s + r.size] = m + np.log(l)
+        L[s:s + r.size] = m + _log(l)
     return O, L
 
 
@@ -296,7 +319,7 @@ def head_rows_backward_dq(qh, kg, vg, doh, rows, causal, scale, window=None):
         dS = P * (dP - D[:, None])
         dQ[s:s + r.size] = scale * (dS @ kg)
         O[s:s + r.size] = Or
-        L[s:s + r.size] = m + np.log(l)
+        L[s:s + r.size] = m + _log(l)
         Dr[s:s + r.size] = D
     return dQ, O, L, Dr
 
@@ -329,12 +352,18 @@ def head_cols_backward_dkdv(q_heads, kg, vg, do_heads, stats, cols, causal, scal
         qh = np.asarray(qh, dtype=np.float64)
         doh = np.asarray(doh, dtype=np.float64)
         S = scale * (qh @ kg[cols].T)                      # [n, |cols|]
+        vis = None
         if causal:
             vis = cols[None, :] <= rows[:, None]
             if window is not None:
                 vis &= _band_visible(cols[None, :], rows[:, None], window)
+        elif window is not None:
+            vis = _band_visible(cols[None, :], rows[:, None], window)
+        if vis is not None:
             S = np.where(vis, S, -np.inf)
-        P = np.exp(S - np.asarray(L)[:, None])
+        L_ = np.asarray(L)
+        seen = np.isfinite(L_)                          # rows that see no key at all have P = 0
+        P = np.where(seen[:, None], np.exp(S - np.where(seen, L_, 0.0)[:, None]), 0.0)
         dP = doh @ vg[cols].T
         dS = P * (dP - np.asarray(D)[:, None])
         dV += P.T @ doh

@@ -491,3 +491,56 @@ def test_local_with_global_tokens_matches_torch_sdpa(window, sink):
     Oc, _ = oracle.forward(q, k, v, True, scale)
     On, _ = oracle.forward(q, k, v, True, scale, window=(window, N))
     assert np.max(np.abs(O0 - Ow)) <= 1e-15 and np.max(np.abs(On - Oc)) <= 1e-15
+
+
+# ---------------------------------------------------------------- block-sparse masks
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_mask_matches_torch_sdpa(causal):
+    """Key j visible to query i iff mask[i // bs, j // bs] (and j <= i when causal): torch SDPA + autograd."""
+    B, Hq, Hkv, N, d, bs = 1, 4, 2, 21, 8, 4
+    scale = 1.0 / np.sqrt(d)
+    nb = (N + bs - 1) // bs
+    mask = np.random.default_rng(180).random((nb, nb)) < 0.5
+    np.fill_diagonal(mask, True)                      # every row sees at least its own block
+    bm = oracle.BlockMask(mask, bs)
+    q, k, v, do = (rnd(181 + i, (B, H, N, d)) for i, H in enumerate((Hq, Hkv, Hkv, Hq)))
+    O, L = oracle.forward(q, k, v, causal, scale, window=bm)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, causal, scale, window=bm)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    i, j = torch.arange(N)[:, None], torch.arange(N)[None, :]
+    m = torch.tensor(mask)[i // bs, j // bs]
+    if causal:
+        m &= j <= i
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=scale, enable_gqa=True)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    s = scale * (tq.detach() @ tk.detach().repeat_interleave(Hq // Hkv, dim=1).transpose(-1, -2))
+    tl = torch.logsumexp(s.masked_fill(~m, float("-inf")), dim=-1)
+    for a, b in ((O, o.detach()), (L, tl), (dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.max(np.abs(a - b.numpy())) <= 1e-12 * max(1.0, float(b.abs().max()))
+    # all blocks on: plain attention
+    On, Ln = oracle.forward(q, k, v, causal, scale, window=oracle.BlockMask(np.ones((nb, nb), bool), bs))
+    Op, Lp = oracle.forward(q, k, v, causal, scale)
+    assert np.max(np.abs(On - Op)) <= 1e-15 and np.max(np.abs(Ln - Lp)) <= 1e-15
+
+
+def test_block_mask_rows_without_keys():
+    """A query block with no visible block: O = 0, LSE = -inf, dQ = 0, and its dO reaches no dK or dV."""
+    B, H, N, d, bs = 1, 1, 12, 4, 4
+    mask = np.ones((3, 3), bool)
+    mask[1, :] = False                                  # rows 4..7 see nothing
+    bm = oracle.BlockMask(mask, bs)
+    q, k, v, do = (rnd(190 + i, (B, H, N, d)) for i in range(4))
+    O, L = oracle.forward(q, k, v, False, 0.5, window=bm)
+    dq, dk, dv, _ = oracle.backward(q, k, v, do, False, 0.5, window=bm)
+    assert np.all(O[0, 0, 4:8] == 0) and np.all(np.isneginf(L[0, 0, 4:8]))
+    assert np.all(dq[0, 0, 4:8] == 0)
+    do2 = do.copy()
+    do2[0, 0, 4:8] += 5.0                               # the masked rows' output gradient changes nothing
+    dq2, dk2, dv2, _ = oracle.backward(q, k, v, do2, False, 0.5, window=bm)
+    assert np.max(np.abs(dk2 - dk)) <= 1e-12 and np.max(np.abs(dv2 - dv)) <= 1e-12
+    rows = np.array([0, 5, 11])
+    stats = [oracle.head_full_stats(q[0, 0], k[0, 0], v[0, 0], do[0, 0], False, 0.5, window=bm)]
+    dKc, dVc = oracle.head_cols_backward_dkdv([q[0, 0]], k[0, 0], v[0, 0], [do[0, 0]], stats, rows, False, 0.5,
+                                             window=bm)
+    assert np.max(np.abs(dKc - dk[0, 0, rows])) <= 1e-12 and np.max(np.abs(dVc - dv[0, 0, rows])) <= 1e-12
