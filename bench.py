@@ -147,6 +147,69 @@ def local_leg(torch, fa, I, dev, stream, args):
             "note": "causal sliding window; credited 4 d flops per visible pair forward, 2.5x backward"}
 
 
+def block_pairs(mask, N, bs=256):
+    """(query, key) pairs inside the on blocks of a block mask, keys and rows past N left out."""
+    import numpy as np
+    ext = np.minimum(bs, N - bs * np.arange(mask.shape[0]))
+    return int(ext @ mask.astype(np.int64) @ ext)
+
+
+def bsparse_leg(torch, fa, I, dev, stream, args):
+    """fa_fwd_bsparse and fa_bwd_bsparse on the block-sparse workload, HIP events on the launch stream.
+
+    Credited flops: 4 d per (query, key) pair in an on block and query head forward, 2.5x that backward."""
+    w, pat = I.BSPARSE_WORKLOADS[args.bsparse_workload]
+    mask = I.block_pattern((w.N + 255) // 256, **pat)
+    L = fa.BlockSparseLayout(mask, device=dev)
+    q, k, v, do = (I.full_tensor(w, t).to(dev) for t in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.N) // 4, dtype=torch.float32, device=dev)
+    sh = stream.cuda_stream
+    code = fa.FA_DTYPE_BF16
+
+    def fwd():
+        st = fa.fa_fwd_bsparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq,
+                               w.Hkv, w.N, w.d, 0, L.row_ptr.data_ptr(), L.col_idx.data_ptr(), L.nnz, w.scale, code,
+                               sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_fwd_bsparse")
+
+    def bwd():
+        st = fa.fa_bwd_bsparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), w.B, w.Hq,
+                               w.Hkv, w.N, w.d, 0, L.row_ptr.data_ptr(), L.col_idx.data_ptr(), L.col_ptr.data_ptr(),
+                               L.row_idx.data_ptr(), L.nnz, w.scale, code, sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_bwd_bsparse")
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tf = tb = 0.0
+    for _ in range(args.steps):
+        ev[0].record(stream)
+        fwd()
+        ev[1].record(stream)
+        bwd()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        tf += ev[0].elapsed_time(ev[1])
+        tb += ev[1].elapsed_time(ev[2])
+    tf /= args.steps
+    tb /= args.steps
+    fl = 4.0 * w.B * w.Hq * w.d * block_pairs(mask, w.N)
+    fwd_tf = fl / (tf * 1e-3) / 1e12
+    fb_tf = 3.5 * fl / ((tf + tb) * 1e-3) / 1e12
+    return {"workload": args.bsparse_workload, "blocks_on": L.nnz, "density": round(L.nnz / mask.size, 4),
+            "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4), "fwd_bwd_ms": round(tf + tb, 4),
+            "fwd_tflops": round(fwd_tf, 1), "fwd_frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+            "fwd_bwd_tflops": round(fb_tf, 1), "fwd_bwd_frac_peak": round(fb_tf / PEAK_BF16_TFLOPS, 4),
+            "note": "256-block mask; credited 4 d flops per pair in an on block forward, 2.5x backward"}
+
+
 def decode_bytes(dw):
     """Bytes a decode step must move: the K and V cache once, Q in, O and LSE out."""
     return 2 * dw.B * dw.Hkv * dw.Nk * dw.d * 2 + 2 * dw.B * dw.Hq * dw.Nq * dw.d * 2 + 4 * dw.B * dw.Hq * dw.Nq
@@ -309,6 +372,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode (KV cache) leg")
     ap.add_argument("--no-local", action="store_true", help="skip the sliding-window (local) attention leg")
     ap.add_argument("--local-workload", default="local_bf16_n65536_w4096")
+    ap.add_argument("--no-bsparse", action="store_true", help="skip the block-sparse attention leg")
+    ap.add_argument("--bsparse-workload", default="bsparse_bf16_n16384")
     ap.add_argument("--decode-workload", default="decode_gqa_bf16_n16384")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (calibrates HBM byte counters)")
@@ -454,6 +519,12 @@ def main():
         log("local {}: fwd {} ms ({} TFLOP/s), fwd+bwd {} ms ({} TFLOP/s)".format(
             result["local"]["workload"], result["local"]["fwd_ms"], result["local"]["fwd_tflops"],
             result["local"]["fwd_bwd_ms"], result["local"]["fwd_bwd_tflops"]))
+
+    if not args.no_bsparse:
+        result["bsparse"] = bsparse_leg(torch, fa, I, dev, stream, args)
+        log("block-sparse {} ({} blocks on): fwd {} ms ({} TFLOP/s), fwd+bwd {} ms ({} TFLOP/s)".format(
+            result["bsparse"]["workload"], result["bsparse"]["blocks_on"], result["bsparse"]["fwd_ms"],
+            result["bsparse"]["fwd_tflops"], result["bsparse"]["fwd_bwd_ms"], result["bsparse"]["fwd_bwd_tflops"]))
 
     if not args.no_decode:
         result["decode"] = decode_leg(torch, fa, I, dev, stream, args)

@@ -184,6 +184,50 @@ fa_status_t fa_bwd_local(const void* q, const void* k, const void* v, const void
     return launch_status(e);
 }
 
+// Mask arrays of the block-sparse entry points (device int arrays).
+static fa_status_t check_bsparse(int N, const int* ptr, const int* idx, int nnz) {
+    const int64_t nb = ((int64_t)N + FA_BSPARSE_BLOCK - 1) / FA_BSPARSE_BLOCK;
+    if (nnz < 0 || nnz > nb * nb) return FA_ERR_SHAPE;
+    if (!ptr || (nnz > 0 && !idx)) return FA_ERR_NULL;
+    if (!aligned(ptr, 4) || (idx && !aligned(idx, 4))) return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+fa_status_t fa_fwd_bsparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                           int Hkv, int N, int d, int causal, const int* row_ptr, const int* col_idx, int nnz,
+                           float softmax_scale, int dtype, hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    s = check_bsparse(N, row_ptr, col_idx, nnz);
+    if (s != FA_OK) return s;
+    s = check_ptrs({q, k, v}, {}, {o}, {lse});
+    if (s != FA_OK) return s;
+    return launch_status(fa::launch_fwd_bf16_bsparse(d, causal, q, k, v, o, lse, B, Hq, Hkv, N, row_ptr, col_idx,
+                                                     nnz, softmax_scale, stream));
+}
+
+fa_status_t fa_bwd_bsparse(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                           const float* lse, void* dq, void* dk, void* dv, float* delta_ws, int B, int Hq, int Hkv,
+                           int N, int d, int causal, const int* row_ptr, const int* col_idx, const int* col_ptr,
+                           const int* row_idx, int nnz, float softmax_scale, int dtype, hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    s = check_bsparse(N, row_ptr, col_idx, nnz);
+    if (s == FA_OK) s = check_bsparse(N, col_ptr, row_idx, nnz);
+    if (s != FA_OK) return s;
+    s = check_ptrs({q, k, v, o, dO, delta_ws}, {lse}, {dq, dk, dv}, {});
+    if (s != FA_OK) return s;
+    hipError_t e = fa::launch_bwd_delta(dtype, d, o, dO, lse, delta_ws, B, Hq, N, stream);
+    if (e == hipSuccess)
+        e = fa::launch_bwd_bf16_bsparse(d, causal, q, k, v, dO, delta_ws, dq, dk, dv, B, Hq, Hkv, N, row_ptr,
+                                        col_idx, col_ptr, row_idx, nnz, softmax_scale, stream);
+    return launch_status(e);
+}
+
 // Shape checks of the decode entry points; sets *empty for an empty problem.
 static fa_status_t check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                                 bool* empty) {

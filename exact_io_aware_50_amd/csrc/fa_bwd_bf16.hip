@@ -73,12 +73,16 @@ __device__ __forceinline__ void sched_dkdv_phase() {
 // query i iff j <= i and (i - W < j or j < S); a key block's steps end at the
 // last query block that sees one of its keys (every later one when the block
 // holds global tokens).
-template <int D, bool CAUSAL, bool LOCAL = false>
+// BSP: block-sparse, key block kbk is seen by the query blocks bidx[bptr[kbk]
+// .. bptr[kbk+1]) (ascending, BNK rows each, BNK / BMQ steps per block; the
+// mask's column layout), clamped so that any layout stays in bounds.
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
 __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int n_rows, int Npad, float c2,
-    float scale, int W = 0, int S = 0) {
+    float scale, int W, int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz) {
+    static_assert(!(LOCAL && BSP), "one sparsity pattern at a time");
     using Cfg = KVBf16Cfg<D>;
     using QT = typename Cfg::QT;
     constexpr int NW = Cfg::kWaves, BNK = Cfg::BNK, BMQ = Cfg::BMQ, QB = Cfg::QB, NS = Cfg::kStages;
@@ -117,10 +121,25 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         const uint16_t* Vg = V + ((int64_t)b * Hkv + g) * N * D;
 
         const int nqt = (N + BMQ - 1) / BMQ;
-        const int qt0 = CAUSAL ? k0 / BMQ : 0;          // earlier query blocks see none of these keys
+        const int qt0 = CAUSAL && !BSP ? k0 / BMQ : 0;  // earlier query blocks see none of these keys
         // (local) later query blocks than qt1 - 1 see none of them either
         const int qt1 = LOCAL && k0 >= S ? min(nqt, (min(N, k0 + BNK) - 2 + W) / BMQ + 1) : nqt;
-        const int total = G * (qt1 - qt0);              // steps: (head g*G + i / (qt1-qt0), block qt0 + i % (qt1-qt0))
+        // (block-sparse) the listed row blocks bbeg .. bbeg+bcnt-1, SPB steps
+        // each (fewer for a last block that ends past N): nsh steps per head
+        constexpr int SPB = BNK / BMQ;
+        int bbeg = 0, nsh = 0;
+        if constexpr (BSP) {
+            bbeg = min(max(bptr[kbk], 0), nnz);
+            const int bcnt = min(max(bptr[kbk + 1], bbeg), nnz) - bbeg;
+            if (bcnt) nsh = SPB * (bcnt - 1) + min(SPB, nqt - min(max(bidx[bbeg + bcnt - 1], 0), nkb - 1) * SPB);
+        }
+        // query block (of BMQ rows) of a head's j-th step
+        auto qblk = [&](int j) __attribute__((always_inline)) {
+            return min(min(max(bidx[bbeg + j / SPB], 0), nkb - 1) * SPB + j % SPB, nqt - 1);
+        };
+        // steps: (head g*G + i / (qt1-qt0), block qt0 + i % (qt1-qt0)); block-sparse:
+        // (head g*G + i / nsh, block qblk(i % nsh))
+        const int total = BSP ? G * nsh : G * (qt1 - qt0);
 
         // ---- direct loads of step u, issued in step order.  The next step's
         // rows are kept as running element offsets: one for Q and dO (the two
@@ -135,6 +154,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         int64_t so = bg0 * Npad + qt0 * BMQ;
         int qrem = N - qt0 * BMQ;                       // rows from the next step's first row to the head's end
         int bq = qt0;                                   // (local) query block of the next step
+        int ji = 0, hi = 0;                             // (block-sparse) step and head of the next issue
         // statistics: chunk c < BMQ/4 of a stage holds LSE*log2e rows 4c.., the
         // rest -D rows; chunk c is loaded by wave c / kStatPerWave, so the first
         // half of the waves loads LSE rows and the second half -D rows
@@ -142,6 +162,16 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         int u_next = 0;
         auto issue = [&](int u) __attribute__((always_inline)) {
             const uint32_t st = lds_addr(smem + (u % NS) * Cfg::kStageBytes);
+            if constexpr (BSP) {
+                const int qb = qblk(ji);
+                qo = ((bg0 + hi) * N + (int64_t)qb * BMQ) * D;
+                so = (bg0 + hi) * Npad + qb * BMQ;
+                qrem = N - qb * BMQ;
+                if (++ji == nsh) {
+                    ji = 0;
+                    ++hi;
+                }
+            }
             int ln = lane;
             asm volatile("" : "+v"(ln));
 #pragma unroll
@@ -153,14 +183,16 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
                 dma16s(dO + qo, off, st + QT::kBytes + (i * NW + wave) * QT::RGS);
             }
             if (ln < Cfg::kStatPerWave) dma16s(Sw + so, 16u * (uint32_t)ln, st + 2 * QT::kBytes + 16 * wave * Cfg::kStatPerWave);
-            qo += BMQ * D;
-            so += BMQ;
-            qrem -= BMQ;
-            if (LOCAL ? ++bq == qt1 : qrem <= 0) {     // past the head's last block: the next head, block qt0
-                qo += ((int64_t)N - (qt1 - qt0) * BMQ) * D;
-                so += Npad - (qt1 - qt0) * BMQ;
-                qrem = N - qt0 * BMQ;
-                if (LOCAL) bq = qt0;
+            if constexpr (!BSP) {
+                qo += BMQ * D;
+                so += BMQ;
+                qrem -= BMQ;
+                if (LOCAL ? ++bq == qt1 : qrem <= 0) {     // past the head's last block: the next head, block qt0
+                    qo += ((int64_t)N - (qt1 - qt0) * BMQ) * D;
+                    so += Npad - (qt1 - qt0) * BMQ;
+                    qrem = N - qt0 * BMQ;
+                    if (LOCAL) bq = qt0;
+                }
             }
         };
         VT::load(Vg + (int64_t)k0 * D, N - k0, Vl, wave, lane);
@@ -249,7 +281,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         // steps are both such blocks is void and skipped (the slot takes as
         // long, but the matrix cores spend no power on it)
         int gb = qt0;
-        const int nd = CAUSAL ? 32 * wave / BMQ : 0;
+        const int nd = CAUSAL && !BSP ? 32 * wave / BMQ : 0;
         auto gemm = [&](int i) __attribute__((always_inline)) {
             if (++gb == qt1) gb = qt0;
             if (gb > qt0 && gb - qt0 < nd) return;
@@ -264,7 +296,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         // X(i): step i's query block is xq.  `mid` (the phase's loads) is
         // issued after the first query block's exponentials, whose results it
         // waits for
-        int xq = qt0;
+        int xq = qt0, jx = 0;
         auto softmax = [&](int i, auto&& mid) __attribute__((always_inline)) {
             if (i >= total) {
                 mid();
@@ -272,8 +304,14 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
                 for (int qb = 0; qb < QB; ++qb) pb[qb][0] = pb[qb][1] = sb[qb][0] = sb[qb][1] = u32x4{};
                 return;
             }
-            const int q0 = xq * BMQ;
-            if (++xq == qt1) xq = qt0;
+            int q0;
+            if constexpr (BSP) {
+                q0 = qblk(jx) * BMQ;
+                if (++jx == nsh) jx = 0;
+            } else {
+                q0 = xq * BMQ;
+                if (++xq == qt1) xq = qt0;
+            }
             const float* sl = (const float*)(smem + (i % NS) * Cfg::kStageBytes + 2 * QT::kBytes);
             // causal: key krow is hidden from query q0 + 32*qb + row(r) iff
             // delta > 8*(r/4) + r%4, delta = krow - q0 - 32*qb - 4*hh; steps whose
@@ -450,12 +488,15 @@ __device__ __forceinline__ void sched_dq_phase() {
 // query i iff j <= i and (i - W < j or j < S); a query block's key tiles are
 // the ns tiles holding global tokens left of its window, then the tiles from
 // the first one its first row can see.
-template <int D, bool CAUSAL, bool LOCAL = false>
+// BSP: block-sparse, row block mb sees the key blocks bidx[bptr[mb] ..
+// bptr[mb+1]) (ascending, BM keys each), clamped as in the forward.
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
 __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
-    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int n_rows, int Npad, float c2, float scale, int W = 0,
-    int S = 0) {
+    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int n_rows, int Npad, float c2, float scale, int W,
+    int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz) {
+    static_assert(!(LOCAL && BSP), "one sparsity pattern at a time");
     using Cfg = QBf16Cfg<D>;
     using KT = typename Cfg::KT;
     constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BNK = Cfg::BNK, NS = Cfg::kStages, KB = BNK / 32;
@@ -491,9 +532,20 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
         const int kend = CAUSAL ? min(N, q0 + BM) : N;
         const int ts = LOCAL ? max(0, q0 - W + 1) / BNK : 0;   // first window key tile
         const int ns = LOCAL ? min((S + BNK - 1) / BNK, ts) : 0;  // global-token tiles before it
-        auto tile_of = [&](int t) __attribute__((always_inline)) { return LOCAL ? (t < ns ? t : t - ns + ts) : t; };
-        const int ntiles = ns + (kend + BNK - 1) / BNK - ts;
-        const int ntw = qw >= N ? 0 : CAUSAL ? ns + (min(N, qw + 32) + BNK - 1) / BNK - ts : ntiles;
+        constexpr int TPB = BM / BNK;               // key tiles per mask block
+        const int ntk = (N + BNK - 1) / BNK;
+        int bbeg = 0, bcnt = 0;
+        if constexpr (BSP) {
+            bbeg = min(max(bptr[mb], 0), nnz);
+            bcnt = min(max(bptr[mb + 1], bbeg), nnz) - bbeg;
+        }
+        auto bcol = [&](int e) __attribute__((always_inline)) { return min(max(bidx[bbeg + e], 0), nmb - 1); };
+        auto tile_of = [&](int t) __attribute__((always_inline)) {
+            return BSP ? min(bcol(t / TPB) * TPB + t % TPB, ntk - 1) : LOCAL ? (t < ns ? t : t - ns + ts) : t;
+        };
+        const int ntiles = BSP ? (bcnt ? TPB * (bcnt - 1) + min(TPB, ntk - bcol(bcnt - 1) * TPB) : 0)
+                               : ns + (kend + BNK - 1) / BNK - ts;
+        const int ntw = qw >= N ? 0 : CAUSAL && !BSP ? ns + (min(N, qw + 32) + BNK - 1) / BNK - ts : ntiles;
 
         // direct loads of tile t; the per-lane offsets are recomputed at every
         // issue from an opaque copy of the lane index (kept live across the
@@ -690,35 +742,38 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     }
 }
 
-template <int D, bool CAUSAL, bool LOCAL = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
 static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* ws,
                               void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, hipStream_t st,
-                              int W = 0, int S = 0) {
+                              int W = 0, int S = 0, const int* bptr = nullptr, const int* bidx = nullptr,
+                              int nnz = 0) {
     using Cfg = KVBf16Cfg<D>;
     const int nkb = (N + Cfg::BNK - 1) / Cfg::BNK;
     const int Np = ws_rows(N);
     static std::atomic<int> slots{0};
-    const int grid =
-        persistent_grid((const void*)bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL>, Cfg::kThreads, nkb * Hkv * B, slots);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
+    const int grid = persistent_grid((const void*)bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP>, Cfg::kThreads,
+                                     nkb * Hkv * B, slots);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0,
+                       st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
                        ws + (int64_t)B * Hq * Np, (uint16_t*)dk, (uint16_t*)dv, B, Hq, Hkv, N, Np, scale * kLog2e,
-                       scale, W, S);
+                       scale, W, S, bptr, bidx, nnz);
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool LOCAL = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
 static hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dq,
-                            int B, int Hq, int Hkv, int N, float scale, hipStream_t st, int W = 0, int S = 0) {
+                            int B, int Hq, int Hkv, int N, float scale, hipStream_t st, int W = 0, int S = 0,
+                            const int* bptr = nullptr, const int* bidx = nullptr, int nnz = 0) {
     using Cfg = QBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
     const int Np = ws_rows(N);
     static std::atomic<int> slots{0};
     const int grid =
-        persistent_grid((const void*)bwd_dq_bf16_kernel<D, CAUSAL, LOCAL>, Cfg::kThreads, nmb * Hq * B, slots);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, LOCAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
-                       ws + (int64_t)B * Hq * Np, (uint16_t*)dq, B, Hq, Hkv, N, Np, scale * kLog2e, scale, W, S);
+        persistent_grid((const void*)bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP>, Cfg::kThreads, nmb * Hq * B, slots);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0,
+                       st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
+                       ws + (int64_t)B * Hq * Np, (uint16_t*)dq, B, Hq, Hkv, N, Np, scale * kLog2e, scale, W, S,
+                       bptr, bidx, nnz);
     return hipGetLastError();
 }
 
@@ -747,6 +802,22 @@ hipError_t launch_bwd_dkdv_bf16_local(int d, const void* q, const void* k, const
     if (d == 64) return launch_dkdv<64, true, true>(q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st, W, S);
     if (d == 128) return launch_dkdv<128, true, true>(q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st, W, S);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_bf16_bsparse(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
+                                   const float* ws, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                                   const int* row_ptr, const int* col_idx, const int* col_ptr, const int* row_idx,
+                                   int nnz, float scale, hipStream_t st) {
+#define KV q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st, 0, 0, col_ptr, row_idx, nnz
+#define QA q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st, 0, 0, row_ptr, col_idx, nnz
+    hipError_t e = hipErrorInvalidValue;
+    if (d == 64) e = causal ? launch_dkdv<64, true, false, true>(KV) : launch_dkdv<64, false, false, true>(KV);
+    if (d == 128) e = causal ? launch_dkdv<128, true, false, true>(KV) : launch_dkdv<128, false, false, true>(KV);
+    if (e != hipSuccess) return e;
+    if (d == 64) return causal ? launch_dq<64, true, false, true>(QA) : launch_dq<64, false, false, true>(QA);
+    return causal ? launch_dq<128, true, false, true>(QA) : launch_dq<128, false, false, true>(QA);
+#undef KV
+#undef QA
 }
 
 hipError_t launch_bwd_dq_bf16_local(int d, const void* q, const void* k, const void* v, const void* dO,

@@ -81,11 +81,19 @@ __device__ __forceinline__ void sched_gemm_phase() {
 // tiles are the ns tiles holding global tokens left of its window, then the
 // tiles from ts, the first one holding a key its first query row can see;
 // other keys left of a row's window are masked like those past the diagonal.
-template <int D, bool CAUSAL, bool LOCAL = false>
+//
+// BSP: block-sparse attention (same glossary entry: a mask over BM x BM blocks
+// of the score matrix, the blocks that are off never computed).  Row block mb
+// sees the key blocks bidx[bptr[mb] .. bptr[mb+1]), ascending, BM / BN tiles
+// each; with CAUSAL the keys past the diagonal are masked as well.  Offsets are
+// clamped to [0, nnz) and block indices to the block count, so any layout keeps
+// every access in bounds.  A row that sees no key gets O = 0 and LSE = -inf.
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
 __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int N, float c2, int W = 0,
-    int S = 0) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int N, float c2, int W,
+    int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz) {
+    static_assert(!(LOCAL && BSP), "one sparsity pattern at a time");
     using Cfg = FwdBf16Cfg<D>;
     using KT = typename Cfg::KT;
     constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::kStages, KB = BN / 32;
@@ -116,10 +124,23 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
         const int kend = CAUSAL ? min(N, q0 + BM) : N;
         const int ts = LOCAL ? max(0, q0 - W + 1) / BN : 0;   // first window tile of the workgroup
         const int ns = LOCAL ? min((S + BN - 1) / BN, ts) : 0;    // global-token tiles before it
-        // the workgroup's t-th tile: tiles 0 .. ns-1, then ts, ts+1, ...
-        auto tile_of = [&](int t) __attribute__((always_inline)) { return LOCAL ? (t < ns ? t : t - ns + ts) : t; };
-        const int ntiles = ns + (kend + BN - 1) / BN - ts;    // tiles of the workgroup
-        const int ntw = qw >= N ? 0 : CAUSAL ? ns + (min(N, qw + 32) + BN - 1) / BN - ts : ntiles;   // tiles of this wave
+        // (block-sparse) the row block's entries bbeg .. bbeg+bcnt-1
+        constexpr int TPB = BM / BN;                      // tiles per mask block
+        const int ntk = (N + BN - 1) / BN;
+        int bbeg = 0, bcnt = 0;
+        if constexpr (BSP) {
+            bbeg = min(max(bptr[mb], 0), nnz);
+            bcnt = min(max(bptr[mb + 1], bbeg), nnz) - bbeg;
+        }
+        auto bcol = [&](int e) __attribute__((always_inline)) { return min(max(bidx[bbeg + e], 0), nmb - 1); };
+        // the workgroup's t-th tile: tiles 0 .. ns-1, then ts, ts+1, ... (local);
+        // tile t % TPB of the (t / TPB)-th listed block (block-sparse)
+        auto tile_of = [&](int t) __attribute__((always_inline)) {
+            return BSP ? min(bcol(t / TPB) * TPB + t % TPB, ntk - 1) : LOCAL ? (t < ns ? t : t - ns + ts) : t;
+        };
+        const int ntiles = BSP ? (bcnt ? TPB * (bcnt - 1) + min(TPB, ntk - bcol(bcnt - 1) * TPB) : 0)
+                               : ns + (kend + BN - 1) / BN - ts;    // tiles of the workgroup
+        const int ntw = qw >= N ? 0 : CAUSAL && !BSP ? ns + (min(N, qw + 32) + BN - 1) / BN - ts : ntiles;   // tiles of this wave
 
         // ---- direct loads: this wave's row groups of a K/V tile, as byte offsets
         // from the tile's first row (rows past the end re-read the last row)
@@ -329,7 +350,7 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
         // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
         const float ltot = pair_sum(lsum);
         if (qrow < N) {
-            const float inv = 1.0f / ltot;
+            const float inv = BSP && !(ltot > 0.f) ? 0.f : 1.0f / ltot;   // (block-sparse) a row with no key: O = 0
             uint16_t* Orow = O + (((int64_t)b * Hq + h) * N + qrow) * D;
 #pragma unroll
             for (int ct = 0; ct < D / 32; ++ct)
@@ -340,22 +361,24 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
                     w[1] = pack_bf16x2(oacc[ct][4 * gq + 2] * inv, oacc[ct][4 * gq + 3] * inv);
                     *reinterpret_cast<u32x2*>(Orow + 32 * ct + 8 * gq + 4 * hh) = w;
                 }
-            if (hh == 0) LSE[((int64_t)b * Hq + h) * N + qrow] = (m + log2f(ltot)) * kLn2;
+            if (hh == 0)
+                LSE[((int64_t)b * Hq + h) * N + qrow] = BSP && !(ltot > 0.f) ? -INFINITY : (m + log2f(ltot)) * kLn2;
         }
     }
 }
 
-template <int D, bool CAUSAL, bool LOCAL = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
 static hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                         int N, float scale, hipStream_t st, int W = 0, int S = 0) {
+                         int N, float scale, hipStream_t st, int W = 0, int S = 0, const int* bptr = nullptr,
+                         const int* bidx = nullptr, int nnz = 0) {
     using Cfg = FwdBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
     static std::atomic<int> slots{0};
     const int grid =
-        persistent_grid((const void*)fwd_bf16_kernel<D, CAUSAL, LOCAL>, Cfg::kThreads, nmb * Hq * B, slots);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, LOCAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
+        persistent_grid((const void*)fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP>, Cfg::kThreads, nmb * Hq * B, slots);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, B, Hq, Hkv, N,
-                       scale * kLog2e, W, S);
+                       scale * kLog2e, W, S, bptr, bidx, nnz);
     return hipGetLastError();
 }
 
@@ -372,6 +395,16 @@ hipError_t launch_fwd_bf16_local(int d, const void* q, const void* k, const void
                                  int Hq, int Hkv, int N, int W, int S, float scale, hipStream_t st) {
     if (d == 64) return launch<64, true, true>(q, k, v, o, lse, B, Hq, Hkv, N, scale, st, W, S);
     if (d == 128) return launch<128, true, true>(q, k, v, o, lse, B, Hq, Hkv, N, scale, st, W, S);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_bf16_bsparse(int d, int causal, const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int B, int Hq, int Hkv, int N, const int* row_ptr,
+                                   const int* col_idx, int nnz, float scale, hipStream_t st) {
+#define ARGS q, k, v, o, lse, B, Hq, Hkv, N, scale, st, 0, 0, row_ptr, col_idx, nnz
+    if (d == 64) return causal ? launch<64, true, false, true>(ARGS) : launch<64, false, false, true>(ARGS);
+    if (d == 128) return causal ? launch<128, true, false, true>(ARGS) : launch<128, false, false, true>(ARGS);
+#undef ARGS
     return hipErrorInvalidValue;
 }
 

@@ -74,6 +74,17 @@ hipError_t launch_bwd_dq_bf16_local(int d, const void* q, const void* k, const v
                                     const float* ws, void* dq, int B, int Hq, int Hkv, int N, int W, int S,
                                     float scale, hipStream_t st);
 
+// Block-sparse attention, bf16: key j visible to query i iff block
+// (i / 256, j / 256) is on (and j <= i with causal).  The forward and dQ read
+// the mask by rows (row_ptr / col_idx), dK / dV by columns (col_ptr / row_idx).
+hipError_t launch_fwd_bf16_bsparse(int d, int causal, const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int B, int Hq, int Hkv, int N, const int* row_ptr,
+                                   const int* col_idx, int nnz, float scale, hipStream_t st);
+hipError_t launch_bwd_bf16_bsparse(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
+                                   const float* ws, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                                   const int* row_ptr, const int* col_idx, const int* col_ptr, const int* row_idx,
+                                   int nnz, float scale, hipStream_t st);
+
 hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
 
 // Decode split over the keys: nrb blocks of 32 packed query rows per K/V head,

@@ -47,6 +47,10 @@ _lib.fa_fwd_local.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f
 _lib.fa_fwd_local.restype = _i
 _lib.fa_bwd_local.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_bwd_local.restype = _i
+_lib.fa_fwd_bsparse.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _i, _f, _i, _p]
+_lib.fa_fwd_bsparse.restype = _i
+_lib.fa_bwd_bsparse.argtypes = ([_p] * 10 + [_i] * 6 + [_p] * 4 + [_i, _f, _i, _p])
+_lib.fa_bwd_bsparse.restype = _i
 _lib.fa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_decode.restype = _i
 _lib.fa_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
@@ -61,8 +65,9 @@ _lib.fa_abi_version.argtypes = []
 _lib.fa_abi_version.restype = _i
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
-           "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_decode", "fa_decode_workspace_bytes",
-           "fa_decode_paged", "fa_decode_paged_workspace_bytes", "fa_status_string", "fa_abi_version")
+           "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_decode",
+           "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes", "fa_status_string",
+           "fa_abi_version")
 
 
 class FAError(RuntimeError):
@@ -214,6 +219,88 @@ def bwd(q, k, v, o, do, lse, causal: bool, scale: float, stream=None, workspace=
     _check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, d, causal,
                   scale, code, _stream_handle(stream)), "fa_bwd")
+    return dq, dk, dv, workspace
+
+
+def fa_fwd_bsparse(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, row_ptr, col_idx, nnz, softmax_scale, dtype,
+                   stream) -> int:
+    return _lib.fa_fwd_bsparse(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, row_ptr, col_idx, nnz,
+                               float(softmax_scale), dtype, stream)
+
+
+def fa_bwd_bsparse(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal, row_ptr, col_idx, col_ptr,
+                   row_idx, nnz, softmax_scale, dtype, stream) -> int:
+    return _lib.fa_bwd_bsparse(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal, row_ptr,
+                               col_idx, col_ptr, row_idx, nnz, float(softmax_scale), dtype, stream)
+
+
+BSPARSE_BLOCK = 256   # side of a mask block (FA_BSPARSE_BLOCK)
+
+
+class BlockSparseLayout:
+    """A block mask [nb, nb] (nb = ceil(N / 256)) as the two int32 layouts the kernels read.
+
+    ``row_ptr``/``col_idx``: the blocks that are on, row by row (columns ascending);
+    ``col_ptr``/``row_idx``: the same blocks column by column.  With ``causal``
+    the blocks above the diagonal are dropped (their keys are masked anyway)."""
+
+    def __init__(self, mask, causal: bool = False, device=None):
+        torch = _torch()
+        m = torch.as_tensor(mask, dtype=torch.bool).cpu()
+        if m.dim() != 2 or m.shape[0] != m.shape[1]:
+            raise ValueError("the block mask must be square [nb, nb]")
+        if causal:
+            m = torch.tril(m)
+        self.mask, self.nb = m, m.shape[0]
+        rows = m.to(torch.int32)
+        self.nnz = int(rows.sum())
+        cnt_r, cnt_c = rows.sum(1), rows.sum(0)
+        zero = torch.zeros(1, dtype=torch.int64)
+        rp = torch.cat([zero, torch.cumsum(cnt_r, 0)]).to(torch.int32)
+        cp = torch.cat([zero, torch.cumsum(cnt_c, 0)]).to(torch.int32)
+        ci = torch.nonzero(m, as_tuple=False)[:, 1].to(torch.int32)           # row-major: columns ascending per row
+        ri = torch.nonzero(m.t().contiguous(), as_tuple=False)[:, 1].to(torch.int32)
+        pad = lambda t: t if t.numel() else torch.zeros(1, dtype=torch.int32)
+        self.row_ptr, self.col_ptr = rp.to(device), cp.to(device)
+        self.col_idx, self.row_idx = pad(ci).to(device), pad(ri).to(device)
+
+
+def _layout(layout, N, q):
+    nb = (N + BSPARSE_BLOCK - 1) // BSPARSE_BLOCK
+    if layout.nb != nb:
+        raise ValueError(f"the block mask is {layout.nb} blocks per side, N = {N} needs {nb}")
+    if layout.row_ptr.device != q.device:
+        raise ValueError("the block-sparse layout must be on the tensors' device")
+
+
+def fwd_bsparse(q, k, v, layout: BlockSparseLayout, causal: bool, scale: float, stream=None):
+    """(o, lse) of block-sparse attention, bf16: key j is visible to query i iff
+    ``layout.mask[i // 256, j // 256]`` (and j <= i with ``causal``)."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    _layout(layout, N, q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_bsparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
+                          int(causal), layout.row_ptr.data_ptr(), layout.col_idx.data_ptr(), layout.nnz, scale,
+                          _dtype_code(q), _stream_handle(stream)), "fa_fwd_bsparse")
+    return o, lse
+
+
+def bwd_bsparse(q, k, v, o, do, lse, layout: BlockSparseLayout, causal: bool, scale: float, stream=None,
+                workspace=None):
+    """(dq, dk, dv, workspace) of block-sparse attention (the mask of ``fwd_bsparse``)."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    _layout(layout, N, q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_bytes(B, Hq, N) // 4, dtype=torch.float32, device=q.device)
+    _check(fa_bwd_bsparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, d,
+                          int(causal), layout.row_ptr.data_ptr(), layout.col_idx.data_ptr(),
+                          layout.col_ptr.data_ptr(), layout.row_idx.data_ptr(), layout.nnz, scale, _dtype_code(q),
+                          _stream_handle(stream)), "fa_bwd_bsparse")
     return dq, dk, dv, workspace
 
 

@@ -89,6 +89,30 @@ LOCAL_WORKLOADS = {
 }
 
 
+def block_pattern(nb: int, band: int = 1, n_global: int = 0, n_random: int = 2, seed: int = 0) -> np.ndarray:
+    """A [nb, nb] boolean block mask: a band of |r - c| <= band blocks, the first
+    n_global block rows and columns, and n_random seeded random permutations
+    (block (r, perm(r)) on), so that every block row and every block column
+    gets about the same number of blocks."""
+    r = np.arange(nb)
+    m = np.abs(r[:, None] - r[None, :]) <= band
+    m[:n_global, :] = True
+    m[:, :n_global] = True
+    rng = np.random.default_rng(seed)
+    for _ in range(n_random):
+        m[r, rng.permutation(nb)] = True
+    return m
+
+
+# Block-sparse workload: tensors of a Workload and the block mask's parameters.
+BSPARSE_WORKLOADS = {
+    "bsparse_bf16_n16384": (
+        Workload("bsparse_bf16_n16384 (B=1 Hq=32 Hkv=8 N=16384 d=128, non-causal, 256-blocks: 3-block band "
+                 "and 2 random permutations, bf16)", 8, 1, 32, 8, 16384, 128, False, "bf16"),
+        dict(band=1, n_global=0, n_random=2, seed=8)),
+}
+
+
 def decode_tensor(w: DecodeWorkload, tensor_id: int, device="cpu"):
     """Q ([B, Hq, Nq, d]) or the K / V cache ([B, Hkv, Nk, d]) of a decode workload, bf16."""
     import torch

@@ -191,6 +191,49 @@ fa_status_t fa_bwd_local(const void* q, const void* k, const void* v,
                          hipStream_t stream);
 
 /*
+ * Block-sparse attention: key j is visible to query i iff block
+ * (i / FA_BSPARSE_BLOCK, j / FA_BSPARSE_BLOCK) of the mask is on (and, with
+ * causal = 1, j <= i).  The FlashAttention legal glossary, entry
+ * "Block-sparse": a mask over the blocks of the attention matrix says which
+ * blocks are computed; the blocks that are off are skipped whole.  Same
+ * arguments, layouts and outputs as fa_fwd / fa_bwd plus the mask, one
+ * pattern for every batch entry and head, in device memory (the library
+ * neither copies nor frees it):
+ *   nb      = ceil(N / FA_BSPARSE_BLOCK) blocks per side
+ *   row_ptr : int[nb + 1], col_idx : int[nnz] — the blocks that are on, by
+ *             rows: row block r sees the key blocks col_idx[row_ptr[r] ..
+ *             row_ptr[r+1]), strictly ascending (compressed sparse rows)
+ *   col_ptr : int[nb + 1], row_idx : int[nnz] — the same mask by columns
+ *             (the backward's dK / dV pass reads it that way)
+ * A query row that sees no key gets O = 0 and LSE = -inf, and contributes
+ * nothing to the gradients; a key seen by no row gets dK = dV = 0.  With
+ * causal = 1, blocks above the diagonal may be listed (their keys are masked)
+ * but cost time.  The kernels clamp every offset and block index to the
+ * arrays, so a malformed layout reads nothing out of bounds, but its results
+ * are unspecified.  bf16 only, d in {64, 128}.  Errors: FA_ERR_SHAPE for
+ * nnz < 0 or nnz > nb * nb, FA_ERR_NULL for a null row_ptr / col_ptr or a
+ * null index array with nnz > 0, FA_ERR_ALIGN for a misaligned mask array,
+ * others as fa_fwd / fa_bwd.  The backward reads
+ * the LSE of fa_fwd_bsparse with the same mask.
+ */
+#define FA_BSPARSE_BLOCK 256
+
+fa_status_t fa_fwd_bsparse(const void* q, const void* k, const void* v,
+                           void* o, float* lse,
+                           int B, int Hq, int Hkv, int N, int d, int causal,
+                           const int* row_ptr, const int* col_idx, int nnz,
+                           float softmax_scale, int dtype, hipStream_t stream);
+
+fa_status_t fa_bwd_bsparse(const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse,
+                           void* dq, void* dk, void* dv,
+                           float* delta_ws,
+                           int B, int Hq, int Hkv, int N, int d, int causal,
+                           const int* row_ptr, const int* col_idx,
+                           const int* col_ptr, const int* row_idx, int nnz,
+                           float softmax_scale, int dtype, hipStream_t stream);
+
+/*
  * Decode: attention of Nq new query rows against a key/value cache of Nk
  * rows.  "Paper digest: FlashAttention", section "Limits" (decode-time
  * attention reads a large KV cache for few queries); self-hosted LLM
