@@ -104,6 +104,29 @@ def test_bsparse_small_shapes(fa, dev, shape):
     check(f64(o), f64(lse), [f64(x) for x in (dq, dk, dv)], O, L, [rq, rk, rv], str(shape))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bsparse_dilated_block_window(fa, dev, d):
+    """A dilated causal window at block granularity: row block r sees key blocks r, r-2, r-4, r-6 (and within
+    the diagonal block only keys j <= i)."""
+    B, Hq, Hkv, N = 1, 4, 2, 2000
+    nb = (N + BS - 1) // BS
+    r = np.arange(nb)
+    off = r[:, None] - r[None, :]
+    mask = (off >= 0) & (off < 8) & (off % 2 == 0)
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, do = (I.random_tensor(93 + d, (B, H, N, d), "bf16", tensor_id=t) for t, H in enumerate((Hq, Hkv, Hkv, Hq)))
+    layout = fa.BlockSparseLayout(mask, causal=True, device=dev)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.fwd_bsparse(qd, kd, vd, layout, True, scale)
+    dq, dk, dv, _ = fa.bwd_bsparse(qd, kd, vd, o, dod, lse, layout, True, scale)
+    torch.cuda.synchronize()
+    Q, K, V, dO = (f64(t) for t in (q, k, v, do))
+    bm = oracle.BlockMask(mask, BS)
+    O, L = oracle.forward(Q, K, V, True, scale, window=bm)
+    rq, rk, rv, _ = oracle.backward(Q, K, V, dO, True, scale, window=bm)
+    check(f64(o), f64(lse), [f64(x) for x in (dq, dk, dv)], O, L, [rq, rk, rv], f"dilated d={d}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bsparse_full_mask_is_dense(fa, dev, causal):
     """Every block on: the same tiles in the same order as the dense kernels, bit for bit."""
