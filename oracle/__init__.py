@@ -20,6 +20,10 @@ Pages cited throughout (by title and section):
               opening paragraphs; entries "Grouped-Query Attention (GQA)",
               "KV Cache" and "PagedAttention".
 
+Dropout (``dropout.py``) also follows a published definition outside the
+pages: the Philox4x32-10 counter-based generator of Salmon et al. (SC 2011),
+pinned to that generator's published known-answer vectors.
+
 Parity pins: every function here is pinned by a ``-m "not gpu"`` test against
 closed forms, invariants, finite differences, a library routine (torch CPU
 float64 scaled_dot_product_attention) or the pages' printed memory arithmetic.
@@ -40,3 +44,10 @@ from .attention import (  # noqa: F401
     attention_matrix_bytes,
 )
 from .fp8 import e4m3_decode, e4m3_encode_rne_sat, quantize_per_tensor, E4M3_MAX  # noqa: F401
+from .dropout import (  # noqa: F401,E402
+    backward_dropout,
+    drop_threshold,
+    forward_dropout,
+    keep_mask,
+    philox4x32_10,
+)

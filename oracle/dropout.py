@@ -1,0 +1,114 @@
+"""Attention dropout for the float64 oracle: a counter-based mask and the forward and backward through it.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+[FA-LLM], opening paragraphs: the fused kernel does the matrix products,
+masking, softmax and dropout in one program; [Digest], "Limits": dropout is
+one of the features a kernel must handle.  Neither page specifies the random
+numbers, the drop rule or where the rescale goes.  Readings taken here:
+
+- Random numbers: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
+  random numbers: as easy as 1, 2, 3", SC 2011): a 4 x 32-bit counter, a
+  2 x 32-bit key, ten rounds.  Each round multiplies counter words 0 and 2 by
+  0xD2511F53 and 0xCD9E8D57 into 64-bit products and forms the new counter
+  from their high and low halves, the other two words and the key; the key
+  is bumped by the Weyl constants 0x9E3779B9 and 0xBB67AE85 between rounds.
+- The score element (query i, key j) of batch entry b and query head h takes
+  word j mod 4 of Philox(counter = (j div 4, i, b * Hq + h, 0),
+  key = (seed mod 2^32, seed div 2^32)).
+- The element is kept iff that word is >= floor(p * 2^32), so it is dropped
+  with probability floor(p * 2^32) / 2^32 (p itself for any p on a 2^-32 grid).
+- Dropout acts on the normalised probabilities: O = ((Z o P) / (1 - p)) V,
+  Z the keep mask.  The row statistic LSE is that of the undropped softmax,
+  so the backward recomputes P from it as without dropout.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import probabilities
+
+_M0, _M1 = 0xD2511F53, 0xCD9E8D57
+_W0, _W1 = 0x9E3779B9, 0xBB67AE85
+_MASK = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 on arrays: ``ctr`` is four uint32 arrays (broadcastable), ``key`` two; returns four uint32 arrays."""
+    c = [np.asarray(x, dtype=np.uint64) for x in ctr]
+    k0, k1 = (np.asarray(x, dtype=np.uint64) for x in key)
+    c0, c1, c2, c3 = np.broadcast_arrays(*c)
+    for _ in range(10):
+        p0 = np.uint64(_M0) * c0                        # < 2^64: exact in uint64
+        p1 = np.uint64(_M1) * c2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & _MASK
+        hi1, lo1 = p1 >> np.uint64(32), p1 & _MASK
+        c0, c1, c2, c3 = (hi1 ^ c1 ^ k0) & _MASK, lo1, (hi0 ^ c3 ^ k1) & _MASK, lo0
+        k0 = (k0 + np.uint64(_W0)) & _MASK
+        k1 = (k1 + np.uint64(_W1)) & _MASK
+    return [x.astype(np.uint32) for x in (c0, c1, c2, c3)]
+
+
+def drop_threshold(p: float) -> int:
+    """The keep threshold floor(p * 2^32) for a drop probability 0 <= p < 1."""
+    if not 0.0 <= p < 1.0:
+        raise ValueError("the drop probability must be in [0, 1)")
+    return int(np.floor(p * 2.0 ** 32))
+
+
+def keep_mask(b: int, h: int, Hq: int, rows, n_keys: int, p: float, seed: int) -> np.ndarray:
+    """Boolean keep mask Z [len(rows), n_keys] of batch entry b, query head h."""
+    rows = np.asarray(rows, dtype=np.uint64)[:, None]
+    keys = np.arange(n_keys, dtype=np.uint64)[None, :]
+    words = philox4x32_10((keys >> np.uint64(2), rows, np.uint64(b * Hq + h), np.uint64(0)),
+                          (np.uint64(seed & 0xFFFFFFFF), np.uint64(seed >> 32)))
+    sel = (keys & np.uint64(3)).astype(np.int64)
+    w = np.choose(np.broadcast_to(sel, words[0].shape), words)
+    return w >= np.uint32(drop_threshold(p))
+
+
+def forward_dropout(q, k, v, causal, scale, p, seed):
+    """O [B, Hq, N, d] and the (undropped) LSE [B, Hq, N] of attention with dropout on P."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, N, _ = q.shape
+    G = Hq // k.shape[1]
+    O = np.empty((B, Hq, N, v.shape[3]))
+    L = np.empty((B, Hq, N))
+    for b in range(B):
+        for h in range(Hq):
+            _, P, m, l = probabilities(q[b, h], k[b, h // G], scale, causal)
+            Z = keep_mask(b, h, Hq, np.arange(N), k.shape[2], p, seed)
+            O[b, h] = (np.where(Z, P, 0.0) / (1.0 - p)) @ np.asarray(v[b, h // G], dtype=np.float64)
+            L[b, h] = m + np.log(l)
+    return O, L
+
+
+def backward_dropout(q, k, v, do, causal, scale, p, seed):
+    """dQ, dK, dV of O = ((Z o P) / (1 - p)) V for a loss with dL/dO = dO; returns (dq, dk, dv, O).
+
+    The chain rule of that definition, Z fixed by the seed: with Pd = Z o P / (1 - p),
+    dV = Pd^T dO, dPd = dO V^T, dP = Z o dPd / (1 - p), and through the softmax
+    dS = P o (dP - D) with D_i = sum_j P_ij dP_ij = dO_i . O_i; then dQ = scale dS K and
+    dK = scale dS^T Q.  The K/V gradients of a group sum over its query heads."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, N, _ = q.shape
+    G = Hq // k.shape[1]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    O = np.empty((B, Hq, N, v.shape[3]))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            _, P, _, _ = probabilities(q[b, h], k[b, g], scale, causal)
+            Z = keep_mask(b, h, Hq, np.arange(N), k.shape[2], p, seed)
+            Pd = np.where(Z, P, 0.0) / (1.0 - p)
+            O[b, h] = Pd @ v[b, g]
+            dv[b, g] += Pd.T @ do[b, h]
+            dP = np.where(Z, do[b, h] @ v[b, g].T, 0.0) / (1.0 - p)
+            D = np.sum(do[b, h] * O[b, h], axis=1)
+            dS = P * (dP - D[:, None])
+            dq[b, h] = scale * (dS @ k[b, g])
+            dk[b, g] += scale * (dS.T @ q[b, h])
+    return dq, dk, dv, O
