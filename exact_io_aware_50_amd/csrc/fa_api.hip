@@ -184,6 +184,22 @@ fa_status_t fa_bwd_local(const void* q, const void* k, const void* v, const void
     return launch_status(e);
 }
 
+fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                           int N, int d, int causal, float dropout_p, uint64_t seed, float softmax_scale, int dtype,
+                           hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    if (!(dropout_p >= 0.f && dropout_p < 1.f)) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    s = check_ptrs({q, k, v}, {}, {o}, {lse});
+    if (s != FA_OK) return s;
+    const uint32_t thr = (uint32_t)floor((double)dropout_p * 4294967296.0);
+    const float rkeep = (float)(1.0 / (1.0 - (double)dropout_p));
+    return launch_status(fa::launch_fwd_bf16_dropout(d, causal, q, k, v, o, lse, B, Hq, Hkv, N, thr, seed, rkeep,
+                                                     softmax_scale, stream));
+}
+
 // Mask arrays of the block-sparse entry points (device int arrays).
 static fa_status_t check_bsparse(int N, const int* ptr, const int* idx, int nnz) {
     const int64_t nb = ((int64_t)N + FA_BSPARSE_BLOCK - 1) / FA_BSPARSE_BLOCK;

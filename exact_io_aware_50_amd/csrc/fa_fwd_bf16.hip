@@ -88,11 +88,40 @@ __device__ __forceinline__ void sched_gemm_phase() {
 // each; with CAUSAL the keys past the diagonal are masked as well.  Offsets are
 // clamped to [0, nnz) and block indices to the block count, so any layout keeps
 // every access in bounds.  A row that sees no key gets O = 0 and LSE = -inf.
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011): counter c, key
+// (k0, k1); ten rounds of two 32 x 32 -> 64-bit products with the Weyl key
+// schedule.  Returns the four output words in c.
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+        const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+        const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+}
+
+// Dropout parameters: element (query i, key j) of (batch b, query head h) is
+// kept iff word j % 4 of Philox((j / 4, i, b * Hq + h, 0), (key0, key1)) is
+// >= thr; kept probabilities are scaled by rkeep = 1 / (1 - p).
+struct DropArgs {
+    uint32_t thr, key0, key1;
+    float rkeep;
+};
+
+// DROP: attention dropout on the normalised probabilities (the FlashAttention
+// page of the self-hosted LLM glossary: dropout is one of the operations fused
+// into the kernel).  The normaliser and LSE are those of the undropped softmax.
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
 __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int N, float c2, int W,
-    int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz) {
+    int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz, DropArgs drop) {
     static_assert(!(LOCAL && BSP), "one sparsity pattern at a time");
     using Cfg = FwdBf16Cfg<D>;
     using KT = typename Cfg::KT;
@@ -287,6 +316,23 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
                 }
             }
             lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+            if constexpr (DROP) {
+                // lane keys k0 + 32 kb + 8 g + 4 hh + e (e < 4): one Philox call per run of four
+                const uint32_t bhq = (uint32_t)(b * Hq + h);
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        uint32_t c[4] = {(uint32_t)((k0 + 32 * kb + 8 * gq) >> 2) + (uint32_t)hh, (uint32_t)qrow, bhq, 0u};
+                        philox4x32_10(c, drop.key0, drop.key1);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (c[e] < drop.thr) sacc[kb][4 * gq + e] = 0.f;
+                    }
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) pf[kb][t2] = pack_bf16x8(sacc[kb], 8 * t2);
+                }
+            }
             // P is finished inside this phase (not sunk into the next matrix phase)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -350,7 +396,8 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
         // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
         const float ltot = pair_sum(lsum);
         if (qrow < N) {
-            const float inv = BSP && !(ltot > 0.f) ? 0.f : 1.0f / ltot;   // (block-sparse) a row with no key: O = 0
+            float inv = BSP && !(ltot > 0.f) ? 0.f : 1.0f / ltot;   // (block-sparse) a row with no key: O = 0
+            if constexpr (DROP) inv *= drop.rkeep;
             uint16_t* Orow = O + (((int64_t)b * Hq + h) * N + qrow) * D;
 #pragma unroll
             for (int ct = 0; ct < D / 32; ++ct)
@@ -367,18 +414,18 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
     }
 }
 
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
 static hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                          int N, float scale, hipStream_t st, int W = 0, int S = 0, const int* bptr = nullptr,
-                         const int* bidx = nullptr, int nnz = 0) {
+                         const int* bidx = nullptr, int nnz = 0, DropArgs drop = {0u, 0u, 0u, 1.f}) {
     using Cfg = FwdBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
     static std::atomic<int> slots{0};
-    const int grid =
-        persistent_grid((const void*)fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP>, Cfg::kThreads, nmb * Hq * B, slots);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, B, Hq, Hkv, N,
-                       scale * kLog2e, W, S, bptr, bidx, nnz);
+    const int grid = persistent_grid((const void*)fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>, Cfg::kThreads,
+                                     nmb * Hq * B, slots);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0,
+                       st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, B, Hq, Hkv,
+                       N, scale * kLog2e, W, S, bptr, bidx, nnz, drop);
     return hipGetLastError();
 }
 
@@ -404,6 +451,18 @@ hipError_t launch_fwd_bf16_bsparse(int d, int causal, const void* q, const void*
 #define ARGS q, k, v, o, lse, B, Hq, Hkv, N, scale, st, 0, 0, row_ptr, col_idx, nnz
     if (d == 64) return causal ? launch<64, true, false, true>(ARGS) : launch<64, false, false, true>(ARGS);
     if (d == 128) return causal ? launch<128, true, false, true>(ARGS) : launch<128, false, false, true>(ARGS);
+#undef ARGS
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_bf16_dropout(int d, int causal, const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int B, int Hq, int Hkv, int N, uint32_t thr, uint64_t seed, float rkeep,
+                                   float scale, hipStream_t st) {
+    const DropArgs dr{thr, (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), rkeep};
+#define ARGS q, k, v, o, lse, B, Hq, Hkv, N, scale, st, 0, 0, nullptr, nullptr, 0, dr
+    if (d == 64) return causal ? launch<64, true, false, false, true>(ARGS) : launch<64, false, false, false, true>(ARGS);
+    if (d == 128)
+        return causal ? launch<128, true, false, false, true>(ARGS) : launch<128, false, false, false, true>(ARGS);
 #undef ARGS
     return hipErrorInvalidValue;
 }

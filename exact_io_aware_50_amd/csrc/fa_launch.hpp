@@ -85,6 +85,13 @@ hipError_t launch_bwd_bf16_bsparse(int d, int causal, const void* q, const void*
                                    const int* row_ptr, const int* col_idx, const int* col_ptr, const int* row_idx,
                                    int nnz, float scale, hipStream_t st);
 
+// Forward with attention dropout, bf16: element (i, j) of (b, h) kept iff word
+// j % 4 of Philox4x32-10((j / 4, i, b * Hq + h, 0), seed halves) >= thr; kept
+// probabilities scaled by rkeep.
+hipError_t launch_fwd_bf16_dropout(int d, int causal, const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int B, int Hq, int Hkv, int N, uint32_t thr, uint64_t seed, float rkeep,
+                                   float scale, hipStream_t st);
+
 hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
 
 // Decode split over the keys: nrb blocks of 32 packed query rows per K/V head,

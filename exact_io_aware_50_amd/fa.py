@@ -47,6 +47,8 @@ _lib.fa_fwd_local.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f
 _lib.fa_fwd_local.restype = _i
 _lib.fa_bwd_local.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_bwd_local.restype = _i
+_lib.fa_fwd_dropout.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, ctypes.c_uint64, _f, _i, _p]
+_lib.fa_fwd_dropout.restype = _i
 _lib.fa_fwd_bsparse.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _i, _f, _i, _p]
 _lib.fa_fwd_bsparse.restype = _i
 _lib.fa_bwd_bsparse.argtypes = ([_p] * 10 + [_i] * 6 + [_p] * 4 + [_i, _f, _i, _p])
@@ -65,7 +67,7 @@ _lib.fa_abi_version.argtypes = []
 _lib.fa_abi_version.restype = _i
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
-           "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_decode",
+           "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_dropout", "fa_decode",
            "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes", "fa_status_string",
            "fa_abi_version")
 
@@ -232,6 +234,23 @@ def fa_bwd_bsparse(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, 
                    row_idx, nnz, softmax_scale, dtype, stream) -> int:
     return _lib.fa_bwd_bsparse(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal, row_ptr,
                                col_idx, col_ptr, row_idx, nnz, float(softmax_scale), dtype, stream)
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, dropout_p, seed, softmax_scale, dtype, stream) -> int:
+    return _lib.fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, float(dropout_p), int(seed),
+                               float(softmax_scale), dtype, stream)
+
+
+def fwd_dropout(q, k, v, causal: bool, scale: float, dropout_p: float, seed: int, stream=None):
+    """(o, lse) of attention with dropout on P (Philox4x32-10 keep mask, see fa_fwd_dropout), bf16."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check(fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
+                          int(causal), dropout_p, seed, scale, _dtype_code(q), _stream_handle(stream)),
+           "fa_fwd_dropout")
+    return o, lse
 
 
 BSPARSE_BLOCK = 256   # side of a mask block (FA_BSPARSE_BLOCK)

@@ -39,6 +39,7 @@
 #define FA_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -189,6 +190,26 @@ fa_status_t fa_bwd_local(const void* q, const void* k, const void* v,
                          int B, int Hq, int Hkv, int N, int d,
                          int window, int sink, float softmax_scale, int dtype,
                          hipStream_t stream);
+
+/*
+ * Forward with attention dropout on the normalised probabilities: the
+ * FlashAttention page of the self-hosted LLM glossary (opening paragraphs:
+ * matrix products, masking, softmax and dropout fused in one kernel) and the
+ * FlashAttention digest, section "Limits" (dropout among the features a
+ * kernel must handle).  The pages fix no generator; this library uses
+ * Philox4x32-10 (Salmon et al., SC 2011): element (query i, key j) of batch
+ * entry b and query head h is kept iff word j % 4 of
+ * Philox((j / 4, i, b * Hq + h, 0), (seed % 2^32, seed / 2^32)) is
+ * >= floor(dropout_p * 2^32); O = ((Z o P) / (1 - dropout_p)) V.  LSE is that of
+ * the undropped softmax.  Same arguments, layouts and errors as fa_fwd
+ * (bf16 only) plus dropout_p in [0, 1) (else FA_ERR_UNSUPPORTED) and the
+ * 64-bit seed.  The backward through the mask is not provided.
+ */
+fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v,
+                           void* o, float* lse,
+                           int B, int Hq, int Hkv, int N, int d, int causal,
+                           float dropout_p, uint64_t seed,
+                           float softmax_scale, int dtype, hipStream_t stream);
 
 /*
  * Block-sparse attention: key j is visible to query i iff block

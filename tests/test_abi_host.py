@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_bwd_workspace_bytes", "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_decode",
-                          "fa_fwd_bsparse", "fa_bwd_bsparse",
+                          "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_dropout",
                           "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
                           "fa_status_string", "fa_abi_version"}
     for n in names:
@@ -227,6 +227,20 @@ def test_bsparse_validation():
     assert fa.fa_bwd_bsparse(**{**bw, "delta_ws": None}) == 1
     assert fa.fa_bwd_bsparse(**{**bw, "Hq": 3}) == 2
     assert fa.fa_bwd_bsparse(**{**bw, "B": 0}) == 0
+
+
+def test_dropout_validation():
+    from exact_io_aware_50_amd import fa
+    f = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, Hq=2, Hkv=2, N=256, d=128, causal=1, dropout_p=0.1,
+             seed=2 ** 40 + 3, softmax_scale=0.1, dtype=1, stream=None)
+    assert fa.fa_fwd_dropout(**{**f, "dropout_p": 1.0}) == 3
+    assert fa.fa_fwd_dropout(**{**f, "dropout_p": -0.1}) == 3
+    assert fa.fa_fwd_dropout(**{**f, "dropout_p": float("nan")}) == 3
+    assert fa.fa_fwd_dropout(**{**f, "dtype": 0}) == 3
+    assert fa.fa_fwd_dropout(**{**f, "q": None}) == 1
+    assert fa.fa_fwd_dropout(**{**f, "o": A[2]}) == 6
+    assert fa.fa_fwd_dropout(**{**f, "Hq": 3}) == 2
+    assert fa.fa_fwd_dropout(**{**f, "N": 0}) == 0
 
 
 def test_bsparse_layout():
