@@ -293,11 +293,18 @@ def cpu_baseline(w, seconds):
     import numpy as np
     import oracle
     from exact_io_aware_50_amd import inputs as I
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    from threadpoolctl import threadpool_limits
+    # BLAS threads: the cores this process may run on, capped by OMP_NUM_THREADS
+    # (the host's CPU share for one GPU); the oracle runs with exactly that many
+    affinity = len(os.sched_getaffinity(0))
+    threads = min(affinity, int(os.environ.get("OMP_NUM_THREADS", affinity) or affinity))
+    with threadpool_limits(limits=threads):
+        return _cpu_baseline_run(w, seconds, threads, affinity)
+
+
+def _cpu_baseline_run(w, seconds, threads, affinity):
+    import oracle
+    from exact_io_aware_50_amd import inputs as I
     heads = 0
     t0 = time.perf_counter()
     while True:
@@ -323,7 +330,8 @@ def cpu_baseline(w, seconds):
     return {"value": per_head * heads / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"float64 oracle forward+backward of {heads} whole head(s) (b, h) in order of "
-                      f"{w.name.split(' ')[0]}; credited flops of those heads / compute time ({elapsed:.1f} s)"}
+                      f"{w.name.split(' ')[0]}; credited flops of those heads / compute time ({elapsed:.1f} s); "
+                      f"{threads} BLAS threads ({affinity} cores in the affinity mask)"}
 
 
 def gemm_reference(torch, dev, stream, kern, n=8192, iters=15):

@@ -34,7 +34,7 @@ fa_status_t launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ER
 extern "C" {
 
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                   int N, int d, int causal, float softmax_scale, int dtype, const float* descale_qkv,
+                   int N, int d, int causal, float softmax_scale, fa_dtype_t dtype, const float* descale_qkv,
                    hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3) return FA_ERR_UNSUPPORTED;
@@ -93,7 +93,7 @@ extern "C" {
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                    void* dq, void* dk, void* dv, float* delta_ws, int B, int Hq, int Hkv, int N, int d,
-                   int causal, float softmax_scale, int dtype, hipStream_t stream) {
+                   int causal, float softmax_scale, fa_dtype_t dtype, hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
@@ -110,7 +110,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
 }
 
 fa_status_t fa_bwd_delta(const void* o, const void* dO, const float* lse, float* ws, int B, int Hq, int N, int d,
-                         int dtype, hipStream_t stream) {
+                         fa_dtype_t dtype, hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, 1, N, d, 0, 1.0f, &empty);
@@ -121,8 +121,8 @@ fa_status_t fa_bwd_delta(const void* o, const void* dO, const float* lse, float*
 }
 
 fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dk,
-                        void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype,
-                        hipStream_t stream) {
+                        void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float softmax_scale,
+                        fa_dtype_t dtype, hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
@@ -134,7 +134,8 @@ fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v, const void*
 }
 
 fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dq, int B,
-                      int Hq, int Hkv, int N, int d, int causal, float softmax_scale, int dtype, hipStream_t stream) {
+                      int Hq, int Hkv, int N, int d, int causal, float softmax_scale, fa_dtype_t dtype,
+                      hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
@@ -148,7 +149,8 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v, const void* d
 // Sliding window: W >= N, or S >= N, sees exactly the causal keys, so the
 // causal kernels run.
 fa_status_t fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                         int N, int d, int window, int sink, float softmax_scale, int dtype, hipStream_t stream) {
+                         int N, int d, int window, int sink, float softmax_scale, fa_dtype_t dtype,
+                         hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     if (window < 1 || sink < 0) return FA_ERR_UNSUPPORTED;
@@ -164,7 +166,8 @@ fa_status_t fa_fwd_local(const void* q, const void* k, const void* v, void* o, f
 
 fa_status_t fa_bwd_local(const void* q, const void* k, const void* v, const void* o, const void* dO,
                          const float* lse, void* dq, void* dk, void* dv, float* delta_ws, int B, int Hq, int Hkv,
-                         int N, int d, int window, int sink, float softmax_scale, int dtype, hipStream_t stream) {
+                         int N, int d, int window, int sink, float softmax_scale, fa_dtype_t dtype,
+                         hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     if (window < 1 || sink < 0) return FA_ERR_UNSUPPORTED;
@@ -185,17 +188,17 @@ fa_status_t fa_bwd_local(const void* q, const void* k, const void* v, const void
 }
 
 fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                           int N, int d, int causal, float dropout_p, uint64_t seed, float softmax_scale, int dtype,
-                           hipStream_t stream) {
+                           int N, int d, int causal, double dropout_p, uint64_t seed, float softmax_scale,
+                           fa_dtype_t dtype, hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
-    if (!(dropout_p >= 0.f && dropout_p < 1.f)) return FA_ERR_UNSUPPORTED;
+    if (!(dropout_p >= 0.0 && dropout_p < 1.0)) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
     if (s != FA_OK || empty) return s;
     s = check_ptrs({q, k, v}, {}, {o}, {lse});
     if (s != FA_OK) return s;
-    const uint32_t thr = (uint32_t)floor((double)dropout_p * 4294967296.0);
-    const float rkeep = (float)(1.0 / (1.0 - (double)dropout_p));
+    const uint32_t thr = (uint32_t)floor(dropout_p * 4294967296.0);
+    const float rkeep = (float)(1.0 / (1.0 - dropout_p));
     return launch_status(fa::launch_fwd_bf16_dropout(d, causal, q, k, v, o, lse, B, Hq, Hkv, N, thr, seed, rkeep,
                                                      softmax_scale, stream));
 }
@@ -211,7 +214,7 @@ static fa_status_t check_bsparse(int N, const int* ptr, const int* idx, int nnz)
 
 fa_status_t fa_fwd_bsparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                            int Hkv, int N, int d, int causal, const int* row_ptr, const int* col_idx, int nnz,
-                           float softmax_scale, int dtype, hipStream_t stream) {
+                           float softmax_scale, fa_dtype_t dtype, hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
@@ -227,7 +230,7 @@ fa_status_t fa_fwd_bsparse(const void* q, const void* k, const void* v, void* o,
 fa_status_t fa_bwd_bsparse(const void* q, const void* k, const void* v, const void* o, const void* dO,
                            const float* lse, void* dq, void* dk, void* dv, float* delta_ws, int B, int Hq, int Hkv,
                            int N, int d, int causal, const int* row_ptr, const int* col_idx, const int* col_ptr,
-                           const int* row_idx, int nnz, float softmax_scale, int dtype, hipStream_t stream) {
+                           const int* row_idx, int nnz, float softmax_scale, fa_dtype_t dtype, hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
@@ -256,7 +259,7 @@ static fa_status_t check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, i
     if (Hkv == 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
     // every query row must see at least one key
     if (Nk == 0 || (causal && Nq > Nk)) return FA_ERR_SHAPE;
-    const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d, 1);
+    const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d, 1, fa::kCuBound);
     const int64_t units = (int64_t)B * Hkv * p.nrb * p.nsplit;
     const int64_t rows = (int64_t)B * Hq * Nq;
     if (units / 4 + 1 > INT32_MAX || rows / 4 + 1 > INT32_MAX) return FA_ERR_SHAPE;
@@ -266,11 +269,11 @@ static fa_status_t check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, i
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     bool empty = false;
     if (check_decode(B, Hq, Hkv, Nq, Nk, d, 0, 1.0f, &empty) != FA_OK || empty) return 0;
-    return fa::decode_ws_bytes(fa::decode_plan(B, Hq, Hkv, Nq, Nk, d, 1), B, Hq, Nq, d);
+    return fa::decode_ws_bytes(fa::decode_plan(B, Hq, Hkv, Nq, Nk, d, 1, fa::device_cus()), B, Hq, Nq, d);
 }
 
 fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int B, int Hq,
-                      int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale, int dtype,
+                      int Hkv, int Nq, int Nk, int d, int causal, float softmax_scale, fa_dtype_t dtype,
                       hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
@@ -293,7 +296,8 @@ static fa_status_t check_paged(int B, int Hq, int Hkv, int Nq, int maxb, int bs,
     if (s != FA_OK || *empty) return s;
     if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
     if (nblk == 0) return FA_ERR_SHAPE;
-    const int64_t units = (int64_t)fa::paged_chunks(B, Hq, Hkv, Nq, d) * Hkv * ((Hq / Hkv * (int64_t)Nq + 31) / 32);
+    const int64_t units =
+        (int64_t)fa::paged_chunks(B, Hq, Hkv, Nq, d, fa::kCuBound) * Hkv * ((Hq / Hkv * (int64_t)Nq + 31) / 32);
     if (units / 4 + 1 > INT32_MAX) return FA_ERR_SHAPE;
     return FA_OK;
 }
@@ -307,7 +311,7 @@ size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int Nq, int max_b
 fa_status_t fa_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
                             const int* seq_lens, void* o, float* lse, float* ws, int B, int Hq, int Hkv, int Nq,
                             int max_blocks, int block_size, int num_blocks, int d, int causal, float softmax_scale,
-                            int dtype, hipStream_t stream) {
+                            fa_dtype_t dtype, hipStream_t stream) {
     bool empty = false;
     if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     fa_status_t s = check_paged(B, Hq, Hkv, Nq, max_blocks, block_size, num_blocks, d, causal, softmax_scale, &empty);

@@ -750,7 +750,7 @@ static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const
     using Cfg = KVBf16Cfg<D>;
     const int nkb = (N + Cfg::BNK - 1) / Cfg::BNK;
     const int Np = ws_rows(N);
-    static std::atomic<int> slots{0};
+    static PerDevice slots;
     const int grid = persistent_grid((const void*)bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP>, Cfg::kThreads,
                                      nkb * Hkv * B, slots);
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0,
@@ -767,7 +767,7 @@ static hipError_t launch_dq(const void* q, const void* k, const void* v, const v
     using Cfg = QBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
     const int Np = ws_rows(N);
-    static std::atomic<int> slots{0};
+    static PerDevice slots;
     const int grid =
         persistent_grid((const void*)bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP>, Cfg::kThreads, nmb * Hq * B, slots);
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0,

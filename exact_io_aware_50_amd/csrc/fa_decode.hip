@@ -325,15 +325,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     if (lane == 0) LSE[row] = wsum > 0.f ? L + logf(wsum) : -INFINITY;
 }
 
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int per_slot) {
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int per_slot, int cus) {
     DecodePlan p;
     const int G = Hq / Hkv;
     p.nrb = (G * Nq + 31) / 32;
     const int64_t base = (int64_t)B * Hkv * p.nrb;
-    // per_slot wave units per resident wave of the 256 CUs (each unit streams
+    // per_slot wave units per resident wave of the device's CUs (each unit streams
     // its chunk with its own ring, so fewer, longer units pay the ring's
     // start-up latency less often); chunks of at least 256 keys
-    const int64_t slots = (int64_t)per_slot * 256 * (d == 128 ? DecCfg<128>::kWaves : DecCfg<64>::kWaves);
+    const int64_t slots = (int64_t)per_slot * cus * (d == 128 ? DecCfg<128>::kWaves : DecCfg<64>::kWaves);
     const int64_t want = (slots + base - 1) / base;
     const int64_t most = ((int64_t)Nk + 255) / 256;
     int64_t ns = want < most ? want : most;
@@ -349,7 +349,7 @@ template <int D, bool CAUSAL>
 static hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int B,
                          int Hq, int Hkv, int Nq, int Nk, float scale, hipStream_t st) {
     using Cfg = DecCfg<D>;
-    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk, D, 1);
+    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk, D, 1, device_cus());
     const int64_t rows = (int64_t)B * Hq * Nq;
     float* wo = ws;
     float* wl = ws + rows * p.nsplit * D;
@@ -365,22 +365,22 @@ static hipError_t launch(const void* q, const void* k, const void* v, void* o, f
     return hipGetLastError();
 }
 
-int paged_chunks(int B, int Hq, int Hkv, int Nq, int d) {
+int paged_chunks(int B, int Hq, int Hkv, int Nq, int d, int cus) {
     // about two wave units (chunk x K/V head x row block) per resident wave
-    // of the 256 CUs, and at least two chunk slots per sequence.  Two per wave
+    // of the device's CUs, and at least two chunk slots per sequence.  Two per wave
     // measured best on the 16-sequence 16K workload with mixed lengths: 0.124
     // ms against 0.136 for one and 0.134 for four (the rounding of each
     // sequence's chunk count leaves some slots empty; a second round of units
     // fills the waves those free)
     const int nrb = (Hq / Hkv * Nq + 31) / 32;
-    const int64_t slots = 256 * (int64_t)(d == 128 ? DecCfg<128>::kWaves : DecCfg<64>::kWaves);
+    const int64_t slots = (int64_t)cus * (d == 128 ? DecCfg<128>::kWaves : DecCfg<64>::kWaves);
     const int64_t per = (int64_t)Hkv * nrb;
     const int64_t T = (2 * slots + per - 1) / per;
     return (int)(T > 2 * (int64_t)B ? T : 2 * (int64_t)B);
 }
 
 size_t paged_ws_bytes(int B, int Hq, int Hkv, int Nq, int d) {
-    const int64_t T = paged_chunks(B, Hq, Hkv, Nq, d);
+    const int64_t T = paged_chunks(B, Hq, Hkv, Nq, d, device_cus());
     const int64_t ints = ((4 * (int64_t)B + 3 * T) * 4 + 15) / 16 * 16;
     return (size_t)(ints + 4 * T * Hq * Nq * (int64_t)(d + 1));
 }
@@ -390,7 +390,7 @@ static hipError_t launch_paged(const void* q, const void* kc, const void* vc, co
                                void* o, float* lse, float* ws, int B, int Hq, int Hkv, int Nq, int maxb, int bs,
                                int nblk, float scale, hipStream_t st) {
     using Cfg = DecCfg<D>;
-    const int T = paged_chunks(B, Hq, Hkv, Nq, D);
+    const int T = paged_chunks(B, Hq, Hkv, Nq, D, device_cus());
     const int nrb = (Hq / Hkv * Nq + 31) / 32;
     int* seq = reinterpret_cast<int*>(ws);
     int* unit = seq + 4 * (int64_t)B;

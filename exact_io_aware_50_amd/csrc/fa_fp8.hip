@@ -629,7 +629,7 @@ static hipError_t launch_fp8_pp(const void* q, const void* k, const void* v, voi
                                 const float* descale, int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
     using Cfg = FwdFp8Cfg<128>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
-    static std::atomic<int> slots{0};
+    static PerDevice slots;
     const int grid = persistent_grid((const void*)fwd_fp8_pp_kernel<128, CAUSAL>, Cfg::kThreads, nmb * Hq * B, slots);
     hipLaunchKernelGGL((fwd_fp8_pp_kernel<128, CAUSAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
                        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (uint16_t*)o, lse, descale, B, Hq,

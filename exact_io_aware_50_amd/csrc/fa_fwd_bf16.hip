@@ -420,7 +420,7 @@ static hipError_t launch(const void* q, const void* k, const void* v, void* o, f
                          const int* bidx = nullptr, int nnz = 0, DropArgs drop = {0u, 0u, 0u, 1.f}) {
     using Cfg = FwdBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
-    static std::atomic<int> slots{0};
+    static PerDevice slots;
     const int grid = persistent_grid((const void*)fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>, Cfg::kThreads,
                                      nmb * Hq * B, slots);
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0,

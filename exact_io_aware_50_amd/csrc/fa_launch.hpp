@@ -9,23 +9,50 @@
 
 namespace fa {
 
+// Values fixed by the device and the code object (the CU count, a kernel's
+// resident workgroups per CU), queried on a device's first use and kept per
+// device for the process.  0 = not yet known.
+constexpr int kMaxDevices = 64;
+struct PerDevice {
+    std::atomic<int> v[kMaxDevices];
+};
+
+// The current device, or -1 if it cannot be queried or is past kMaxDevices.
+inline int current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    return dev;
+}
+
+// CUs of the current device (256 on MI355X; 256 also if the query fails).
+inline int device_cus() {
+    static PerDevice cache;
+    const int dev = current_device();
+    if (dev < 0) return 256;
+    int cus = cache.v[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return 256;
+        cache.v[dev].store(cus, std::memory_order_relaxed);
+    }
+    return cus;
+}
+
 // Workgroups of a persistent launch: every resident slot of the current
-// device (CUs x workgroups per CU), at most `items`.  The CU count and the
-// kernel's occupancy are queried once and kept in `cache` (a property of the
-// device and the code object, the same on every call); if a query fails the
-// grid is `items`, one item per workgroup, which the kernels' schedule also
-// handles.
-inline int persistent_grid(const void* kernel, int threads, int items, std::atomic<int>& cache) {
-    int slots = cache.load(std::memory_order_relaxed);
+// device (CUs x workgroups per CU), at most `items`.  The slot count is kept
+// per device in `cache`; if a query fails the grid is `items`, one item per
+// workgroup, which the kernels' schedule also handles.
+inline int persistent_grid(const void* kernel, int threads, int items, PerDevice& cache) {
+    const int dev = current_device();
+    int slots = dev < 0 ? 0 : cache.v[dev].load(std::memory_order_relaxed);
     if (slots == 0) {
-        int dev = 0, cus = 0, per = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess || cus <= 0 ||
+        int per = 0;
+        const int cus = device_cus();
+        if (dev < 0 || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess ||
             per <= 0)
             return items;
         slots = cus * per;
-        cache.store(slots, std::memory_order_relaxed);
+        cache.v[dev].store(slots, std::memory_order_relaxed);
     }
     return items < slots ? items : slots;
 }
@@ -99,12 +126,17 @@ hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descal
 struct DecodePlan {
     int nrb, nsplit, chunk;
 };
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int per_slot);
+// `cus` is the CU count the split is sized for (the current device's at a
+// launch and in the workspace size).
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int per_slot, int cus);
 // Paged decode: chunk slots of the device-side plan, and the workspace
 // (plan ints [B][4] + [T][3], 16-byte aligned, then float32 O [T][Hq][Nq][d]
-// and LSE [T][Hq][Nq]).
-int paged_chunks(int B, int Hq, int Hkv, int Nq, int d);
+// and LSE [T][Hq][Nq]), both for the current device's CU count.
+int paged_chunks(int B, int Hq, int Hkv, int Nq, int d, int cus);
 size_t paged_ws_bytes(int B, int Hq, int Hkv, int Nq, int d);
+
+// Upper bound on the CU count used when sizes are checked before any HIP call.
+constexpr int kCuBound = 1024;
 
 // Workspace of fa_decode: float32 O per (row, chunk) [rows][nsplit][d], then
 // the chunk LSEs [rows][nsplit], rows = B * Hq * Nq.

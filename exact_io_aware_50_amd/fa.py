@@ -47,7 +47,8 @@ _lib.fa_fwd_local.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f
 _lib.fa_fwd_local.restype = _i
 _lib.fa_bwd_local.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_bwd_local.restype = _i
-_lib.fa_fwd_dropout.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, ctypes.c_uint64, _f, _i, _p]
+_d = ctypes.c_double
+_lib.fa_fwd_dropout.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _d, ctypes.c_uint64, _f, _i, _p]
 _lib.fa_fwd_dropout.restype = _i
 _lib.fa_fwd_bsparse.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _i, _f, _i, _p]
 _lib.fa_fwd_bsparse.restype = _i

@@ -15,8 +15,11 @@
  *
  * Conventions shared by every entry point:
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
- *    library never allocates, frees or synchronises, keeps no mutable global
- *    state, and enqueues all work on `stream` (NULL = the default stream).
+ *    library never allocates, frees or synchronises, and enqueues all work on
+ *    `stream` (NULL = the default stream).  Its only mutable global state is
+ *    a per-device cache of values fixed by the device and the code object
+ *    (CU count, resident workgroups per CU of each kernel), filled on a
+ *    device's first call; no argument or result of a call is kept.
  *  - Layouts are contiguous, row-major, head dimension fastest:
  *    Q, O, dO, dQ are [B, Hq, N, d]; K, V, dK, dV are [B, Hkv, N, d];
  *    LSE and the backward workspace are [B, Hq, N] float32.
@@ -64,7 +67,7 @@ enum {
     FA_ERR_ALIAS = 6          /* an output aliases an input                  */
 };
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 /*
  * Forward pass.  "flash attention io aware", section "Flash Attention
@@ -83,7 +86,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v,
                    void* o, float* lse,
                    int B, int Hq, int Hkv, int N, int d,
                    int causal, float softmax_scale,
-                   int dtype, const float* descale_qkv,
+                   fa_dtype_t dtype, const float* descale_qkv,
                    hipStream_t stream);
 
 /*
@@ -106,7 +109,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v,
                    void* dq, void* dk, void* dv,
                    float* delta_ws,
                    int B, int Hq, int Hkv, int N, int d,
-                   int causal, float softmax_scale, int dtype,
+                   int causal, float softmax_scale, fa_dtype_t dtype,
                    hipStream_t stream);
 
 /*
@@ -126,21 +129,21 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v,
  * fa_bwd_dkdv and fa_bwd_dq only read `ws` and do not depend on each other.
  */
 fa_status_t fa_bwd_delta(const void* o, const void* dO, const float* lse, float* ws,
-                         int B, int Hq, int N, int d, int dtype,
+                         int B, int Hq, int N, int d, fa_dtype_t dtype,
                          hipStream_t stream);
 
 fa_status_t fa_bwd_dkdv(const void* q, const void* k, const void* v,
                         const void* dO, const float* ws,
                         void* dk, void* dv,
                         int B, int Hq, int Hkv, int N, int d,
-                        int causal, float softmax_scale, int dtype,
+                        int causal, float softmax_scale, fa_dtype_t dtype,
                         hipStream_t stream);
 
 fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v,
                       const void* dO, const float* ws,
                       void* dq,
                       int B, int Hq, int Hkv, int N, int d,
-                      int causal, float softmax_scale, int dtype,
+                      int causal, float softmax_scale, fa_dtype_t dtype,
                       hipStream_t stream);
 
 /*
@@ -180,7 +183,7 @@ fa_status_t fa_quantize_fp8(const void* x_bf16, size_t n, void* x_e4m3,
 fa_status_t fa_fwd_local(const void* q, const void* k, const void* v,
                          void* o, float* lse,
                          int B, int Hq, int Hkv, int N, int d,
-                         int window, int sink, float softmax_scale, int dtype,
+                         int window, int sink, float softmax_scale, fa_dtype_t dtype,
                          hipStream_t stream);
 
 fa_status_t fa_bwd_local(const void* q, const void* k, const void* v,
@@ -188,7 +191,7 @@ fa_status_t fa_bwd_local(const void* q, const void* k, const void* v,
                          void* dq, void* dk, void* dv,
                          float* delta_ws,
                          int B, int Hq, int Hkv, int N, int d,
-                         int window, int sink, float softmax_scale, int dtype,
+                         int window, int sink, float softmax_scale, fa_dtype_t dtype,
                          hipStream_t stream);
 
 /*
@@ -200,16 +203,17 @@ fa_status_t fa_bwd_local(const void* q, const void* k, const void* v,
  * Philox4x32-10 (Salmon et al., SC 2011): element (query i, key j) of batch
  * entry b and query head h is kept iff word j % 4 of
  * Philox((j / 4, i, b * Hq + h, 0), (seed % 2^32, seed / 2^32)) is
- * >= floor(dropout_p * 2^32); O = ((Z o P) / (1 - dropout_p)) V.  LSE is that of
- * the undropped softmax.  Same arguments, layouts and errors as fa_fwd
- * (bf16 only) plus dropout_p in [0, 1) (else FA_ERR_UNSUPPORTED) and the
- * 64-bit seed.  The backward through the mask is not provided.
+ * >= floor(dropout_p * 2^32) (dropout_p taken as the double passed, so the
+ * drop probability is dropout_p on the 2^-32 grid); O = ((Z o P) /
+ * (1 - dropout_p)) V.  LSE is that of the undropped softmax.  Same arguments,
+ * layouts and errors as fa_fwd (bf16 only) plus dropout_p in [0, 1) (else
+ * FA_ERR_UNSUPPORTED) and the 64-bit seed.
  */
 fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v,
                            void* o, float* lse,
                            int B, int Hq, int Hkv, int N, int d, int causal,
-                           float dropout_p, uint64_t seed,
-                           float softmax_scale, int dtype, hipStream_t stream);
+                           double dropout_p, uint64_t seed,
+                           float softmax_scale, fa_dtype_t dtype, hipStream_t stream);
 
 /*
  * Block-sparse attention: key j is visible to query i iff block
@@ -243,7 +247,7 @@ fa_status_t fa_fwd_bsparse(const void* q, const void* k, const void* v,
                            void* o, float* lse,
                            int B, int Hq, int Hkv, int N, int d, int causal,
                            const int* row_ptr, const int* col_idx, int nnz,
-                           float softmax_scale, int dtype, hipStream_t stream);
+                           float softmax_scale, fa_dtype_t dtype, hipStream_t stream);
 
 fa_status_t fa_bwd_bsparse(const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,
@@ -252,7 +256,7 @@ fa_status_t fa_bwd_bsparse(const void* q, const void* k, const void* v,
                            int B, int Hq, int Hkv, int N, int d, int causal,
                            const int* row_ptr, const int* col_idx,
                            const int* col_ptr, const int* row_idx, int nnz,
-                           float softmax_scale, int dtype, hipStream_t stream);
+                           float softmax_scale, fa_dtype_t dtype, hipStream_t stream);
 
 /*
  * Decode: attention of Nq new query rows against a key/value cache of Nk
@@ -278,7 +282,7 @@ fa_status_t fa_bwd_bsparse(const void* q, const void* k, const void* v,
 fa_status_t fa_decode(const void* q, const void* k, const void* v,
                       void* o, float* lse, float* ws,
                       int B, int Hq, int Hkv, int Nq, int Nk, int d,
-                      int causal, float softmax_scale, int dtype,
+                      int causal, float softmax_scale, fa_dtype_t dtype,
                       hipStream_t stream);
 
 /*
@@ -312,7 +316,7 @@ fa_status_t fa_decode_paged(const void* q, const void* k_cache, const void* v_ca
                             void* o, float* lse, float* ws,
                             int B, int Hq, int Hkv, int Nq,
                             int max_blocks, int block_size, int num_blocks, int d,
-                            int causal, float softmax_scale, int dtype,
+                            int causal, float softmax_scale, fa_dtype_t dtype,
                             hipStream_t stream);
 
 /* Bytes of the paged decode workspace (0 for an empty or invalid problem). */

@@ -28,11 +28,24 @@ def pytest_collection_modifyitems(config, items):
             item.add_marker(skip)
 
 
+def _library_is_stale(lib: str) -> bool:
+    """True if libfa.so is missing or older than any HIP source or the public header."""
+    if not os.path.exists(lib):
+        return True
+    built = os.path.getmtime(lib)
+    dirs = [os.path.join(ROOT, "exact_io_aware_50_amd", "csrc"), os.path.join(ROOT, "include")]
+    for d in dirs:
+        for f in os.listdir(d):
+            if f.endswith((".hip", ".hpp", ".h")) and os.path.getmtime(os.path.join(d, f)) > built:
+                return True
+    return False
+
+
 @pytest.fixture(scope="session", autouse=True)
 def _built_library():
-    """Build libfa.so once if it is missing (a built library is used as is)."""
+    """Build libfa.so once if it is missing or older than its sources."""
     lib = os.path.join(ROOT, "exact_io_aware_50_amd", "libfa.so")
-    if not os.path.exists(lib):
+    if _library_is_stale(lib):
         from exact_io_aware_50_amd import build
         build.build(verbose=False)
     yield

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(fa.EXPORTS) == set(names)
-    assert fa.fa_abi_version() == 1
+    assert fa.fa_abi_version() == 2
 
 
 def test_status_strings():
@@ -289,3 +289,4 @@ def test_decode_paged_validation():
     # the chunk plan (ints), then float32 O and LSE per (chunk slot, query row); at least two slots per sequence
     assert n >= 4 * (2 * 2) * 8 * 1 * 129
     assert fa.fa_decode_paged_workspace_bytes(2, 8, 2, 1, 8, 40, 128) == 0
+

@@ -200,3 +200,29 @@ def test_bsparse_workload_sampled(fa, dev):
     G_, R_ = c(got), c(ref)
     check(G_["O"], G_["L"], [G_["dQ"], G_["dK"], G_["dV"]], R_["O"], R_["L"], [R_["dQ"], R_["dK"], R_["dV"]],
           "N16384 block-sparse")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bsparse_causal_raw_layout_above_diagonal(fa, dev, d):
+    """A layout that is not trimmed to the lower triangle, run with causal = 1: blocks above the diagonal are
+    listed (their keys are all masked), and row block 1 lists only such blocks, so its rows see no key
+    (O = 0, LSE = -inf, no gradient).  Compared with the oracle's block mask with the causal mask."""
+    B, Hq, Hkv, N = 1, 4, 2, 1100
+    nb = (N + BS - 1) // BS
+    mask = np.zeros((nb, nb), bool)
+    for r, cols in {0: (0, 3), 1: (2, 4), 2: (0, 2, 3), 3: (1, 4), 4: (0, 1, 2, 3, 4)}.items():
+        mask[r, list(cols)] = True
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, do = (I.random_tensor(97 + d, (B, H, N, d), "bf16", tensor_id=t) for t, H in enumerate((Hq, Hkv, Hkv, Hq)))
+    layout = fa.BlockSparseLayout(mask, causal=False, device=dev)      # not trimmed: upper blocks stay listed
+    assert layout.nnz == int(mask.sum())
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.fwd_bsparse(qd, kd, vd, layout, True, scale)
+    dq, dk, dv, _ = fa.bwd_bsparse(qd, kd, vd, o, dod, lse, layout, True, scale)
+    torch.cuda.synchronize()
+    Q, K, V, dO = (f64(t) for t in (q, k, v, do))
+    bm = oracle.BlockMask(mask, BS)
+    O, L = oracle.forward(Q, K, V, True, scale, window=bm)
+    rq, rk, rv, _ = oracle.backward(Q, K, V, dO, True, scale, window=bm)
+    assert np.all(np.isneginf(L[:, :, BS:2 * BS]))                      # row block 1 sees nothing
+    check(f64(o), f64(lse), [f64(x) for x in (dq, dk, dv)], O, L, [rq, rk, rv], f"raw causal layout d={d}")

@@ -172,14 +172,16 @@ def test_causal_bf16_n4096_workload(fa, dev):
     sampled_check(fa, dev, I.WORKLOADS["causal_bf16_n4096"])
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_gqa_bf16_n16384_workload(fa, dev):
-    sampled_check(fa, dev, I.WORKLOADS["gqa_bf16_n16384"], kv_heads_for_cols=[(0, 0)])
+    # key columns of the K/V heads of the sampled query heads: 0 and 1 hold the
+    # group-straddling query heads G - 1 and G, 7 the last one
+    sampled_check(fa, dev, I.WORKLOADS["gqa_bf16_n16384"], kv_heads_for_cols=[(0, 0), (0, 1), (0, 7)])
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_long_bf16_n65536_workload(fa, dev):
-    sampled_check(fa, dev, I.WORKLOADS["long_bf16_n65536"], kv_heads_for_cols=[(0, 7)])
+    sampled_check(fa, dev, I.WORKLOADS["long_bf16_n65536"], kv_heads_for_cols=[(0, 0), (0, 7)])
 
 
 # ---------------------------------------------------------------- fp8
