@@ -3,7 +3,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_launch.hpp"
@@ -106,6 +108,65 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                                 stream);
     if (e == hipSuccess)
         e = fa::launch_bwd_dq(dtype, d, causal, q, k, v, dO, delta_ws, dq, B, Hq, Hkv, N, softmax_scale, stream);
+    return launch_status(e);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- scratch-free backward
+// The workspace of fa_bwd_noalloc: a library-owned device array, one copy per
+// device.  In host code `scratch` only names the symbol; its address on a
+// device comes from hipGetSymbolAddress with that device current, and only
+// that address is ever passed to a kernel.
+static __device__ __align__(256) float scratch[FA_BWD_NOALLOC_MAX_BYTES / 4];
+
+namespace {
+
+std::atomic<float*> g_scratch[fa::kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Address of `scratch` on the current device, looked up once per device
+// (nullptr if the device or the lookup fails).
+float* scratch_on_current_device() {
+    const int dev = fa::current_device();
+    if (dev < 0) return nullptr;
+    float* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void* a = nullptr;
+        if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return nullptr;
+        p = static_cast<float*>(a);
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                           const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                           int causal, float softmax_scale, fa_dtype_t dtype, hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    if ((uint64_t)8 * (uint64_t)B * (uint64_t)Hq * (uint64_t)fa::ws_rows(N) > FA_BWD_NOALLOC_MAX_BYTES)
+        return FA_ERR_SHAPE;
+    s = check_ptrs({q, k, v, o, dO}, {lse}, {dq, dk, dv}, {});
+    if (s != FA_OK) return s;
+    float* ws = scratch_on_current_device();
+    if (!ws) return FA_ERR_LAUNCH;
+    // the three kernels of fa_bwd: the delta kernel writes every workspace row
+    // (padding included) before the other two read it, so nothing is cleared
+    hipError_t e = fa::launch_bwd_delta(dtype, d, o, dO, lse, ws, B, Hq, N, stream);
+    if (e == hipSuccess)
+        e = fa::launch_bwd_dkdv(dtype, d, causal, q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, softmax_scale, stream);
+    if (e == hipSuccess)
+        e = fa::launch_bwd_dq(dtype, d, causal, q, k, v, dO, ws, dq, B, Hq, Hkv, N, softmax_scale, stream);
     return launch_status(e);
 }
 

@@ -33,6 +33,8 @@ _lib.fa_fwd.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, 
 _lib.fa_fwd.restype = _i
 _lib.fa_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
 _lib.fa_bwd.restype = _i
+_lib.fa_bwd_noalloc.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
+_lib.fa_bwd_noalloc.restype = _i
 _lib.fa_bwd_delta.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.fa_bwd_delta.restype = _i
 _lib.fa_bwd_dkdv.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p]
@@ -67,7 +69,8 @@ _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_abi_version.argtypes = []
 _lib.fa_abi_version.restype = _i
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_workspace_bytes",
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
+           "fa_bwd_workspace_bytes",
            "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_dropout", "fa_decode",
            "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes", "fa_status_string",
            "fa_abi_version")
@@ -90,6 +93,15 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal, 
            stream) -> int:
     return _lib.fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, int(causal),
                        float(softmax_scale), dtype, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, softmax_scale, dtype, stream) -> int:
+    return _lib.fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, int(causal), float(softmax_scale),
+                               dtype, stream)
+
+
+# bytes of the library-owned workspace behind fa_bwd_noalloc (FA_BWD_NOALLOC_MAX_BYTES)
+BWD_NOALLOC_MAX_BYTES = 16 << 20
 
 
 def fa_bwd_delta(o, dO, lse, ws, B, Hq, N, d, dtype, stream) -> int:

@@ -19,7 +19,8 @@
  *    `stream` (NULL = the default stream).  Its only mutable global state is
  *    a per-device cache of values fixed by the device and the code object
  *    (CU count, resident workgroups per CU of each kernel), filled on a
- *    device's first call; no argument or result of a call is kept.
+ *    device's first call, and the workspace array of fa_bwd_noalloc; no
+ *    argument or result of a call is kept.
  *  - Layouts are contiguous, row-major, head dimension fastest:
  *    Q, O, dO, dQ are [B, Hq, N, d]; K, V, dK, dV are [B, Hkv, N, d];
  *    LSE and the backward workspace are [B, Hq, N] float32.
@@ -145,6 +146,30 @@ fa_status_t fa_bwd_dq(const void* q, const void* k, const void* v,
                       int B, int Hq, int Hkv, int N, int d,
                       int causal, float softmax_scale, fa_dtype_t dtype,
                       hipStream_t stream);
+
+/*
+ * fa_bwd without a caller workspace, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, validation, kernels and results as
+ * fa_bwd, minus `delta_ws`: the workspace lives in a library-owned device
+ * array of FA_BWD_NOALLOC_MAX_BYTES (one copy on each device the library runs
+ * on, held until the process ends).  No call allocates or frees anything.
+ *  - fa_bwd_workspace_bytes(B, Hq, N) must be <= FA_BWD_NOALLOC_MAX_BYTES
+ *    (B * Hq * Np <= 2^21 rows), else FA_ERR_SHAPE before any HIP call.
+ *  - Every call on one device shares that device's array, and each call
+ *    rewrites every byte it reads: calls that overlap on one device (other
+ *    streams, other threads) race and must be serialised by the caller.
+ *  - The array's device address is looked up on the first call on each
+ *    device; if that fails the call returns FA_ERR_LAUNCH.
+ */
+#define FA_BWD_NOALLOC_MAX_BYTES (16u << 20)
+
+fa_status_t fa_bwd_noalloc(const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse,
+                           void* dq, void* dk, void* dv,
+                           int B, int Hq, int Hkv, int N, int d,
+                           int causal, float softmax_scale, fa_dtype_t dtype,
+                           hipStream_t stream);
 
 /*
  * Bytes of the backward workspace: 8 * B * Hq * Np with Np = N rounded up to

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     from exact_io_aware_50_amd import fa
     lib = ctypes.CDLL(fa.LIB_PATH)
     names = header_functions()
-    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_bwd_workspace_bytes", "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_decode",
                           "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_dropout",
                           "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
@@ -290,3 +290,23 @@ def test_decode_paged_validation():
     assert n >= 4 * (2 * 2) * 8 * 1 * 129
     assert fa.fa_decode_paged_workspace_bytes(2, 8, 2, 1, 8, 40, 128) == 0
 
+
+def test_bwd_noalloc_validation():
+    """fa_bwd_noalloc: fa_bwd's checks, plus the workspace limit of the library-owned array, all before any HIP
+    call (so none of these can touch a device)."""
+    from exact_io_aware_50_amd import fa
+    f = dict(q=A[0], k=A[1], v=A[2], o=A[3], dO=A[4], lse=A[5], dq=A[6], dk=A[7], dv=A[8], B=1, Hq=2, Hkv=2,
+             N=256, d=128, causal=1, softmax_scale=0.1, dtype=1, stream=None)
+    # B * Hq * Np rows of 8 bytes: 2^21 rows fit, one more 64-row block does not
+    assert fa.fa_bwd_workspace_bytes(1, 32, 65536) == fa.BWD_NOALLOC_MAX_BYTES
+    assert fa.fa_bwd_noalloc(**{**f, "B": 1, "Hq": 32, "Hkv": 32, "N": 65537}) == 2
+    assert fa.fa_bwd_noalloc(**{**f, "B": 3, "Hq": 64, "Hkv": 8, "N": 16384}) == 2
+    assert fa.fa_bwd_noalloc(**{**f, "dtype": 2}) == 3
+    assert fa.fa_bwd_noalloc(**{**f, "d": 96}) == 3
+    assert fa.fa_bwd_noalloc(**{**f, "Hq": 3}) == 2
+    assert fa.fa_bwd_noalloc(**{**f, "dq": None}) == 1
+    assert fa.fa_bwd_noalloc(**{**f, "lse": None}) == 1
+    assert fa.fa_bwd_noalloc(**{**f, "dk": A[0]}) == 6
+    assert fa.fa_bwd_noalloc(**{**f, "dv": f["dk"]}) == 6
+    assert fa.fa_bwd_noalloc(**{**f, "q": A[0] + 8}) == 4
+    assert fa.fa_bwd_noalloc(**{**f, "N": 0}) == 0          # empty problem: OK, nothing touched
