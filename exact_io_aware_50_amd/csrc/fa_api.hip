@@ -264,6 +264,26 @@ fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o,
                                                      softmax_scale, stream));
 }
 
+fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                           const float* lse, void* dq, void* dk, void* dv, float* delta_ws, int B, int Hq, int Hkv,
+                           int N, int d, int causal, double dropout_p, uint64_t seed, float softmax_scale,
+                           fa_dtype_t dtype, hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    if (!(dropout_p >= 0.0 && dropout_p < 1.0)) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    s = check_ptrs({q, k, v, o, dO, delta_ws}, {lse}, {dq, dk, dv}, {});
+    if (s != FA_OK) return s;
+    const uint32_t thr = (uint32_t)floor(dropout_p * 4294967296.0);
+    const float rkeep = (float)(1.0 / (1.0 - dropout_p));
+    hipError_t e = fa::launch_bwd_delta(dtype, d, o, dO, lse, delta_ws, B, Hq, N, stream, (float)(1.0 - dropout_p));
+    if (e == hipSuccess)
+        e = fa::launch_bwd_bf16_dropout(d, causal, q, k, v, dO, delta_ws, dq, dk, dv, B, Hq, Hkv, N, thr, seed, rkeep,
+                                        softmax_scale, stream);
+    return launch_status(e);
+}
+
 // Mask arrays of the block-sparse entry points (device int arrays).
 static fa_status_t check_bsparse(int N, const int* ptr, const int* idx, int nnz) {
     const int64_t nb = ((int64_t)N + FA_BSPARSE_BLOCK - 1) / FA_BSPARSE_BLOCK;

@@ -19,14 +19,16 @@
 namespace fa {
 
 // ------------------------------------------------------------ workspace: D, LSE*log2e
-// Row r of the padded [B*Hq][Np] layout: -D = -sum_c dO*O and LSE*log2(e) for
-// query rows < N; 0 and +infinity (zero probability) for padding rows.  -D
-// rather than D: the bf16 dK/dV kernel starts its dP accumulators from it.
+// Row r of the padded [B*Hq][Np] layout: -D * keep with D = sum_c dO*O, and
+// LSE*log2(e), for query rows < N; 0 and +infinity (zero probability) for
+// padding rows.  -D rather than D: the bf16 dK/dV kernel starts its dP
+// accumulators from it.  keep is 1, or 1 - p for the backward through dropout.
 template <class ET, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const typename ET::elem* __restrict__ O,
                                                         const typename ET::elem* __restrict__ dO,
                                                         const float* __restrict__ LSE, float* __restrict__ WSd,
-                                                        float* __restrict__ WSl, int N, int Np, int64_t rows) {
+                                                        float* __restrict__ WSl, int N, int Np, int64_t rows,
+                                                        float keep) {
     constexpr int TPR = D / 8, RPB = 256 / TPR;
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
     const int seg = threadIdx.x % TPR;
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const typename ET::elem*
 #pragma unroll
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (seg == 0 && row < rows) {
-        WSd[row] = -acc;
+        WSd[row] = -acc * keep;
         WSl[row] = valid ? LSE[bh * N + i] * kLog2e : INFINITY;
     }
 }
@@ -374,13 +376,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(
 
 template <class ET, int D>
 static hipError_t launch_delta(const void* o, const void* dO, const float* lse, float* ws, int B, int Hq, int N,
-                               hipStream_t st) {
+                               float keep, hipStream_t st) {
     using elem = typename ET::elem;
     const int Np = ws_rows(N);
     const int64_t rows = (int64_t)B * Hq * Np;
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((bwd_delta_kernel<ET, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                       (const elem*)o, (const elem*)dO, lse, ws, ws + rows, N, Np, rows);
+                       (const elem*)o, (const elem*)dO, lse, ws, ws + rows, N, Np, rows, keep);
     return hipGetLastError();
 }
 
@@ -409,11 +411,11 @@ static hipError_t launch_dq(const void* q, const void* k, const void* v, const v
 }
 
 hipError_t launch_bwd_delta(int dtype, int d, const void* o, const void* dO, const float* lse, float* ws, int B,
-                            int Hq, int N, hipStream_t st) {
-    if (dtype == 1 && d == 64) return launch_delta<BF16, 64>(o, dO, lse, ws, B, Hq, N, st);
-    if (dtype == 1 && d == 128) return launch_delta<BF16, 128>(o, dO, lse, ws, B, Hq, N, st);
-    if (dtype == 0 && d == 64) return launch_delta<F32, 64>(o, dO, lse, ws, B, Hq, N, st);
-    if (dtype == 0 && d == 128) return launch_delta<F32, 128>(o, dO, lse, ws, B, Hq, N, st);
+                            int Hq, int N, hipStream_t st, float keep) {
+    if (dtype == 1 && d == 64) return launch_delta<BF16, 64>(o, dO, lse, ws, B, Hq, N, keep, st);
+    if (dtype == 1 && d == 128) return launch_delta<BF16, 128>(o, dO, lse, ws, B, Hq, N, keep, st);
+    if (dtype == 0 && d == 64) return launch_delta<F32, 64>(o, dO, lse, ws, B, Hq, N, keep, st);
+    if (dtype == 0 && d == 128) return launch_delta<F32, 128>(o, dO, lse, ws, B, Hq, N, keep, st);
     return hipErrorInvalidValue;
 }
 

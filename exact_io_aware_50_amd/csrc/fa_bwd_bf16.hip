@@ -76,13 +76,21 @@ __device__ __forceinline__ void sched_dkdv_phase() {
 // BSP: block-sparse, key block kbk is seen by the query blocks bidx[bptr[kbk]
 // .. bptr[kbk+1]) (ascending, BNK rows each, BNK / BMQ steps per block; the
 // mask's column layout), clamped so that any layout stays in bounds.
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
+// DROP: the backward through attention dropout (the FlashAttention page of the
+// self-hosted LLM glossary: dropout is fused into the kernel; its mask is
+// regenerated here from the same counter-based generator, not stored).  With
+// Z the keep mask and r = 1/(1 - p), O = (Z o P) r V, so dV = r (Z o P)^T dO
+// and dS = P o (Z o dP r - D).  The workspace then holds -D (1 - p), the dP
+// accumulator starts from it, and dS = r P o (Z ? acc : -D (1 - p)); the
+// factor r goes into the final scales of dK and dV.
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
 __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int n_rows, int Npad, float c2,
-    float scale, int W, int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz) {
+    float scale, int W, int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz, DropArgs drop) {
     static_assert(!(LOCAL && BSP), "one sparsity pattern at a time");
+    static_assert(!(DROP && (LOCAL || BSP)), "dropout with the dense masks only");
     using Cfg = KVBf16Cfg<D>;
     using QT = typename Cfg::QT;
     constexpr int NW = Cfg::kWaves, BNK = Cfg::BNK, BMQ = Cfg::BMQ, QB = Cfg::QB, NS = Cfg::kStages;
@@ -296,7 +304,7 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         // X(i): step i's query block is xq.  `mid` (the phase's loads) is
         // issued after the first query block's exponentials, whose results it
         // waits for
-        int xq = qt0, jx = 0;
+        int xq = qt0, jx = 0, hx = 0;                   // (dropout) hx: the step's head within the group
         auto softmax = [&](int i, auto&& mid) __attribute__((always_inline)) {
             if (i >= total) {
                 mid();
@@ -312,6 +320,8 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
                 q0 = xq * BMQ;
                 if (++xq == qt1) xq = qt0;
             }
+            const int hstep = hx;
+            if constexpr (DROP) hx += xq == qt0;
             const float* sl = (const float*)(smem + (i % NS) * Cfg::kStageBytes + 2 * QT::kBytes);
             // causal: key krow is hidden from query q0 + 32*qb + row(r) iff
             // delta > 8*(r/4) + r%4, delta = krow - q0 - 32*qb - 4*hh; steps whose
@@ -348,8 +358,42 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
                     for (int r = 0; r < 16; ++r)
                         if (dw + 8 * (r / 4) + r % 4 >= W) sacc[qb][r] = 0.f;
                 }
+                if constexpr (DROP) {
+                    // keep bits of this lane's key krow for the queries
+                    // q0 + 32 qb + 8 gq + 4 hh + e (element 4 gq + e).  The call for
+                    // query i serves keys 4 (krow / 4) .. + 3, the four lanes of a
+                    // quad: lane x of the quad makes the calls of the queries with
+                    // e = x, and a quad transpose hands word y of each call to lane y
+                    int ln = lane;
+                    asm volatile("" : "+v"(ln));
+                    const int x = ln & 3;
+                    const uint32_t bhq = (uint32_t)(b * Hq + g * G + hstep);
+                    uint32_t zw[4][4];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dpacc[qb][r] = sacc[qb][r] * dpacc[qb][r];
+                    for (int gq = 0; gq < 4; ++gq) {
+                        zw[gq][0] = (uint32_t)krow >> 2;
+                        zw[gq][1] = (uint32_t)(q0 + 32 * qb + 8 * gq + 4 * (ln >> 5) + x);
+                        zw[gq][2] = bhq;
+                        zw[gq][3] = 0u;
+                        philox4x32_10(zw[gq], drop.key0, drop.key1);
+                    }
+                    const float* sd = sl + BMQ;       // -D (1 - p) of the step's rows: the dP accumulator's start
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        quad_transpose(zw[gq], x);
+                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sd + 32 * qb + 8 * gq + 4 * hh);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 4 * gq + e;
+                            const bool keep = zw[gq][e] >= drop.thr;
+                            dpacc[qb][r] = sacc[qb][r] * (keep ? dpacc[qb][r] : d4[e]);
+                            sacc[qb][r] = keep ? sacc[qb][r] : 0.f;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dpacc[qb][r] = sacc[qb][r] * dpacc[qb][r];
+                }
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     pb[qb][t] = pack_bf16x8(sacc[qb], 8 * t);
@@ -426,16 +470,23 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
             const int64_t row = ((int64_t)b * Hkv + g) * N + kw + (le & 31);
             uint16_t* dKr = dK + row * D;
             uint16_t* dVr = dV + row * D;
+            const float sk = DROP ? scale * drop.rkeep : scale;     // (dropout) r = 1/(1 - p) into both
+            const float sv = DROP ? drop.rkeep : 1.f;
 #pragma unroll
             for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     const int c = 32 * ct + 8 * gq + 4 * (le >> 5);
                     u32x2 wk, wv;
-                    wk[0] = pack_bf16x2(dkacc[ct][4 * gq] * scale, dkacc[ct][4 * gq + 1] * scale);
-                    wk[1] = pack_bf16x2(dkacc[ct][4 * gq + 2] * scale, dkacc[ct][4 * gq + 3] * scale);
-                    wv[0] = pack_bf16x2(dvacc[ct][4 * gq], dvacc[ct][4 * gq + 1]);
-                    wv[1] = pack_bf16x2(dvacc[ct][4 * gq + 2], dvacc[ct][4 * gq + 3]);
+                    wk[0] = pack_bf16x2(dkacc[ct][4 * gq] * sk, dkacc[ct][4 * gq + 1] * sk);
+                    wk[1] = pack_bf16x2(dkacc[ct][4 * gq + 2] * sk, dkacc[ct][4 * gq + 3] * sk);
+                    if constexpr (DROP) {
+                        wv[0] = pack_bf16x2(dvacc[ct][4 * gq] * sv, dvacc[ct][4 * gq + 1] * sv);
+                        wv[1] = pack_bf16x2(dvacc[ct][4 * gq + 2] * sv, dvacc[ct][4 * gq + 3] * sv);
+                    } else {
+                        wv[0] = pack_bf16x2(dvacc[ct][4 * gq], dvacc[ct][4 * gq + 1]);
+                        wv[1] = pack_bf16x2(dvacc[ct][4 * gq + 2], dvacc[ct][4 * gq + 3]);
+                    }
                     *reinterpret_cast<u32x2*>(dKr + c) = wk;
                     *reinterpret_cast<u32x2*>(dVr + c) = wv;
                 }
@@ -490,13 +541,17 @@ __device__ __forceinline__ void sched_dq_phase() {
 // the first one its first row can see.
 // BSP: block-sparse, row block mb sees the key blocks bidx[bptr[mb] ..
 // bptr[mb+1]) (ascending, BM keys each), clamped as in the forward.
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
+// DROP: through attention dropout, as in the dK/dV kernel: the workspace holds
+// -D (1 - p), dS = r P o (Z ? dP + (-D (1 - p)) : -D (1 - p)) with the mask
+// regenerated per element, and r = 1/(1 - p) goes into dQ's final scale.
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
 __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
     uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int n_rows, int Npad, float c2, float scale, int W,
-    int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz) {
+    int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz, DropArgs drop) {
     static_assert(!(LOCAL && BSP), "one sparsity pattern at a time");
+    static_assert(!(DROP && (LOCAL || BSP)), "dropout with the dense masks only");
     using Cfg = QBf16Cfg<D>;
     using KT = typename Cfg::KT;
     constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BNK = Cfg::BNK, NS = Cfg::kStages, KB = BNK / 32;
@@ -666,8 +721,26 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
             }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
+                if constexpr (DROP) {
+                    // keys k0 + 32 kb + 8 gq + 4 hh + e (element 4 gq + e): one
+                    // Philox call per run of four, word e for key offset e
+                    const uint32_t bhq = (uint32_t)(b * Hq + h);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dpacc[kb][r] = sacc[kb][r] * (dpacc[kb][r] + dq_nd);
+                    for (int gq = 0; gq < 4; ++gq) {
+                        uint32_t c[4] = {(uint32_t)((k0 + 32 * kb + 8 * gq) >> 2) + (uint32_t)hh, (uint32_t)qrow,
+                                         bhq, 0u};
+                        philox4x32_10(c, drop.key0, drop.key1);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 4 * gq + e;
+                            const float x = dpacc[kb][r] + dq_nd;
+                            dpacc[kb][r] = sacc[kb][r] * (c[e] >= drop.thr ? x : dq_nd);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dpacc[kb][r] = sacc[kb][r] * (dpacc[kb][r] + dq_nd);
+                }
                 dsf[kb][0] = pack_bf16x8(dpacc[kb], 0);
                 dsf[kb][1] = pack_bf16x8(dpacc[kb], 8);
             }
@@ -729,51 +802,53 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
             int le = lane;
             asm volatile("" : "+v"(le));
             uint16_t* dQr = dQ + (rowbase + qw + (le & 31)) * D + 4 * (le >> 5);
+            const float sq = DROP ? scale * drop.rkeep : scale;     // (dropout) r = 1/(1 - p)
 #pragma unroll
             for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     u32x2 w;
-                    w[0] = pack_bf16x2(dqacc[ct][4 * gq] * scale, dqacc[ct][4 * gq + 1] * scale);
-                    w[1] = pack_bf16x2(dqacc[ct][4 * gq + 2] * scale, dqacc[ct][4 * gq + 3] * scale);
+                    w[0] = pack_bf16x2(dqacc[ct][4 * gq] * sq, dqacc[ct][4 * gq + 1] * sq);
+                    w[1] = pack_bf16x2(dqacc[ct][4 * gq + 2] * sq, dqacc[ct][4 * gq + 3] * sq);
                     *reinterpret_cast<u32x2*>(dQr + 32 * ct + 8 * gq) = w;
                 }
         }
     }
 }
 
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
 static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* ws,
                               void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, hipStream_t st,
                               int W = 0, int S = 0, const int* bptr = nullptr, const int* bidx = nullptr,
-                              int nnz = 0) {
+                              int nnz = 0, DropArgs drop = {0u, 0u, 0u, 1.f}) {
     using Cfg = KVBf16Cfg<D>;
     const int nkb = (N + Cfg::BNK - 1) / Cfg::BNK;
     const int Np = ws_rows(N);
     static PerDevice slots;
-    const int grid = persistent_grid((const void*)bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP>, Cfg::kThreads,
-                                     nkb * Hkv * B, slots);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0,
-                       st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
-                       ws + (int64_t)B * Hq * Np, (uint16_t*)dk, (uint16_t*)dv, B, Hq, Hkv, N, Np, scale * kLog2e,
-                       scale, W, S, bptr, bidx, nnz);
+    const int grid = persistent_grid((const void*)bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>,
+                                     Cfg::kThreads, nkb * Hkv * B, slots);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>), dim3((unsigned)grid),
+                       dim3(Cfg::kThreads), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                       (const uint16_t*)dO, ws, ws + (int64_t)B * Hq * Np, (uint16_t*)dk, (uint16_t*)dv, B, Hq, Hkv, N,
+                       Np, scale * kLog2e, scale, W, S, bptr, bidx, nnz, drop);
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
 static hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dq,
                             int B, int Hq, int Hkv, int N, float scale, hipStream_t st, int W = 0, int S = 0,
-                            const int* bptr = nullptr, const int* bidx = nullptr, int nnz = 0) {
+                            const int* bptr = nullptr, const int* bidx = nullptr, int nnz = 0,
+                            DropArgs drop = {0u, 0u, 0u, 1.f}) {
     using Cfg = QBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
     const int Np = ws_rows(N);
     static PerDevice slots;
-    const int grid =
-        persistent_grid((const void*)bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP>, Cfg::kThreads, nmb * Hq * B, slots);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0,
-                       st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, ws,
-                       ws + (int64_t)B * Hq * Np, (uint16_t*)dq, B, Hq, Hkv, N, Np, scale * kLog2e, scale, W, S,
-                       bptr, bidx, nnz);
+    const int grid = persistent_grid((const void*)bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>, Cfg::kThreads,
+                                     nmb * Hq * B, slots);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>), dim3((unsigned)grid),
+                       dim3(Cfg::kThreads), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                       (const uint16_t*)dO, ws, ws + (int64_t)B * Hq * Np, (uint16_t*)dq, B, Hq, Hkv, N, Np,
+                       scale * kLog2e, scale, W, S, bptr, bidx, nnz, drop);
     return hipGetLastError();
 }
 
@@ -826,6 +901,23 @@ hipError_t launch_bwd_dq_bf16_local(int d, const void* q, const void* k, const v
     if (d == 64) return launch_dq<64, true, true>(q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st, W, S);
     if (d == 128) return launch_dq<128, true, true>(q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st, W, S);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_bf16_dropout(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
+                                   const float* ws, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                                   uint32_t thr, uint64_t seed, float rkeep, float scale, hipStream_t st) {
+    const DropArgs dr{thr, (uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32), rkeep};
+#define KV q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st, 0, 0, nullptr, nullptr, 0, dr
+#define QA q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st, 0, 0, nullptr, nullptr, 0, dr
+    hipError_t e = hipErrorInvalidValue;
+    if (d == 64) e = causal ? launch_dkdv<64, true, false, false, true>(KV) : launch_dkdv<64, false, false, false, true>(KV);
+    if (d == 128)
+        e = causal ? launch_dkdv<128, true, false, false, true>(KV) : launch_dkdv<128, false, false, false, true>(KV);
+    if (e != hipSuccess) return e;
+    if (d == 64) return causal ? launch_dq<64, true, false, false, true>(QA) : launch_dq<64, false, false, false, true>(QA);
+    return causal ? launch_dq<128, true, false, false, true>(QA) : launch_dq<128, false, false, false, true>(QA);
+#undef KV
+#undef QA
 }
 
 }  // namespace fa

@@ -484,6 +484,60 @@ struct LdsTile {
     }
 };
 
+// ----------------------------------------------------------------------------
+// Attention dropout.  Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011):
+// a four-word counter and a two-word key; each of ten rounds forms two 32 x 32
+// -> 64-bit products of counter words 0 and 2, builds the new counter from
+// their halves, the other two words and the key, and bumps the key by the
+// Weyl constants.  The 64-bit product form compiles to one v_mad_u64_u32 per
+// product.  Returns the four output words in c.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        c[1] = (uint32_t)p1;
+        c[3] = (uint32_t)p0;
+        c[0] = n0;
+        c[2] = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+}
+
+// Dropout parameters: element (query i, key j) of (batch b, query head h) is
+// kept iff word j % 4 of Philox((j / 4, i, b * Hq + h, 0), (key0, key1)) is
+// >= thr; kept probabilities are scaled by rkeep = 1 / (1 - p).
+struct DropArgs {
+    uint32_t thr, key0, key1;
+    float rkeep;
+};
+
+// 4 x 4 transpose of 32-bit words inside each quad of lanes: lane x of a quad
+// holds a[0..3]; afterwards lane y holds (a[y] of lane 0, ..., a[y] of lane 3).
+// Two butterfly stages (partners x ^ 1, then x ^ 2), each lane sending the
+// words whose index bit differs from its own lane bit.
+__device__ __forceinline__ void quad_transpose(uint32_t a[4], int x) {
+    const bool b0 = x & 1, b1 = x & 2;
+#pragma unroll
+    for (int k = 0; k < 4; k += 2) {
+        const uint32_t s = b0 ? a[k] : a[k + 1];
+        const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)s, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+        a[k] = b0 ? r : a[k];
+        a[k + 1] = b0 ? a[k + 1] : r;
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t s = b1 ? a[k] : a[k + 2];
+        const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)s, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+        a[k] = b1 ? r : a[k];
+        a[k + 2] = b1 ? a[k + 2] : r;
+    }
+}
+
 __device__ __forceinline__ f32x16 mma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);

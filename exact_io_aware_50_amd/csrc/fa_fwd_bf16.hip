@@ -88,32 +88,6 @@ __device__ __forceinline__ void sched_gemm_phase() {
 // each; with CAUSAL the keys past the diagonal are masked as well.  Offsets are
 // clamped to [0, nnz) and block indices to the block count, so any layout keeps
 // every access in bounds.  A row that sees no key gets O = 0 and LSE = -inf.
-// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011): counter c, key
-// (k0, k1); ten rounds of two 32 x 32 -> 64-bit products with the Weyl key
-// schedule.  Returns the four output words in c.
-__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        const uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
-        const uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
-        const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
-        c[0] = n0;
-        c[1] = lo1;
-        c[2] = n2;
-        c[3] = lo0;
-        k0 += 0x9E3779B9u;
-        k1 += 0xBB67AE85u;
-    }
-}
-
-// Dropout parameters: element (query i, key j) of (batch b, query head h) is
-// kept iff word j % 4 of Philox((j / 4, i, b * Hq + h, 0), (key0, key1)) is
-// >= thr; kept probabilities are scaled by rkeep = 1 / (1 - p).
-struct DropArgs {
-    uint32_t thr, key0, key1;
-    float rkeep;
-};
-
 // DROP: attention dropout on the normalised probabilities (the FlashAttention
 // page of the self-hosted LLM glossary: dropout is one of the operations fused
 // into the kernel).  The normaliser and LSE are those of the undropped softmax.

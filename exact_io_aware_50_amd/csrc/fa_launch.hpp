@@ -72,8 +72,9 @@ hipError_t launch_fwd_fp8(int d, int causal, const void* q, const void* k, const
 // Rows per (batch, head) in the backward workspace: N rounded up to 64.
 inline int ws_rows(int N) { return (N + 63) / 64 * 64; }
 
+// keep: the factor on -D in the workspace (1, or 1 - p through dropout)
 hipError_t launch_bwd_delta(int dtype, int d, const void* o, const void* dO, const float* lse, float* ws, int B,
-                            int Hq, int N, hipStream_t st);
+                            int Hq, int N, hipStream_t st, float keep = 1.f);
 
 hipError_t launch_bwd_dkdv(int dtype, int d, int causal, const void* q, const void* k, const void* v,
                            const void* dO, const float* ws, void* dk, void* dv, int B, int Hq, int Hkv, int N,
@@ -118,6 +119,12 @@ hipError_t launch_bwd_bf16_bsparse(int d, int causal, const void* q, const void*
 hipError_t launch_fwd_bf16_dropout(int d, int causal, const void* q, const void* k, const void* v, void* o,
                                    float* lse, int B, int Hq, int Hkv, int N, uint32_t thr, uint64_t seed, float rkeep,
                                    float scale, hipStream_t st);
+
+// Backward through that dropout (the same mask regenerated), bf16: dK/dV then
+// dQ, from a workspace written by launch_bwd_delta with keep = 1 - p.
+hipError_t launch_bwd_bf16_dropout(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
+                                   const float* ws, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                                   uint32_t thr, uint64_t seed, float rkeep, float scale, hipStream_t st);
 
 hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
 

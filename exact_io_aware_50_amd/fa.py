@@ -52,6 +52,8 @@ _lib.fa_bwd_local.restype = _i
 _d = ctypes.c_double
 _lib.fa_fwd_dropout.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _d, ctypes.c_uint64, _f, _i, _p]
 _lib.fa_fwd_dropout.restype = _i
+_lib.fa_bwd_dropout.argtypes = [_p] * 10 + [_i] * 6 + [_d, ctypes.c_uint64, _f, _i, _p]
+_lib.fa_bwd_dropout.restype = _i
 _lib.fa_fwd_bsparse.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _i, _f, _i, _p]
 _lib.fa_fwd_bsparse.restype = _i
 _lib.fa_bwd_bsparse.argtypes = ([_p] * 10 + [_i] * 6 + [_p] * 4 + [_i, _f, _i, _p])
@@ -71,7 +73,7 @@ _lib.fa_abi_version.restype = _i
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_bwd_workspace_bytes",
-           "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_dropout", "fa_decode",
+           "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_dropout", "fa_bwd_dropout", "fa_decode",
            "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes", "fa_status_string",
            "fa_abi_version")
 
@@ -252,6 +254,27 @@ def fa_bwd_bsparse(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, 
 def fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, dropout_p, seed, softmax_scale, dtype, stream) -> int:
     return _lib.fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, float(dropout_p), int(seed),
                                float(softmax_scale), dtype, stream)
+
+
+def fa_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal, dropout_p, seed,
+                   softmax_scale, dtype, stream) -> int:
+    return _lib.fa_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal,
+                               float(dropout_p), int(seed), float(softmax_scale), dtype, stream)
+
+
+def bwd_dropout(q, k, v, o, do, lse, causal: bool, scale: float, dropout_p: float, seed: int, stream=None,
+                workspace=None):
+    """(dq, dk, dv, workspace) through the dropout of ``fwd_dropout`` (same p and seed; o, lse its outputs)."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_bytes(B, Hq, N) // 4, dtype=torch.float32, device=q.device)
+    _check(fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, N, d,
+                          int(causal), dropout_p, seed, scale, _dtype_code(q), _stream_handle(stream)),
+           "fa_bwd_dropout")
+    return dq, dk, dv, workspace
 
 
 def fwd_dropout(q, k, v, causal: bool, scale: float, dropout_p: float, seed: int, stream=None):

@@ -241,6 +241,24 @@ fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v,
                            float softmax_scale, fa_dtype_t dtype, hipStream_t stream);
 
 /*
+ * Backward through the dropout of fa_fwd_dropout (same pages).  The keep mask
+ * Z is regenerated from (dropout_p, seed), never stored.  With r = 1/(1 - p)
+ * and P the undropped softmax: dV = r (Z o P)^T dO, dP = r Z o (dO V^T),
+ * D = rowsum(dO o O) (= rowsum(P o dP), O the dropped output), dS = P o (dP - D),
+ * dQ = scale dS K, dK = scale dS^T Q, K/V gradients summed over each group.
+ * Same arguments, layouts, workspace and errors as fa_bwd (bf16 only) plus the
+ * dropout_p and seed given to fa_fwd_dropout; o and lse are its outputs.  The
+ * workspace holds -D (1 - p) instead of -D.
+ */
+fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse,
+                           void* dq, void* dk, void* dv,
+                           float* delta_ws,
+                           int B, int Hq, int Hkv, int N, int d, int causal,
+                           double dropout_p, uint64_t seed,
+                           float softmax_scale, fa_dtype_t dtype, hipStream_t stream);
+
+/*
  * Block-sparse attention: key j is visible to query i iff block
  * (i / FA_BSPARSE_BLOCK, j / FA_BSPARSE_BLOCK) of the mask is on (and, with
  * causal = 1, j <= i).  The FlashAttention legal glossary, entry

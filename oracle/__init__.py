@@ -48,6 +48,7 @@ from .dropout import (  # noqa: F401,E402
     backward_dropout,
     drop_threshold,
     forward_dropout,
+    head_backward_dropout,
     keep_mask,
     philox4x32_10,
 )

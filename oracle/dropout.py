@@ -83,13 +83,33 @@ def forward_dropout(q, k, v, causal, scale, p, seed):
     return O, L
 
 
+def head_backward_dropout(qh, kg, vg, doh, b, h, Hq, causal, scale, p, seed):
+    """One query head's share of the backward through dropout: (dq_h, dk_h, dv_h, O_h).
+
+    qh, doh [N, d] of (batch b, query head h); kg, vg [N, d] of its K/V head.
+    The chain rule of O = ((Z o P) / (1 - p)) V, Z fixed by the seed: with
+    Pd = Z o P / (1 - p), dV = Pd^T dO, dPd = dO V^T, dP = Z o dPd / (1 - p), and
+    through the softmax dS = P o (dP - D) with D_i = sum_j P_ij dP_ij = dO_i . O_i;
+    then dQ = scale dS K and dK = scale dS^T Q.  dk_h, dv_h are this head's terms
+    of its K/V head's gradients (a group sums them over its query heads)."""
+    qh, kg, vg, doh = (np.asarray(x, dtype=np.float64) for x in (qh, kg, vg, doh))
+    N = qh.shape[0]
+    _, P, _, _ = probabilities(qh, kg, scale, causal)
+    Z = keep_mask(b, h, Hq, np.arange(N), kg.shape[0], p, seed)
+    Pd = np.where(Z, P, 0.0) / (1.0 - p)
+    O = Pd @ vg
+    dv = Pd.T @ doh
+    dP = np.where(Z, doh @ vg.T, 0.0) / (1.0 - p)
+    D = np.sum(doh * O, axis=1)
+    dS = P * (dP - D[:, None])
+    return scale * (dS @ kg), scale * (dS.T @ qh), dv, O
+
+
 def backward_dropout(q, k, v, do, causal, scale, p, seed):
     """dQ, dK, dV of O = ((Z o P) / (1 - p)) V for a loss with dL/dO = dO; returns (dq, dk, dv, O).
 
-    The chain rule of that definition, Z fixed by the seed: with Pd = Z o P / (1 - p),
-    dV = Pd^T dO, dPd = dO V^T, dP = Z o dPd / (1 - p), and through the softmax
-    dS = P o (dP - D) with D_i = sum_j P_ij dP_ij = dO_i . O_i; then dQ = scale dS K and
-    dK = scale dS^T Q.  The K/V gradients of a group sum over its query heads."""
+    Every (batch, query head) through head_backward_dropout; the K/V gradients
+    of a group sum over its query heads."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -101,14 +121,8 @@ def backward_dropout(q, k, v, do, causal, scale, p, seed):
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            _, P, _, _ = probabilities(q[b, h], k[b, g], scale, causal)
-            Z = keep_mask(b, h, Hq, np.arange(N), k.shape[2], p, seed)
-            Pd = np.where(Z, P, 0.0) / (1.0 - p)
-            O[b, h] = Pd @ v[b, g]
-            dv[b, g] += Pd.T @ do[b, h]
-            dP = np.where(Z, do[b, h] @ v[b, g].T, 0.0) / (1.0 - p)
-            D = np.sum(do[b, h] * O[b, h], axis=1)
-            dS = P * (dP - D[:, None])
-            dq[b, h] = scale * (dS @ k[b, g])
-            dk[b, g] += scale * (dS.T @ q[b, h])
+            dq[b, h], dkh, dvh, O[b, h] = head_backward_dropout(q[b, h], k[b, g], v[b, g], do[b, h], b, h, Hq,
+                                                                causal, scale, p, seed)
+            dk[b, g] += dkh
+            dv[b, g] += dvh
     return dq, dk, dv, O
