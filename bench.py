@@ -375,6 +375,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-dropout", action="store_true", help="skip the attention-dropout leg")
     ap.add_argument("--no-gemm-reference", action="store_true",
                     help="skip the vendor bf16 GEMM timed for context (practical MFMA rate on this data)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode (KV cache) leg")
@@ -469,6 +470,7 @@ def main():
             gbs = delta_bytes(w) / (t * 1e-3) / 1e9
             ent.update(gbs=round(gbs, 1), frac_peak=round(gbs / PEAK_HBM_GBS, 4))
         kern[n] = ent
+    bwd_ms = per["bwd_delta"] + per["bwd_dkdv"] + per["bwd_dq"]
     dom = max((n for n in per if n in kfl), key=lambda n: per[n])
     ach = kfl[dom] / (per[dom] * 1e-3) / 1e12
     roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
@@ -521,6 +523,60 @@ def main():
                              "frac_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
                              "note": "E4M3 forward of the same shape, inputs quantised per tensor outside the timing"}
         log(f"fp8 forward {t8:.3f} ms ({tf8:.0f} TFLOP/s)")
+        if d == 128:
+            # the backward of that forward (fa_bwd_fp8): dO quantised per tensor outside the timing
+            do8, sdo = fa.quantize_fp8(do)
+            ds4 = torch.cat([sq, sk, sv, sdo])
+            g8 = [torch.empty(t.shape, dtype=torch.bfloat16, device=dev) for t in (q, k, v)]
+            run8b = lambda: check(fa.fa_bwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o8.data_ptr(),
+                                                do8.data_ptr(), lse.data_ptr(), ds4.data_ptr(), g8[0].data_ptr(),
+                                                g8[1].data_ptr(), g8[2].data_ptr(), ws.data_ptr(), B, Hq, Hkv, N, d,
+                                                w.causal, w.scale, sh), "fa_bwd_fp8")
+            for _ in range(args.warmup):
+                run8b()
+            e0.record(stream)
+            for _ in range(args.steps):
+                run8b()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tb8 = e0.elapsed_time(e1) / args.steps
+            tfb8 = 2.5 * fwd_fl / (tb8 * 1e-3) / 1e12
+            result["fp8_bwd"] = {"ms": round(tb8, 4), "tflops": round(tfb8, 1),
+                                 "frac_fp8_peak": round(tfb8 / PEAK_FP8_TFLOPS, 4),
+                                 "vs_bf16_bwd": round(bwd_ms / tb8, 3),
+                                 "note": "fa_bwd_fp8 (delta + dK/dV + dQ) of the same shape; credited 2.5x forward"}
+            log(f"fp8 backward {tb8:.3f} ms ({tfb8:.0f} TFLOP/s, {bwd_ms / tb8:.2f}x the bf16 backward)")
+
+    if not args.no_dropout and w.dtype == "bf16" and d == 128:
+        # attention dropout (p = 0.125): forward and backward through the regenerated mask
+        p_drop, seed = 0.125, 2026
+        od, lsed = torch.empty_like(q), torch.empty_like(lse)
+        gd = [torch.empty_like(t) for t in (q, k, v)]
+        rund = lambda: check(fa.fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), od.data_ptr(),
+                                               lsed.data_ptr(), B, Hq, Hkv, N, d, w.causal, p_drop, seed, w.scale,
+                                               fa.FA_DTYPE_BF16, sh), "fa_fwd_dropout")
+        rundb = lambda: check(fa.fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), od.data_ptr(),
+                                                do.data_ptr(), lsed.data_ptr(), gd[0].data_ptr(), gd[1].data_ptr(),
+                                                gd[2].data_ptr(), ws.data_ptr(), B, Hq, Hkv, N, d, w.causal, p_drop,
+                                                seed, w.scale, fa.FA_DTYPE_BF16, sh), "fa_bwd_dropout")
+        times = []
+        for fn in (rund, rundb):
+            for _ in range(args.warmup):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / args.steps)
+        fwd_ms = kern["fwd"]["ms"]
+        result["dropout"] = {"p": p_drop, "fwd_ms": round(times[0], 4), "bwd_ms": round(times[1], 4),
+                             "fwd_vs_plain": round(times[0] / fwd_ms, 3), "bwd_vs_plain": round(times[1] / bwd_ms, 3),
+                             "note": "fa_fwd_dropout / fa_bwd_dropout on the same shape (Philox4x32-10 keep mask "
+                                     "regenerated in every kernel); ratios to the plain forward / backward"}
+        log(f"dropout p={p_drop}: fwd {times[0]:.3f} ms ({times[0] / fwd_ms:.2f}x), bwd {times[1]:.3f} ms "
+            f"({times[1] / bwd_ms:.2f}x)")
 
     if not args.no_local:
         result["local"] = local_leg(torch, fa, I, dev, stream, args)

@@ -284,6 +284,19 @@ fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const vo
     return launch_status(e);
 }
 
+fa_status_t fa_bwd_fp8(const void* q8, const void* k8, const void* v8, const void* o, const void* do8,
+                       const float* lse, const float* descale, void* dq, void* dk, void* dv, float* delta_ws, int B,
+                       int Hq, int Hkv, int N, int d, int causal, float softmax_scale, hipStream_t stream) {
+    bool empty = false;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    s = check_ptrs({q8, k8, v8, o, do8, delta_ws}, {lse, descale}, {dq, dk, dv}, {});
+    if (s != FA_OK) return s;
+    return launch_status(fa::launch_bwd_fp8(causal, q8, k8, v8, o, do8, lse, descale, delta_ws, dq, dk, dv, B, Hq,
+                                            Hkv, N, softmax_scale, stream));
+}
+
 // Mask arrays of the block-sparse entry points (device int arrays).
 static fa_status_t check_bsparse(int N, const int* ptr, const int* idx, int nnz) {
     const int64_t nb = ((int64_t)N + FA_BSPARSE_BLOCK - 1) / FA_BSPARSE_BLOCK;

@@ -126,6 +126,11 @@ hipError_t launch_bwd_bf16_dropout(int d, int causal, const void* q, const void*
                                    const float* ws, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
                                    uint32_t thr, uint64_t seed, float rkeep, float scale, hipStream_t st);
 
+// FP8 backward (d = 128): delta, dK/dV and dQ kernels; descale = (s_Q, s_K, s_V, s_dO).
+hipError_t launch_bwd_fp8(int causal, const void* q, const void* k, const void* v, const void* o, const void* dO,
+                          const float* lse, const float* descale, float* ws, void* dq, void* dk, void* dv, int B,
+                          int Hq, int Hkv, int N, float scale, hipStream_t st);
+
 hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
 
 // Decode split over the keys: nrb blocks of 32 packed query rows per K/V head,

@@ -54,6 +54,8 @@ _lib.fa_fwd_dropout.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _d, 
 _lib.fa_fwd_dropout.restype = _i
 _lib.fa_bwd_dropout.argtypes = [_p] * 10 + [_i] * 6 + [_d, ctypes.c_uint64, _f, _i, _p]
 _lib.fa_bwd_dropout.restype = _i
+_lib.fa_bwd_fp8.argtypes = [_p] * 11 + [_i] * 6 + [_f, _p]
+_lib.fa_bwd_fp8.restype = _i
 _lib.fa_fwd_bsparse.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _i, _f, _i, _p]
 _lib.fa_fwd_bsparse.restype = _i
 _lib.fa_bwd_bsparse.argtypes = ([_p] * 10 + [_i] * 6 + [_p] * 4 + [_i, _f, _i, _p])
@@ -73,7 +75,7 @@ _lib.fa_abi_version.restype = _i
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_bwd_workspace_bytes",
-           "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_dropout", "fa_bwd_dropout", "fa_decode",
+           "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd_fp8", "fa_decode",
            "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes", "fa_status_string",
            "fa_abi_version")
 
@@ -429,6 +431,28 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, causal: bool, scale
                            maxb, bs, nblk, d, causal, scale, _dtype_code(q), _stream_handle(stream)),
            "fa_decode_paged")
     return o, lse
+
+
+def fa_bwd_fp8(q8, k8, v8, o, dO8, lse, descale, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal, softmax_scale,
+               stream) -> int:
+    return _lib.fa_bwd_fp8(q8, k8, v8, o, dO8, lse, descale, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, int(causal),
+                           float(softmax_scale), stream)
+
+
+def bwd_fp8(q8, k8, v8, o, do8, lse, descale, causal: bool, scale: float, stream=None, workspace=None):
+    """(dq, dk, dv, workspace), bf16, through the FP8 forward: q8, k8, v8, do8 E4M3 codes (uint8), o and lse the
+    FP8 forward's outputs, descale float32[4] = (s_Q, s_K, s_V, s_dO) on the device."""
+    torch = _torch()
+    B, Hq, Hkv, N, d = _shape(q8, k8)
+    dq = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    dk = torch.empty(k8.shape, dtype=torch.bfloat16, device=q8.device)
+    dv = torch.empty(v8.shape, dtype=torch.bfloat16, device=q8.device)
+    if workspace is None:
+        workspace = torch.empty(fa_bwd_workspace_bytes(B, Hq, N) // 4, dtype=torch.float32, device=q8.device)
+    _check(fa_bwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), do8.data_ptr(), lse.data_ptr(),
+                      descale.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Hq,
+                      Hkv, N, d, int(causal), scale, _stream_handle(stream)), "fa_bwd_fp8")
+    return dq, dk, dv, workspace
 
 
 def quantize_fp8(x, stream=None):

@@ -180,6 +180,35 @@ fa_status_t fa_bwd_noalloc(const void* q, const void* k, const void* v,
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N);
 
 /*
+ * FP8 backward: dQ, dK, dV of the FP8 forward (fa_fwd with FA_DTYPE_FP8_E4M3).
+ * The FlashAttention legal glossary (FlashAttention-3 paragraph) and "flash
+ * attention io aware" (section "Flash Attention 2 and 3") name FP8 attention
+ * without a recipe; this one carries the forward's through the recomputation
+ * of the glossary's backward paragraph.  S = Q K^T and dP = dO V^T run on the
+ * fp8 matrix cores; dQ = scale dS K too, dS rounded to E4M3 after a power-of-
+ * two scale per query and block of 32 keys that the matrix core divides back
+ * out; dK = scale dS^T Q and dV = P^T dO run on the bf16 matrix cores (P, dS
+ * rounded to bf16, the E4M3 codes of Q and dO widened exactly).  float32
+ * accumulation; D = rowsum(dO o O).
+ *   q8, k8, v8, do8 : E4M3 codes, [B,Hq,N,d], [B,Hkv,N,d], [B,Hkv,N,d],
+ *                     [B,Hq,N,d] (fa_quantize_fp8 of the bf16 tensors)
+ *   o, lse          : the FP8 forward's outputs (o bf16)
+ *   descale         : device float[4] = (s_Q, s_K, s_V, s_dO)
+ *   dq, dk, dv      : bf16 outputs, [B,Hq,N,d], [B,Hkv,N,d] x 2
+ *   delta_ws        : as fa_bwd (fa_bwd_workspace_bytes bytes); it holds
+ *                     -D / (s_dO s_V) and LSE * log2(e)
+ * d must be 128 (else FA_ERR_UNSUPPORTED); other checks as fa_bwd.
+ */
+fa_status_t fa_bwd_fp8(const void* q8, const void* k8, const void* v8,
+                       const void* o, const void* do8, const float* lse,
+                       const float* descale,
+                       void* dq, void* dk, void* dv,
+                       float* delta_ws,
+                       int B, int Hq, int Hkv, int N, int d,
+                       int causal, float softmax_scale,
+                       hipStream_t stream);
+
+/*
  * Per-tensor FP8 quantisation for the FP8 forward ("FlashAttention" legal
  * glossary, FlashAttention-3 paragraph, and "flash attention io aware",
  * section "Flash Attention 2 and 3", name FP8 attention but give no recipe;

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_bwd_workspace_bytes", "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_decode",
-                          "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_dropout", "fa_bwd_dropout",
+                          "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd_fp8",
                           "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
                           "fa_status_string", "fa_abi_version"}
     for n in names:

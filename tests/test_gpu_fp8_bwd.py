@@ -1,0 +1,152 @@
+"""GPU parity of the FP8 backward (fa_bwd_fp8) with the float64 oracle.
+
+Q, K, V and dO are quantised on the CPU by the oracle's per-tensor E4M3
+quantiser (bit-exact with fa_quantize_fp8, pinned elsewhere); the GPU runs
+the FP8 forward and then the FP8 backward on those codes.  Two references:
+
+- the exact gradients at the unquantised bf16 inputs (the budget the recipe
+  is judged by): relative L2 <= 1e-1 on dQ, dK, dV.  A float64 simulation of
+  the recipe gives about 6.5% (dQ), 6% (dK) and 4.5% (dV), nearly all of it
+  the E4M3 rounding of the inputs;
+  (With a single key the exact dQ and dK are zero; there the bound is the
+  one the recipe implies for that case, stated in the test.)
+- the exact gradients at the dequantised inputs (code * descale), which
+  leaves only the kernels' own rounding (P in the forward, dS to E4M3 with
+  per-block scales in dQ, P and dS to bf16 in dK/dV): relative L2 <= 4e-2 on
+  dQ and <= 2e-2 (the bf16 bound) on dK and dV; the simulation gives 2.7% and
+  under 1%.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_50_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+REL_EXACT = 1e-1
+REL_DEQ = {"dQ": 4e-2, "dK": 2e-2, "dV": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def fa():
+    from exact_io_aware_50_amd import fa as _fa
+    return _fa
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def rel_l2(x, y):
+    return float(np.linalg.norm(x - y) / max(np.linalg.norm(y), 1e-300))
+
+
+def quantise(x):
+    """(codes uint8 like x, descale, dequantised float64) by the oracle's quantiser."""
+    codes, s = oracle.quantize_per_tensor(x.float().numpy())
+    return codes, float(s), oracle.e4m3_decode(codes).astype(np.float64) * float(s)
+
+
+def run_fp8(fa, dev, q, k, v, do, causal, scale):
+    """FP8 forward then FP8 backward on the oracle's codes; returns (dq, dk, dv) and the dequantised inputs."""
+    qs = [quantise(t) for t in (q, k, v, do)]
+    c8 = [torch.from_numpy(c).to(dev) for c, _, _ in qs]
+    s = [sv for _, sv, _ in qs]
+    o, lse = fa.fwd(c8[0], c8[1], c8[2], causal, scale, descale=torch.tensor(s[:3], dtype=torch.float32, device=dev))
+    dq, dk, dv, _ = fa.bwd_fp8(c8[0], c8[1], c8[2], o, c8[3], lse, torch.tensor(s, dtype=torch.float32, device=dev),
+                               causal, scale)
+    torch.cuda.synchronize()
+    return (dq, dk, dv), [d for _, _, d in qs]
+
+
+SMALL = [
+    # B, Hq, Hkv, N, causal
+    (1, 1, 1, 1, False),
+    (1, 2, 2, 63, True),
+    (1, 4, 2, 200, True),
+    (1, 2, 2, 257, False),
+    (2, 4, 1, 1000, True),
+    (1, 8, 2, 385, False),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}H{}x{}N{}c{}".format(*s))
+def test_fp8_backward_small(fa, shape):
+    B, Hq, Hkv, N, causal = shape
+    d, dev = 128, torch.device("cuda:0")
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, do = (I.random_tensor(8100 + N, (B, H, N, d), "bf16", tensor_id=t) for t, H in enumerate((Hq, Hkv, Hkv, Hq)))
+    print(f"case {shape}", flush=True)
+    got, deq = run_fp8(fa, dev, q, k, v, do, causal, scale)
+    exact = oracle.backward(f64(q), f64(k), f64(v), f64(do), causal, scale)[:3]
+    at_deq = oracle.backward(*deq, causal, scale)[:3]
+    for name, g, r, rd in zip(("dQ", "dK", "dV"), got, exact, at_deq):
+        g = f64(g)
+        if not np.any(r):
+            # one key: the softmax does not depend on it and dQ = dK = 0 exactly.
+            # Here D comes from O = bf16(V8 s_V), which is V to within a bf16
+            # half-ulp, so dS = dP - D is at most 2^-9 sum_c |dO_c V_c| (x 1.1 for
+            # its E4M3 rounding), and |dQ| <= scale |dS| max|K|, |dK| <= scale |dS| max|Q|
+            dS_bound = 1.1 * 2.0 ** -9 * float(np.max(np.sum(np.abs(deq[3] * deq[2]), axis=-1)))
+            bound = scale * dS_bound * float(np.max(np.abs(deq[1] if name == "dQ" else deq[0])))
+            e = float(np.max(np.abs(g)))
+            print(f"[{shape}] {name} max|err| {e:.3e} (zero reference, bound {bound:.3e})", flush=True)
+            assert e <= bound, (shape, name, e, bound)
+            continue
+        e1, e2 = rel_l2(g, r), rel_l2(g, rd)
+        print(f"[{shape}] {name} rel-L2 {e1:.3e} (exact inputs), {e2:.3e} (dequantised inputs)", flush=True)
+        assert e1 <= REL_EXACT and e2 <= REL_DEQ[name], (shape, name, e1, e2)
+
+
+def test_fp8_backward_deterministic(fa):
+    """Bitwise run-to-run determinism of the FP8 backward (no atomics)."""
+    dev = torch.device("cuda:0")
+    q, k, v, do = (I.random_tensor(77, (2, 4, 700, 128), "bf16", tensor_id=t) for t in range(4))
+    a, _ = run_fp8(fa, dev, q, k, v, do, True, 0.09)
+    b, _ = run_fp8(fa, dev, q, k, v, do, True, 0.09)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wl", ["causal_bf16_n4096", "gqa_bf16_n16384"])
+def test_fp8_backward_workload_sampled(fa, wl):
+    """The whole workload on the GPU; sampled query rows (dQ) and key columns (dK, dV) of sampled heads against
+    the exact gradients at the unquantised and at the dequantised inputs."""
+    w = I.WORKLOADS[wl]
+    dev = torch.device("cuda:0")
+    q, k, v, do = (I.full_tensor(w, t) for t in range(4))
+    print(f"workload {w.name}: quantising on the CPU", flush=True)
+    (dq, dk, dv), deq = run_fp8(fa, dev, q, k, v, do, w.causal, w.scale)
+    print("gpu done", flush=True)
+    G = w.Hq // w.Hkv
+    rows = I.sample_rows(w.N)
+    got = {n: [] for n in ("dQ", "dK", "dV")}
+    ref = {n: [] for n in got}
+    refd = {n: [] for n in got}
+    heads = I.sample_heads(w)
+    for (b, h) in heads:
+        g = h // G
+        ex = oracle.head_rows_backward_dq(f64(q[b, h]), f64(k[b, g]), f64(v[b, g]), f64(do[b, h]), rows, w.causal,
+                                          w.scale)[0]
+        dd = oracle.head_rows_backward_dq(deq[0][b, h], deq[1][b, g], deq[2][b, g], deq[3][b, h], rows, w.causal,
+                                          w.scale)[0]
+        got["dQ"].append(f64(dq[b, h, rows])); ref["dQ"].append(ex); refd["dQ"].append(dd)
+    for (b, g) in sorted({(b, h // G) for b, h in heads})[:2]:
+        hs = list(range(g * G, (g + 1) * G))
+        for src, out in (((f64(q), f64(k), f64(v), f64(do)), ref), (deq, refd)):
+            Q_, K_, V_, dO_ = src
+            stats = [oracle.head_full_stats(Q_[b, h], K_[b, g], V_[b, g], dO_[b, h], w.causal, w.scale) for h in hs]
+            dKc, dVc = oracle.head_cols_backward_dkdv([Q_[b, h] for h in hs], K_[b, g], V_[b, g],
+                                                     [dO_[b, h] for h in hs], stats, rows, w.causal, w.scale)
+            out["dK"].append(dKc)
+            out["dV"].append(dVc)
+        got["dK"].append(f64(dk[b, g, rows])); got["dV"].append(f64(dv[b, g, rows]))
+        print(f"cols of kv head {(b, g)} done", flush=True)
+    for n in ("dQ", "dK", "dV"):
+        x = np.concatenate(got[n])
+        e1, e2 = rel_l2(x, np.concatenate(ref[n])), rel_l2(x, np.concatenate(refd[n]))
+        print(f"[{wl}] fp8 {n} rel-L2 {e1:.3e} (exact inputs), {e2:.3e} (dequantised inputs)", flush=True)
+        assert e1 <= REL_EXACT and e2 <= REL_DEQ[n], (wl, n, e1, e2)
