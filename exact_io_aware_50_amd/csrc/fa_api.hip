@@ -248,6 +248,10 @@ fa_status_t fa_bwd_local(const void* q, const void* k, const void* v, const void
     return launch_status(e);
 }
 
+// The keep threshold of a drop probability 0 <= p < 1: a score element is
+// kept iff its random byte is >= floor(256 p).
+static uint32_t drop_threshold(double p) { return (uint32_t)floor(p * 256.0); }
+
 fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                            int N, int d, int causal, double dropout_p, uint64_t seed, float softmax_scale,
                            fa_dtype_t dtype, hipStream_t stream) {
@@ -258,8 +262,8 @@ fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o,
     if (s != FA_OK || empty) return s;
     s = check_ptrs({q, k, v}, {}, {o}, {lse});
     if (s != FA_OK) return s;
-    const uint32_t thr = (uint32_t)floor(dropout_p * 4294967296.0);
-    const float rkeep = (float)(1.0 / (1.0 - dropout_p));
+    const uint32_t thr = drop_threshold(dropout_p);
+    const float rkeep = 256.f / (float)(256u - thr);
     return launch_status(fa::launch_fwd_bf16_dropout(d, causal, q, k, v, o, lse, B, Hq, Hkv, N, thr, seed, rkeep,
                                                      softmax_scale, stream));
 }
@@ -275,9 +279,10 @@ fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const vo
     if (s != FA_OK || empty) return s;
     s = check_ptrs({q, k, v, o, dO, delta_ws}, {lse}, {dq, dk, dv}, {});
     if (s != FA_OK) return s;
-    const uint32_t thr = (uint32_t)floor(dropout_p * 4294967296.0);
-    const float rkeep = (float)(1.0 / (1.0 - dropout_p));
-    hipError_t e = fa::launch_bwd_delta(dtype, d, o, dO, lse, delta_ws, B, Hq, N, stream, (float)(1.0 - dropout_p));
+    const uint32_t thr = drop_threshold(dropout_p);
+    const float rkeep = 256.f / (float)(256u - thr);
+    // the keep probability (256 - thr) / 256 is exact in float32
+    hipError_t e = fa::launch_bwd_delta(dtype, d, o, dO, lse, delta_ws, B, Hq, N, stream, (float)(256u - thr) / 256.f);
     if (e == hipSuccess)
         e = fa::launch_bwd_bf16_dropout(d, causal, q, k, v, dO, delta_ws, dq, dk, dv, B, Hq, Hkv, N, thr, seed, rkeep,
                                         softmax_scale, stream);

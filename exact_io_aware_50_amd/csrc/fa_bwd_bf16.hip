@@ -79,7 +79,8 @@ __device__ __forceinline__ void sched_dkdv_phase() {
 // DROP: the backward through attention dropout (the FlashAttention page of the
 // self-hosted LLM glossary: dropout is fused into the kernel; its mask is
 // regenerated here from the same counter-based generator, not stored).  With
-// Z the keep mask and r = 1/(1 - p), O = (Z o P) r V, so dV = r (Z o P)^T dO
+// Z the keep mask, p the drop probability (thr / 256) and r = 1/(1 - p),
+// O = (Z o P) r V, so dV = r (Z o P)^T dO
 // and dS = P o (Z o dP r - D).  The workspace then holds -D (1 - p), the dP
 // accumulator starts from it, and dS = r P o (Z ? acc : -D (1 - p)); the
 // factor r goes into the final scales of dK and dV.
@@ -359,33 +360,22 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
                         if (dw + 8 * (r / 4) + r % 4 >= W) sacc[qb][r] = 0.f;
                 }
                 if constexpr (DROP) {
-                    // keep bits of this lane's key krow for the queries
-                    // q0 + 32 qb + 8 gq + 4 hh + e (element 4 gq + e).  The call for
-                    // query i serves keys 4 (krow / 4) .. + 3, the four lanes of a
-                    // quad: lane x of the quad makes the calls of the queries with
-                    // e = x, and a quad transpose hands word y of each call to lane y
+                    // keep bytes of this lane's key krow for the queries
+                    // q0 + 32 qb + 8 gq + 4 hh + e (element 4 gq + e): one Philox
+                    // call per lane and 32-query block, shared by the quad
                     int ln = lane;
                     asm volatile("" : "+v"(ln));
-                    const int x = ln & 3;
                     const uint32_t bhq = (uint32_t)(b * Hq + g * G + hstep);
-                    uint32_t zw[4][4];
-#pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        zw[gq][0] = (uint32_t)krow >> 2;
-                        zw[gq][1] = (uint32_t)(q0 + 32 * qb + 8 * gq + 4 * (ln >> 5) + x);
-                        zw[gq][2] = bhq;
-                        zw[gq][3] = 0u;
-                        philox4x32_10(zw[gq], drop.key0, drop.key1);
-                    }
+                    uint32_t zw[4];
+                    drop_words_krow(zw, q0 + 32 * qb, krow, ln >> 5, ln & 3, bhq, drop);
                     const float* sd = sl + BMQ;       // -D (1 - p) of the step's rows: the dP accumulator's start
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
-                        quad_transpose(zw[gq], x);
                         const f32x4 d4 = *reinterpret_cast<const f32x4*>(sd + 32 * qb + 8 * gq + 4 * hh);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int r = 4 * gq + e;
-                            const bool keep = zw[gq][e] >= drop.thr;
+                            const bool keep = drop_keep(zw[gq], e, drop.thr);
                             dpacc[qb][r] = sacc[qb][r] * (keep ? dpacc[qb][r] : d4[e]);
                             sacc[qb][r] = keep ? sacc[qb][r] : 0.f;
                         }
@@ -719,22 +709,24 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
                             sacc[kb][r] = 0.f;
                     }
             }
+            // (dropout) keys k0 + 32 kb + 8 gq + 4 hh + e (element 4 gq + e of
+            // block kb): one Philox call per lane and 32-key block, shared by the quad
+            uint32_t zw[DROP ? KB : 1][4];
+            if constexpr (DROP) {
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                drop_words_qrow(zw, k0, qrow, ln >> 5, ln & 3, (uint32_t)(b * Hq + h), drop);
+            }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 if constexpr (DROP) {
-                    // keys k0 + 32 kb + 8 gq + 4 hh + e (element 4 gq + e): one
-                    // Philox call per run of four, word e for key offset e
-                    const uint32_t bhq = (uint32_t)(b * Hq + h);
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
-                        uint32_t c[4] = {(uint32_t)((k0 + 32 * kb + 8 * gq) >> 2) + (uint32_t)hh, (uint32_t)qrow,
-                                         bhq, 0u};
-                        philox4x32_10(c, drop.key0, drop.key1);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int r = 4 * gq + e;
                             const float x = dpacc[kb][r] + dq_nd;
-                            dpacc[kb][r] = sacc[kb][r] * (c[e] >= drop.thr ? x : dq_nd);
+                            dpacc[kb][r] = sacc[kb][r] * (drop_keep(zw[kb][gq], e, drop.thr) ? x : dq_nd);
                         }
                     }
                 } else {

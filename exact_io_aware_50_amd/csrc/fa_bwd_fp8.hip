@@ -32,7 +32,6 @@ namespace fa {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 __device__ __forceinline__ f32x16 mma_fp8s(const u32x8& a, const u32x8& b, f32x16 c, int scale_b) {

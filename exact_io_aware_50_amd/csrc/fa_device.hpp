@@ -29,6 +29,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -492,29 +493,41 @@ struct LdsTile {
 // Weyl constants.  The 64-bit product form compiles to one v_mad_u64_u32 per
 // product.  Returns the four output words in c.
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+// NC counters under one key, their rounds interleaved: each round key is
+// formed once for all of them.
+template <int NC>
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[NC][4], uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
-        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
-        c[1] = (uint32_t)p1;
-        c[3] = (uint32_t)p0;
-        c[0] = n0;
-        c[2] = n2;
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            const uint64_t p0 = (uint64_t)0xD2511F53u * c[n][0];
+            const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[n][2];
+            // three-input xor in one v_bitop3_b32 (truth table 0x96)
+            const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[n][1], k0, 0x96);
+            const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[n][3], k1, 0x96);
+            c[n][1] = (uint32_t)p1;
+            c[n][3] = (uint32_t)p0;
+            c[n][0] = n0;
+            c[n][2] = n2;
+        }
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
 }
 
-// Dropout parameters: element (query i, key j) of (batch b, query head h) is
-// kept iff word j % 4 of Philox((j / 4, i, b * Hq + h, 0), (key0, key1)) is
-// >= thr; kept probabilities are scaled by rkeep = 1 / (1 - p).
+// Dropout parameters.  One Philox call serves a 4 x 4 block of the score
+// matrix, one byte per element: element (query i, key j) of (batch b, query
+// head h) takes byte 4 (i % 4) + j % 4 of Philox((j / 4, i / 4, b * Hq + h,
+// 0), (key0, key1)) -- byte e of output word i % 4 -- and is kept iff that
+// byte is >= thr = floor(256 p).  Kept probabilities are scaled by
+// rkeep = 256 / (256 - thr), one over the keep probability.
 struct DropArgs {
     uint32_t thr, key0, key1;
     float rkeep;
 };
+
+__device__ __forceinline__ bool drop_keep(uint32_t w, int e, uint32_t thr) { return ((w >> (8 * e)) & 0xffu) >= thr; }
 
 // 4 x 4 transpose of 32-bit words inside each quad of lanes: lane x of a quad
 // holds a[0..3]; afterwards lane y holds (a[y] of lane 0, ..., a[y] of lane 3).
@@ -536,6 +549,46 @@ __device__ __forceinline__ void quad_transpose(uint32_t a[4], int x) {
         a[k] = b1 ? r : a[k];
         a[k + 2] = b1 ? a[k + 2] : r;
     }
+}
+
+// Keep bytes of KB 32-key blocks for an accumulator that holds a query per
+// lane (forward, dQ): lane query qrow, element 4 t + e of block kb the key
+// k0 + 32 kb + 8 t + 4 hh + e (k0 a multiple of 32).  The quad's lanes hold
+// four consecutive queries (qrow % 4 = x, the lane in the quad), so each call
+// serves the whole quad: lane x makes the calls of the keys k0 + 32 kb + 8 x +
+// 4 hh .. + 3, and the quad transpose gives lane y word y of each block's four
+// calls.  On return byte e of w[kb][t] decides element 4 t + e of block kb.
+template <int KB>
+__device__ __forceinline__ void drop_words_qrow(uint32_t (&w)[KB][4], int k0, int qrow, int hh, int x,
+                                                uint32_t bhq, const DropArgs& d) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        w[kb][0] = (uint32_t)((k0 + 32 * kb) >> 2) + (uint32_t)(2 * x + hh);
+        w[kb][1] = (uint32_t)qrow >> 2;
+        w[kb][2] = bhq;
+        w[kb][3] = 0u;
+    }
+    philox4x32_10(w, d.key0, d.key1);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) quad_transpose(w[kb], x);
+}
+
+// Keep bytes of one 32-query block for an accumulator that holds a key per
+// lane (dK/dV): lane key krow, element 4 g + e the query qb0 + 8 g + 4 hh + e
+// (qb0 a multiple of 32).  The quad's lanes hold four consecutive keys
+// (krow % 4 = x): lane x makes the call of the queries qb0 + 8 x + 4 hh .. + 3,
+// gathers byte y of its four words into word y (word e of a call belongs to
+// query offset e, byte y to key offset y), and the quad transpose gives lane y
+// word y of each call.  On return byte e of w[g] decides element 4 g + e.
+__device__ __forceinline__ void drop_words_krow(uint32_t w[4], int qb0, int krow, int hh, int x, uint32_t bhq,
+                                                const DropArgs& d) {
+    uint32_t c[1][4] = {{(uint32_t)krow >> 2, (uint32_t)(qb0 >> 2) + (uint32_t)(2 * x + hh), bhq, 0u}};
+    philox4x32_10(c, d.key0, d.key1);
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+        w[y] = ((c[0][0] >> (8 * y)) & 0xffu) | (((c[0][1] >> (8 * y)) & 0xffu) << 8) |
+               (((c[0][2] >> (8 * y)) & 0xffu) << 16) | (((c[0][3] >> (8 * y)) & 0xffu) << 24);
+    quad_transpose(w, x);
 }
 
 __device__ __forceinline__ f32x16 mma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {

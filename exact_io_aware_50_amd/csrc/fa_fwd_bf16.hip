@@ -90,7 +90,8 @@ __device__ __forceinline__ void sched_gemm_phase() {
 // every access in bounds.  A row that sees no key gets O = 0 and LSE = -inf.
 // DROP: attention dropout on the normalised probabilities (the FlashAttention
 // page of the self-hosted LLM glossary: dropout is one of the operations fused
-// into the kernel).  The normaliser and LSE are those of the undropped softmax.
+// into the kernel).  The normaliser and LSE are those of the undropped softmax;
+// kept probabilities are scaled by 1 / (1 - p), p = thr / 256 (DropArgs).
 template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
 __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -291,21 +292,27 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
             }
             lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
             if constexpr (DROP) {
-                // lane keys k0 + 32 kb + 8 g + 4 hh + e (e < 4): one Philox call per run of four
+                // one Philox call per lane and 32-key block, shared by the quad
                 const uint32_t bhq = (uint32_t)(b * Hq + h);
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                uint32_t zw[KB][4];
+                drop_words_qrow(zw, k0, qrow, hh, ln & 3, bhq, drop);
+                // the packed pair of elements 2c, 2c + 1 is cleared half by half:
+                // bytes e, e + 1 of the keep word zero-extended to 16 bits, minus
+                // thr, are negative exactly where dropped; the sign spread over
+                // the half is the clearing mask (packed 16-bit integer arithmetic)
+                const s16x2 thr2 = {(short)drop.thr, (short)drop.thr};
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        uint32_t c[4] = {(uint32_t)((k0 + 32 * kb + 8 * gq) >> 2) + (uint32_t)hh, (uint32_t)qrow, bhq, 0u};
-                        philox4x32_10(c, drop.key0, drop.key1);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (c[e] < drop.thr) sacc[kb][4 * gq + e] = 0.f;
+                    for (int c = 0; c < 8; ++c) {
+                        const uint32_t w = zw[kb][c >> 1];
+                        const uint32_t x = __builtin_amdgcn_perm(0u, w, (c & 1) ? 0x0c030c02u : 0x0c010c00u);
+                        const s16x2 y = __builtin_bit_cast(s16x2, x) - thr2;
+                        const uint32_t m = __builtin_bit_cast(uint32_t, (s16x2)(y >> (short)15));
+                        pf[kb][c >> 2][c & 3] &= ~m;
                     }
-#pragma unroll
-                    for (int t2 = 0; t2 < 2; ++t2) pf[kb][t2] = pack_bf16x8(sacc[kb], 8 * t2);
-                }
             }
             // P is finished inside this phase (not sunk into the next matrix phase)
 #pragma unroll

@@ -254,14 +254,16 @@ fa_status_t fa_bwd_local(const void* q, const void* k, const void* v,
  * matrix products, masking, softmax and dropout fused in one kernel) and the
  * FlashAttention digest, section "Limits" (dropout among the features a
  * kernel must handle).  The pages fix no generator; this library uses
- * Philox4x32-10 (Salmon et al., SC 2011): element (query i, key j) of batch
- * entry b and query head h is kept iff word j % 4 of
- * Philox((j / 4, i, b * Hq + h, 0), (seed % 2^32, seed / 2^32)) is
- * >= floor(dropout_p * 2^32) (dropout_p taken as the double passed, so the
- * drop probability is dropout_p on the 2^-32 grid); O = ((Z o P) /
- * (1 - dropout_p)) V.  LSE is that of the undropped softmax.  Same arguments,
- * layouts and errors as fa_fwd (bf16 only) plus dropout_p in [0, 1) (else
- * FA_ERR_UNSUPPORTED) and the 64-bit seed.
+ * Philox4x32-10 (Salmon et al., SC 2011), one call per 4 x 4 block of the
+ * score matrix and one byte per element: element (query i, key j) of batch
+ * entry b and query head h takes byte j % 4 of word i % 4 of
+ * Philox((j / 4, i / 4, b * Hq + h, 0), (seed % 2^32, seed / 2^32)) (byte e =
+ * bits 8e .. 8e+7) and is kept iff that byte is >= t = floor(256 dropout_p).
+ * The drop probability is therefore p' = t / 256, dropout_p rounded down to a
+ * multiple of 1/256 (no dropout below 1/256), and O = ((Z o P) / (1 - p')) V.
+ * LSE is that of the undropped softmax.  Same arguments, layouts and errors
+ * as fa_fwd (bf16 only) plus dropout_p in [0, 1) (else FA_ERR_UNSUPPORTED)
+ * and the 64-bit seed.
  */
 fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v,
                            void* o, float* lse,
@@ -271,13 +273,13 @@ fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v,
 
 /*
  * Backward through the dropout of fa_fwd_dropout (same pages).  The keep mask
- * Z is regenerated from (dropout_p, seed), never stored.  With r = 1/(1 - p)
- * and P the undropped softmax: dV = r (Z o P)^T dO, dP = r Z o (dO V^T),
+ * Z is regenerated from (dropout_p, seed), never stored.  With r = 1/(1 - p')
+ * (p' as in fa_fwd_dropout) and P the undropped softmax: dV = r (Z o P)^T dO, dP = r Z o (dO V^T),
  * D = rowsum(dO o O) (= rowsum(P o dP), O the dropped output), dS = P o (dP - D),
  * dQ = scale dS K, dK = scale dS^T Q, K/V gradients summed over each group.
  * Same arguments, layouts, workspace and errors as fa_bwd (bf16 only) plus the
  * dropout_p and seed given to fa_fwd_dropout; o and lse are its outputs.  The
- * workspace holds -D (1 - p) instead of -D.
+ * workspace holds -D (1 - p') instead of -D.
  */
 fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse,

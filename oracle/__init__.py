@@ -46,6 +46,7 @@ from .attention import (  # noqa: F401
 from .fp8 import e4m3_decode, e4m3_encode_rne_sat, quantize_per_tensor, E4M3_MAX  # noqa: F401
 from .dropout import (  # noqa: F401,E402
     backward_dropout,
+    drop_probability,
     drop_threshold,
     forward_dropout,
     head_backward_dropout,

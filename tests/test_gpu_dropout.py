@@ -1,6 +1,6 @@
 """GPU parity of attention with dropout (fa_fwd_dropout, fa_bwd_dropout) with the float64 oracle.
 
-The keep mask is integer work (Philox4x32-10 words against a threshold): the
+The keep mask is integer work (Philox4x32-10 bytes against a threshold): the
 mask each kernel regenerates is recovered element by element and compared
 with the oracle's bit for bit -- the forward's through O, the dK/dV kernel's
 through dV, the dQ kernel's through the sign of dQ.  O is compared to the
@@ -87,7 +87,7 @@ def test_dropout_forward_headline_shape(fa):
     for b, h in ((0, 0), (w.B - 1, w.Hq - 1)):
         _, P, m, l = oracle.probabilities(f64(q[b, h]), f64(k[b, h]), w.scale, True, rows=rows)
         Z = oracle.keep_mask(b, h, w.Hq, rows, w.N, p, seed)
-        Oref = (np.where(Z, P, 0.0) / (1 - p)) @ f64(v[b, h])
+        Oref = (np.where(Z, P, 0.0) / (1 - oracle.drop_probability(p))) @ f64(v[b, h])
         eo = float(np.max(np.abs(f64(o[b, h, rows]) - Oref)))
         el = float(np.max(np.abs(f64(lse[b, h, rows]) - (m + np.log(l)))))
         print(f"head ({b}, {h}) O max|err| {eo:.3e} LSE max|err| {el:.3e}", flush=True)
@@ -113,10 +113,10 @@ MASK_CASES = [
 @pytest.mark.parametrize("case", MASK_CASES, ids=lambda c: "B{}H{}x{}N{}d{}c{}p{}".format(*c[:7]))
 def test_dropout_keep_mask_bit_exact(fa, case):
     """Q = 0 makes every score 0, so P is uniform over the visible keys (1/N; causal 1/(i+1)).  V one-hot over
-    the d keys of chunk c (V[j] = e_{j - d c}) gives O[i, m] = Z[i, d c + m] P_i / (1 - p): nonzero exactly
+    the d keys of chunk c (V[j] = e_{j - d c}) gives O[i, m] = Z[i, d c + m] P_i / (1 - p'): nonzero exactly
     where key d c + m is kept and visible.  Every chunk of every row of every (batch, head) is compared with
     oracle.keep_mask bit for bit (ragged last chunk, rows past one 256-row block, grouped heads, seeds with a
-    nonzero high word, p off the float32 grid)."""
+    nonzero high word, p off the 1/256 grid)."""
     B, Hq, Hkv, N, d, causal, p, seeds = case
     dev = torch.device("cuda:0")
     q = torch.zeros((B, Hq, N, d), dtype=torch.bfloat16, device=dev)
@@ -189,7 +189,7 @@ BWD_MASK_CASES = [
 def test_dropout_backward_dkdv_mask_bit_exact(fa, case):
     """The dK/dV kernel's mask, read through dV.  Q = 0 (P uniform over the visible keys) and dO one-hot over the
     d queries of chunk c (dO[i] = e_{i - d c}) give dV[j, m] = sum over the group's heads of
-    Z_h[d c + m, j] P / (1 - p): nonzero exactly where some head of the group keeps (visible) element
+    Z_h[d c + m, j] P / (1 - p'): nonzero exactly where some head of the group keeps (visible) element
     (d c + m, j).  Compared with the oracle's masks for every chunk and key."""
     B, Hq, Hkv, N, d, causal, p, seed = case
     G = Hq // Hkv

@@ -4,9 +4,11 @@
   (Random123 distribution, "kat_vectors": counters and keys all zero, all
   ones, and the digits of pi).
 - p = 0 reduces to the oracle's plain forward and backward.
-- The drop rate of a large mask sits within 5 sigma of p, masks differ across
-  heads, batch entries and seeds, and each element's decision is word j mod 4
-  of its own counter.
+- The drop rate of a large mask sits within 5 sigma of p' = floor(256 p) / 256,
+  masks differ across heads, batch entries and seeds, each element's decision
+  is one byte of the call of its 4 x 4 block, and the sixteen elements of a
+  block are the sixteen bytes of one call (each threshold t = 0..255 drops
+  exactly the bytes below it).
 - The backward through a fixed mask matches central finite differences of
   the loss sum(dO * O) in float64.
 """
@@ -42,31 +44,57 @@ def test_philox_vectorised_matches_scalar():
 
 
 def test_keep_mask_layout():
-    """Element (i, j) is word j mod 4 of Philox((j div 4, i, b Hq + h, 0), seed halves)."""
+    """Element (i, j) is byte 4 (i mod 4) + (j mod 4) of Philox((j div 4, i div 4, b Hq + h, 0), seed halves),
+    byte 4 w + e being bits 8 e .. 8 e + 7 of word w (scalar calls, element by element)."""
     seed, b, h, Hq = (7 << 32) | 12345, 1, 2, 4
-    Z = oracle.keep_mask(b, h, Hq, np.arange(3), 10, 0.5, seed)
+    Z = oracle.keep_mask(b, h, Hq, np.arange(9), 10, 0.5, seed)
     thr = oracle.drop_threshold(0.5)
-    for i in range(3):
+    for i in range(9):
         for j in range(10):
-            w = oracle.philox4x32_10((j // 4, i, b * Hq + h, 0), (12345, 7))[j % 4]
-            assert Z[i, j] == (int(w) >= thr)
+            w = oracle.philox4x32_10((j // 4, i // 4, b * Hq + h, 0), (12345, 7))[i % 4]
+            assert Z[i, j] == (((int(w) >> (8 * (j % 4))) & 0xFF) >= thr)
+
+
+def test_block_is_one_call():
+    """The 16 decisions of a 4 x 4 block at thresholds t = 1..255 recover the call's 16 bytes: byte = the
+    largest t that still keeps the element (the mask is monotone in t and each byte is used once)."""
+    seed, b, h, Hq = 2 ** 40 + 3, 0, 3, 5
+    rows, n_keys = np.arange(8, 12), 12                                  # block row 2
+    masks = [oracle.keep_mask(b, h, Hq, rows, n_keys, t / 256.0, seed) for t in range(256)]
+    for tprev, t in zip(range(255), range(1, 256)):
+        assert not np.any(masks[t] & ~masks[tprev])                       # monotone
+    byte = np.sum(masks, axis=0) - 1                                      # kept for t = 0..byte
+    for jb in range(3):
+        words = oracle.philox4x32_10((jb, 2, b * Hq + h, 0), (seed & 0xFFFFFFFF, seed >> 32))
+        got = byte[:, 4 * jb:4 * jb + 4]                                  # [query offset, key offset]
+        raw = bytes(np.array([int(w) for w in words], dtype="<u4").tobytes())
+        assert [[raw[4 * r + e] for e in range(4)] for r in range(4)] == got.tolist()
+
+
+def test_threshold_grid():
+    assert oracle.drop_threshold(0.25) == 64 and oracle.drop_probability(0.25) == 0.25
+    assert oracle.drop_threshold(0.3) == 76 and oracle.drop_probability(0.3) == 76 / 256
+    assert oracle.drop_threshold(1 / 512) == 0 and oracle.drop_threshold(255.9 / 256) == 255
+    assert np.all(oracle.keep_mask(0, 0, 2, np.arange(40), 40, 0.003, 5))        # p < 1/256: nothing dropped
+    with pytest.raises(ValueError):
+        oracle.drop_threshold(-0.01)
 
 
 def test_drop_rate_and_independence():
     p = 0.3
+    pp = oracle.drop_probability(p)
     Z = oracle.keep_mask(0, 0, 8, np.arange(512), 512, p, 99)
     n = Z.size
     rate = 1.0 - Z.mean()
-    assert abs(rate - p) < 5 * np.sqrt(p * (1 - p) / n)
+    assert abs(rate - pp) < 5 * np.sqrt(pp * (1 - pp) / n)
     others = [oracle.keep_mask(0, 1, 8, np.arange(512), 512, p, 99),
               oracle.keep_mask(1, 0, 8, np.arange(512), 512, p, 99),
               oracle.keep_mask(0, 0, 8, np.arange(512), 512, p, 100)]
     for Y in others:
         agree = np.mean(Y == Z)
-        expect = p * p + (1 - p) * (1 - p)                 # two independent masks agree this often
+        expect = pp * pp + (1 - pp) * (1 - pp)             # two independent masks agree this often
         assert abs(agree - expect) < 5 * np.sqrt(expect * (1 - expect) / n)
     assert np.all(oracle.keep_mask(0, 0, 8, np.arange(64), 64, 0.0, 5))
-    assert oracle.drop_threshold(0.25) == 2 ** 30
     with pytest.raises(ValueError):
         oracle.drop_threshold(1.0)
 
