@@ -39,6 +39,35 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def probe_clocks(torch, fa, calls, per, check, dev, span=0.02):
+    """Engine clock (GHz) under each kernel: fa_engine_clock_probe (eight one-wave
+    workgroups, one per XCD, counting shader-clock ticks against the 100 MHz
+    real-time counter for `span` seconds) runs on a second stream while the
+    kernel runs back to back on the current one.  Outside the timed region."""
+    side = torch.cuda.Stream(device=dev)
+    buf = torch.zeros(16, dtype=torch.int64, device=dev)
+    clocks = {}
+    for name, fn in calls:
+        reps = int(1.5 * span * 1e3 / max(per[name], 1e-3)) + 5
+        torch.cuda.synchronize()
+        check(fa.fa_engine_clock_probe(buf.data_ptr(), 8, span, side.cuda_stream), "fa_engine_clock_probe")
+        time.sleep(0.001)                       # the probe's waves are resident before the kernels
+        for _ in range(reps):
+            check(fn(), name)
+        torch.cuda.synchronize()
+        t = buf.cpu().tolist()
+        ghz = [0.1 * t[2 * w] / t[2 * w + 1] for w in range(8) if t[2 * w + 1] > 0]
+        clocks[name] = round(sum(ghz) / len(ghz), 3) if ghz else None
+    return clocks
+
+
+def step_clock(per, clocks):
+    """Time-weighted mean clock over a step's kernels (GHz), or None."""
+    if not clocks or not all(clocks.get(n) for n in per):
+        return None
+    return sum(per[n] * clocks[n] for n in per) / sum(per.values())
+
+
 def credited(w):
     f = 4.0 * w.B * w.Hq * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
     return f, 2.5 * f
@@ -376,6 +405,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-dropout", action="store_true", help="skip the attention-dropout leg")
+    ap.add_argument("--no-clock", action="store_true", help="skip the engine-clock sampling")
     ap.add_argument("--no-gemm-reference", action="store_true",
                     help="skip the vendor bf16 GEMM timed for context (practical MFMA rate on this data)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode (KV cache) leg")
@@ -477,6 +507,19 @@ def main():
             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
             "traffic": stored_traffic(dom, args.workload)}
 
+    # engine clock under each kernel (outside the timed region, probe_clocks);
+    # the peak scales with it, 2516.6 TFLOP/s being quoted at 2.4 GHz
+    clocks = {} if args.no_clock else probe_clocks(torch, fa, calls, per, check, dev)
+    if clocks:
+        log("engine clock under load: " + ", ".join(f"{n} {c} GHz" for n, c in clocks.items()))
+    for n, c in clocks.items():
+        if c and "tflops" in kern[n]:
+            kern[n].update(clock_ghz=c, frac_peak_at_clock=round(kern[n]["tflops"] / (PEAK_BF16_TFLOPS * c / 2.4), 4))
+        elif c:
+            kern[n].update(clock_ghz=c)
+    if clocks.get(dom):
+        roof.update(clock_ghz=clocks[dom], frac_at_clock=round(ach / (PEAK_BF16_TFLOPS * clocks[dom] / 2.4), 4))
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -497,6 +540,14 @@ def main():
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
         "kernels": kern,
+        "clock": {"source": "fa_engine_clock_probe: shader-clock ticks over 20 ms of the 100 MHz real-time "
+                            "counter, one wave per XCD, beside each kernel run back to back outside the timed "
+                            "region; peak taken as 2516.6 x clock / 2.4 GHz",
+                  "ghz": clocks or None},
+        "fwd_frac_at_clock": (round(fwd_tf / (PEAK_BF16_TFLOPS * clocks["fwd"] / 2.4), 4)
+                              if clocks.get("fwd") else None),
+        "fwd_bwd_frac_at_clock": (round(value / (PEAK_BF16_TFLOPS * step_clock(per, clocks) / 2.4), 4)
+                                  if step_clock(per, clocks) else None),
         "roofline": roof,
     }
 
