@@ -183,13 +183,21 @@ def block_pairs(mask, N, bs=256):
     return int(ext @ mask.astype(np.int64) @ ext)
 
 
-def bsparse_leg(torch, fa, I, dev, stream, args):
-    """fa_fwd_bsparse and fa_bwd_bsparse on the block-sparse workload, HIP events on the launch stream.
+def bsparse_leg(torch, fa, I, dev, stream, args, name=None):
+    """fa_fwd_bsparse and fa_bwd_bsparse (fa_*_bsparse_split when the layout cuts long block rows or columns
+    into several work items) on a block-sparse workload, HIP events on the launch stream.
 
     Credited flops: 4 d per (query, key) pair in an on block and query head forward, 2.5x that backward."""
-    w, pat = I.BSPARSE_WORKLOADS[args.bsparse_workload]
+    name = name or args.bsparse_workload
+    w, pat = I.BSPARSE_WORKLOADS[name]
     mask = I.block_pattern((w.N + 255) // 256, **pat)
     L = fa.BlockSparseLayout(mask, device=dev)
+    split = bool(L.n_row_slots or L.n_col_slots)
+    pf = torch.empty(max(1, fa.fa_fwd_bsparse_split_workspace_bytes(w.B, w.Hq, w.d, L.n_row_slots) // 4),
+                     dtype=torch.float32, device=dev)
+    pb = torch.empty(max(1, fa.fa_bwd_bsparse_split_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, L.n_row_slots,
+                                                                    L.n_col_slots) // 4),
+                     dtype=torch.float32, device=dev)
     q, k, v, do = (I.full_tensor(w, t).to(dev) for t in range(4))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
@@ -199,17 +207,32 @@ def bsparse_leg(torch, fa, I, dev, stream, args):
     code = fa.FA_DTYPE_BF16
 
     def fwd():
-        st = fa.fa_fwd_bsparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq,
-                               w.Hkv, w.N, w.d, 0, L.row_ptr.data_ptr(), L.col_idx.data_ptr(), L.nnz, w.scale, code,
-                               sh)
+        if split:
+            st = fa.fa_fwd_bsparse_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B,
+                                         w.Hq, w.Hkv, w.N, w.d, 0, L.col_idx.data_ptr(), L.nnz,
+                                         L.row_chunks.data_ptr(), L.n_row_chunks, L.row_merges.data_ptr(),
+                                         L.n_row_merges, L.n_row_slots, pf.data_ptr(), w.scale, code, sh)
+        else:
+            st = fa.fa_fwd_bsparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B,
+                                   w.Hq, w.Hkv, w.N, w.d, 0, L.row_ptr.data_ptr(), L.col_idx.data_ptr(), L.nnz,
+                                   w.scale, code, sh)
         if st != fa.FA_OK:
             raise fa.FAError(st, "fa_fwd_bsparse")
 
     def bwd():
-        st = fa.fa_bwd_bsparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), w.B, w.Hq,
-                               w.Hkv, w.N, w.d, 0, L.row_ptr.data_ptr(), L.col_idx.data_ptr(), L.col_ptr.data_ptr(),
-                               L.row_idx.data_ptr(), L.nnz, w.scale, code, sh)
+        if split:
+            st = fa.fa_bwd_bsparse_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                                         w.B, w.Hq, w.Hkv, w.N, w.d, 0, L.col_idx.data_ptr(), L.row_idx.data_ptr(),
+                                         L.nnz, L.row_chunks.data_ptr(), L.n_row_chunks, L.row_merges.data_ptr(),
+                                         L.n_row_merges, L.n_row_slots, L.col_chunks.data_ptr(), L.n_col_chunks,
+                                         L.col_merges.data_ptr(), L.n_col_merges, L.n_col_slots, pb.data_ptr(),
+                                         w.scale, code, sh)
+        else:
+            st = fa.fa_bwd_bsparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                   lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), w.B,
+                                   w.Hq, w.Hkv, w.N, w.d, 0, L.row_ptr.data_ptr(), L.col_idx.data_ptr(),
+                                   L.col_ptr.data_ptr(), L.row_idx.data_ptr(), L.nnz, w.scale, code, sh)
         if st != fa.FA_OK:
             raise fa.FAError(st, "fa_bwd_bsparse")
 
@@ -232,7 +255,9 @@ def bsparse_leg(torch, fa, I, dev, stream, args):
     fl = 4.0 * w.B * w.Hq * w.d * block_pairs(mask, w.N)
     fwd_tf = fl / (tf * 1e-3) / 1e12
     fb_tf = 3.5 * fl / ((tf + tb) * 1e-3) / 1e12
-    return {"workload": args.bsparse_workload, "blocks_on": L.nnz, "density": round(L.nnz / mask.size, 4),
+    return {"workload": name, "blocks_on": L.nnz, "density": round(L.nnz / mask.size, 4),
+            "work_split": {"split": L.split, "row_items": L.n_row_chunks, "row_slots": L.n_row_slots,
+                           "col_items": L.n_col_chunks, "col_slots": L.n_col_slots},
             "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4), "fwd_bwd_ms": round(tf + tb, 4),
             "fwd_tflops": round(fwd_tf, 1), "fwd_frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
             "fwd_bwd_tflops": round(fb_tf, 1), "fwd_bwd_frac_peak": round(fb_tf / PEAK_BF16_TFLOPS, 4),
@@ -636,10 +661,12 @@ def main():
             result["local"]["fwd_bwd_ms"], result["local"]["fwd_bwd_tflops"]))
 
     if not args.no_bsparse:
-        result["bsparse"] = bsparse_leg(torch, fa, I, dev, stream, args)
-        log("block-sparse {} ({} blocks on): fwd {} ms ({} TFLOP/s), fwd+bwd {} ms ({} TFLOP/s)".format(
-            result["bsparse"]["workload"], result["bsparse"]["blocks_on"], result["bsparse"]["fwd_ms"],
-            result["bsparse"]["fwd_tflops"], result["bsparse"]["fwd_bwd_ms"], result["bsparse"]["fwd_bwd_tflops"]))
+        for key, wl in (("bsparse", args.bsparse_workload), ("bsparse_global", "bsparse_global_bf16_n16384")):
+            r = result[key] = bsparse_leg(torch, fa, I, dev, stream, args, wl)
+            log("block-sparse {} ({} blocks on, {} split row / {} split column slots): fwd {} ms ({} TFLOP/s), "
+                "fwd+bwd {} ms ({} TFLOP/s)".format(r["workload"], r["blocks_on"], r["work_split"]["row_slots"],
+                                                    r["work_split"]["col_slots"], r["fwd_ms"], r["fwd_tflops"],
+                                                    r["fwd_bwd_ms"], r["fwd_bwd_tflops"]))
 
     if not args.no_decode:
         result["decode"] = decode_leg(torch, fa, I, dev, stream, args)

@@ -346,6 +346,86 @@ fa_status_t fa_bwd_bsparse(const void* q, const void* k, const void* v, const vo
     return launch_status(e);
 }
 
+// Work split of the block-sparse entry points: chunk and merge tables (device
+// int4 arrays) and the float32 partial buffer.
+static fa_status_t check_split(int N, int nnz, const int* chunks, int nchunks, const int* merges, int nmerges,
+                               int nslots, const float* part, int64_t heads) {
+    const int64_t nb = ((int64_t)N + FA_BSPARSE_BLOCK - 1) / FA_BSPARSE_BLOCK;
+    if (nchunks < 1 || nchunks > nb + nnz || nmerges < 0 || nmerges > nb || nslots < 0 || nslots > nnz)
+        return FA_ERR_SHAPE;
+    if ((int64_t)nchunks * heads > INT32_MAX || (int64_t)nmerges * heads > INT32_MAX) return FA_ERR_SHAPE;
+    if (!chunks || (nmerges > 0 && !merges) || (nslots > 0 && !part)) return FA_ERR_NULL;
+    if (!aligned(chunks, 16) || (merges && !aligned(merges, 16)) || (part && !aligned(part, 16))) return FA_ERR_ALIGN;
+    return FA_OK;
+}
+
+fa_status_t fa_fwd_bsparse_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                                 int Hkv, int N, int d, int causal, const int* col_idx, int nnz,
+                                 const int* row_chunks, int n_row_chunks, const int* row_merges, int n_row_merges,
+                                 int n_row_slots, float* part_ws, float softmax_scale, fa_dtype_t dtype,
+                                 hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    const int64_t nb = ((int64_t)N + FA_BSPARSE_BLOCK - 1) / FA_BSPARSE_BLOCK;
+    if (nnz < 0 || nnz > nb * nb) return FA_ERR_SHAPE;
+    if (nnz > 0 && !col_idx) return FA_ERR_NULL;
+    if (col_idx && !aligned(col_idx, 4)) return FA_ERR_ALIGN;
+    s = check_split(N, nnz, row_chunks, n_row_chunks, row_merges, n_row_merges, n_row_slots, part_ws,
+                    (int64_t)B * Hq);
+    if (s != FA_OK) return s;
+    s = n_row_slots > 0 ? check_ptrs({q, k, v}, {}, {o}, {lse, part_ws}) : check_ptrs({q, k, v}, {}, {o}, {lse});
+    if (s != FA_OK) return s;
+    return launch_status(fa::launch_fwd_bf16_bsparse_split(d, causal, q, k, v, o, lse, B, Hq, Hkv, N, col_idx, nnz,
+                                                           row_chunks, n_row_chunks, row_merges, n_row_merges,
+                                                           n_row_slots, part_ws, softmax_scale, stream));
+}
+
+fa_status_t fa_bwd_bsparse_split(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                 const float* lse, void* dq, void* dk, void* dv, float* delta_ws, int B, int Hq,
+                                 int Hkv, int N, int d, int causal, const int* col_idx, const int* row_idx, int nnz,
+                                 const int* row_chunks, int n_row_chunks, const int* row_merges, int n_row_merges,
+                                 int n_row_slots, const int* col_chunks, int n_col_chunks, const int* col_merges,
+                                 int n_col_merges, int n_col_slots, float* part_ws, float softmax_scale,
+                                 fa_dtype_t dtype, hipStream_t stream) {
+    bool empty = false;
+    if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    fa_status_t s = check_shape(B, Hq, Hkv, N, d, causal, softmax_scale, &empty);
+    if (s != FA_OK || empty) return s;
+    const int64_t nb = ((int64_t)N + FA_BSPARSE_BLOCK - 1) / FA_BSPARSE_BLOCK;
+    if (nnz < 0 || nnz > nb * nb) return FA_ERR_SHAPE;
+    if (nnz > 0 && (!col_idx || !row_idx)) return FA_ERR_NULL;
+    if ((col_idx && !aligned(col_idx, 4)) || (row_idx && !aligned(row_idx, 4))) return FA_ERR_ALIGN;
+    const int slots = n_row_slots + n_col_slots;
+    s = check_split(N, nnz, row_chunks, n_row_chunks, row_merges, n_row_merges, n_row_slots, slots ? part_ws : nullptr,
+                    (int64_t)B * Hq);
+    if (s == FA_OK)
+        s = check_split(N, nnz, col_chunks, n_col_chunks, col_merges, n_col_merges, n_col_slots,
+                        slots ? part_ws : nullptr, (int64_t)B * Hkv);
+    if (s != FA_OK) return s;
+    s = slots > 0 ? check_ptrs({q, k, v, o, dO, delta_ws}, {lse}, {dq, dk, dv}, {part_ws})
+                  : check_ptrs({q, k, v, o, dO, delta_ws}, {lse}, {dq, dk, dv}, {});
+    if (s != FA_OK) return s;
+    hipError_t e = fa::launch_bwd_delta(dtype, d, o, dO, lse, delta_ws, B, Hq, N, stream);
+    if (e == hipSuccess)
+        e = fa::launch_bwd_bf16_bsparse_split(d, causal, q, k, v, dO, delta_ws, dq, dk, dv, B, Hq, Hkv, N, col_idx,
+                                              row_idx, nnz, row_chunks, n_row_chunks, row_merges, n_row_merges,
+                                              n_row_slots, col_chunks, n_col_chunks, col_merges, n_col_merges,
+                                              n_col_slots, part_ws, softmax_scale, stream);
+    return launch_status(e);
+}
+
+size_t fa_fwd_bsparse_split_workspace_bytes(int B, int Hq, int d, int n_row_slots) {
+    if (B < 0 || Hq < 0 || (d != 64 && d != 128) || n_row_slots < 0) return 0;
+    return (size_t)n_row_slots * B * Hq * FA_BSPARSE_BLOCK * (d + 1) * sizeof(float);
+}
+
+size_t fa_bwd_bsparse_split_workspace_bytes(int B, int Hq, int Hkv, int d, int n_row_slots, int n_col_slots) {
+    if (B < 0 || Hq < 0 || Hkv < 0 || (d != 64 && d != 128) || n_row_slots < 0 || n_col_slots < 0) return 0;
+    return ((size_t)n_row_slots * B * Hq + 2 * (size_t)n_col_slots * B * Hkv) * FA_BSPARSE_BLOCK * d * sizeof(float);
+}
+
 // Shape checks of the decode entry points; sets *empty for an empty problem.
 static fa_status_t check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                                 bool* empty) {

@@ -84,12 +84,13 @@ __device__ __forceinline__ void sched_dkdv_phase() {
 // and dS = P o (Z o dP r - D).  The workspace then holds -D (1 - p), the dP
 // accumulator starts from it, and dS = r P o (Z ? acc : -D (1 - p)); the
 // factor r goes into the final scales of dK and dV.
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false, bool SPLIT = false>
 __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int n_rows, int Npad, float c2,
-    float scale, int W, int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz, DropArgs drop) {
+    float scale, int W, int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz, DropArgs drop,
+    BspSplit sp) {
     static_assert(!(LOCAL && BSP), "one sparsity pattern at a time");
     static_assert(!(DROP && (LOCAL || BSP)), "dropout with the dense masks only");
     using Cfg = KVBf16Cfg<D>;
@@ -110,7 +111,9 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
     const int grp = wave >> 2;                      // waves w and w+4 share a SIMD
 
     const int nkb = (n_rows + BNK - 1) / BNK;
-    const PersistentSched sched(nkb * Hkv * B);
+    constexpr bool split = BSP && SPLIT;               // work items from sp.chunks
+    const int nit = split ? sp.nchunks : nkb;            // work items per (batch, K/V head)
+    const PersistentSched sched(nit * Hkv * B);
     for (int r = 0; sched.more(r); ++r) {
         const int lin = sched.item(r);
         if (lin < 0) continue;
@@ -119,7 +122,21 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         // out of the item loop into registers for the whole kernel
         int N = n_rows;
         asm volatile("" : "+s"(N));
-        const int kbk = lin % nkb, bg = lin / nkb;      // ascending key blocks: causal-heavy first
+        const int kbi = lin % nit, bg = lin / nit;
+        int kbk = kbi;                                  // ascending key blocks: causal-heavy first
+        // (block-sparse) the item's entries (row blocks) bbeg .. bbeg+bcnt-1
+        int bbeg = 0, bcnt = 0;
+        if constexpr (BSP) {
+            if (split) {
+                const int* c = sp.chunks + 4 * kbi;
+                kbk = min(max(c[0], 0), nkb - 1);
+                bbeg = min(max(c[1], 0), nnz);
+                bcnt = min(max(c[2], bbeg), nnz) - bbeg;
+            } else {
+                bbeg = min(max(bptr[kbk], 0), nnz);
+                bcnt = min(max(bptr[kbk + 1], bbeg), nnz) - bbeg;
+            }
+        }
         const int g = bg % Hkv, b = bg / Hkv;
         const int G = Hq / Hkv;
         const int k0 = kbk * BNK;
@@ -136,10 +153,8 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
         // (block-sparse) the listed row blocks bbeg .. bbeg+bcnt-1, SPB steps
         // each (fewer for a last block that ends past N): nsh steps per head
         constexpr int SPB = BNK / BMQ;
-        int bbeg = 0, nsh = 0;
+        int nsh = 0;
         if constexpr (BSP) {
-            bbeg = min(max(bptr[kbk], 0), nnz);
-            const int bcnt = min(max(bptr[kbk + 1], bbeg), nnz) - bbeg;
             if (bcnt) nsh = SPB * (bcnt - 1) + min(SPB, nqt - min(max(bidx[bbeg + bcnt - 1], 0), nkb - 1) * SPB);
         }
         // query block (of BMQ rows) of a head's j-th step
@@ -452,7 +467,31 @@ __global__ __launch_bounds__(KVBf16Cfg<D>::kThreads, 2) void bwd_dkdv_bf16_kerne
             }
         }
 
-        if (krow < N) {
+        // (split column) the partial slot, read here rather than kept live
+        int slot = -1;
+        if (split) slot = sp.chunks[4 * kbi + 3] < sp.nslots ? sp.chunks[4 * kbi + 3] : -1;
+        if (BSP && slot >= 0 && krow < N) {
+            // (split column) this item's shares of dK and dV, float32, for the
+            // merge; row pointers from an opaque lane, as below
+            int le = lane;
+            asm volatile("" : "+v"(le));
+            const int64_t prow = ((int64_t)slot * B * Hkv + bg) * BNK + 32 * wave + (le & 31);
+            float* Pk = sp.part + prow * D + 4 * (le >> 5);
+            float* Pv = sp.part + ((int64_t)sp.nslots * B * Hkv * BNK + prow) * D + 4 * (le >> 5);
+#pragma unroll
+            for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    f32x4 wk, wv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        wk[e] = dkacc[ct][4 * gq + e] * scale;
+                        wv[e] = dvacc[ct][4 * gq + e];
+                    }
+                    *reinterpret_cast<f32x4*>(Pk + 32 * ct + 8 * gq) = wk;
+                    *reinterpret_cast<f32x4*>(Pv + 32 * ct + 8 * gq) = wv;
+                }
+        } else if (krow < N) {
             // per-lane row pointers from an opaque lane: hoisted out of the
             // item loop they would be spilled
             int le = lane;
@@ -534,12 +573,12 @@ __device__ __forceinline__ void sched_dq_phase() {
 // DROP: through attention dropout, as in the dK/dV kernel: the workspace holds
 // -D (1 - p), dS = r P o (Z ? dP + (-D (1 - p)) : -D (1 - p)) with the mask
 // regenerated per element, and r = 1/(1 - p) goes into dQ's final scale.
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false, bool SPLIT = false>
 __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ WSd, const float* __restrict__ WSl,
     uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int n_rows, int Npad, float c2, float scale, int W,
-    int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz, DropArgs drop) {
+    int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz, DropArgs drop, BspSplit sp) {
     static_assert(!(LOCAL && BSP), "one sparsity pattern at a time");
     static_assert(!(DROP && (LOCAL || BSP)), "dropout with the dense masks only");
     using Cfg = QBf16Cfg<D>;
@@ -554,7 +593,9 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     const int grp = wave >> 2;                  // waves w and w+4 share a SIMD
 
     const int nmb = (n_rows + BM - 1) / BM;
-    const PersistentSched sched(nmb * Hq * B);
+    constexpr bool split = BSP && SPLIT;               // work items from sp.chunks
+    const int nit = split ? sp.nchunks : nmb;            // work items per (batch, head)
+    const PersistentSched sched(nit * Hq * B);
     for (int r = 0; sched.more(r); ++r) {
         const int lin = sched.item(r);
         if (lin < 0) continue;
@@ -563,9 +604,22 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
         // out of the item loop into registers for the whole kernel
         int N = n_rows;
         asm volatile("" : "+s"(N));
-        const int mbi = lin % nmb, bh = lin / nmb;
+        const int mbi = lin % nit, bh = lin / nit;
         const int h = bh % Hq, b = bh / Hq;
-        const int mb = CAUSAL ? nmb - 1 - mbi : mbi;
+        int mb = CAUSAL ? nmb - 1 - mbi : mbi;
+        // (block-sparse) the item's entries bbeg .. bbeg+bcnt-1
+        int bbeg = 0, bcnt = 0;
+        if constexpr (BSP) {
+            if (split) {
+                const int* c = sp.chunks + 4 * mbi;
+                mb = min(max(c[0], 0), nmb - 1);
+                bbeg = min(max(c[1], 0), nnz);
+                bcnt = min(max(c[2], bbeg), nnz) - bbeg;
+            } else {
+                bbeg = min(max(bptr[mb], 0), nnz);
+                bcnt = min(max(bptr[mb + 1], bbeg), nnz) - bbeg;
+            }
+        }
         const int g = h / (Hq / Hkv);
         const int64_t rowbase = ((int64_t)b * Hq + h) * N;
         const uint16_t* Kg = K + ((int64_t)b * Hkv + g) * N * D;
@@ -579,11 +633,6 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
         const int ns = LOCAL ? min((S + BNK - 1) / BNK, ts) : 0;  // global-token tiles before it
         constexpr int TPB = BM / BNK;               // key tiles per mask block
         const int ntk = (N + BNK - 1) / BNK;
-        int bbeg = 0, bcnt = 0;
-        if constexpr (BSP) {
-            bbeg = min(max(bptr[mb], 0), nnz);
-            bcnt = min(max(bptr[mb + 1], bbeg), nnz) - bbeg;
-        }
         auto bcol = [&](int e) __attribute__((always_inline)) { return min(max(bidx[bbeg + e], 0), nmb - 1); };
         auto tile_of = [&](int t) __attribute__((always_inline)) {
             return BSP ? min(bcol(t / TPB) * TPB + t % TPB, ntk - 1) : LOCAL ? (t < ns ? t : t - ns + ts) : t;
@@ -788,7 +837,25 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
             }
         }
 
-        if (qrow < N) {
+        // (split row) the partial slot, read here rather than kept live
+        int slot = -1;
+        if (split) slot = sp.chunks[4 * mbi + 3] < sp.nslots ? sp.chunks[4 * mbi + 3] : -1;
+        if (BSP && slot >= 0 && qrow < N) {
+            // (split row) this item's share of dQ, float32, for the merge; row
+            // pointer from an opaque lane, as below
+            int le = lane;
+            asm volatile("" : "+v"(le));
+            float* P = sp.part + (((int64_t)slot * B * Hq + bh) * BM + 32 * wave + (le & 31)) * D + 4 * (le >> 5);
+#pragma unroll
+            for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    f32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = dqacc[ct][4 * gq + e] * scale;
+                    *reinterpret_cast<f32x4*>(P + 32 * ct + 8 * gq) = w;
+                }
+        } else if (qrow < N) {
             // per-lane row pointer from an opaque lane: hoisted out of the
             // item loop it would be spilled
             int le = lane;
@@ -808,39 +875,90 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
     }
 }
 
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false, bool SPLIT = false>
 static hipError_t launch_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* ws,
                               void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale, hipStream_t st,
                               int W = 0, int S = 0, const int* bptr = nullptr, const int* bidx = nullptr,
-                              int nnz = 0, DropArgs drop = {0u, 0u, 0u, 1.f}) {
+                              int nnz = 0, DropArgs drop = {0u, 0u, 0u, 1.f},
+                              BspSplit sp = {nullptr, 0, 0, nullptr}) {
     using Cfg = KVBf16Cfg<D>;
     const int nkb = (N + Cfg::BNK - 1) / Cfg::BNK;
+    const int nit = BSP && SPLIT ? sp.nchunks : nkb;
     const int Np = ws_rows(N);
     static PerDevice slots;
-    const int grid = persistent_grid((const void*)bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>,
-                                     Cfg::kThreads, nkb * Hkv * B, slots);
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>), dim3((unsigned)grid),
+    const int grid = persistent_grid((const void*)bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP, SPLIT>,
+                                     Cfg::kThreads, nit * Hkv * B, slots);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP, SPLIT>), dim3((unsigned)grid),
                        dim3(Cfg::kThreads), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dO, ws, ws + (int64_t)B * Hq * Np, (uint16_t*)dk, (uint16_t*)dv, B, Hq, Hkv, N,
-                       Np, scale * kLog2e, scale, W, S, bptr, bidx, nnz, drop);
+                       Np, scale * kLog2e, scale, W, S, bptr, bidx, nnz, drop, sp);
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false, bool SPLIT = false>
 static hipError_t launch_dq(const void* q, const void* k, const void* v, const void* dO, const float* ws, void* dq,
                             int B, int Hq, int Hkv, int N, float scale, hipStream_t st, int W = 0, int S = 0,
                             const int* bptr = nullptr, const int* bidx = nullptr, int nnz = 0,
-                            DropArgs drop = {0u, 0u, 0u, 1.f}) {
+                            DropArgs drop = {0u, 0u, 0u, 1.f}, BspSplit sp = {nullptr, 0, 0, nullptr}) {
     using Cfg = QBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
+    const int nit = BSP && SPLIT ? sp.nchunks : nmb;
     const int Np = ws_rows(N);
     static PerDevice slots;
-    const int grid = persistent_grid((const void*)bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>, Cfg::kThreads,
-                                     nmb * Hq * B, slots);
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>), dim3((unsigned)grid),
+    const int grid = persistent_grid((const void*)bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP, SPLIT>, Cfg::kThreads,
+                                     nit * Hq * B, slots);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP, SPLIT>), dim3((unsigned)grid),
                        dim3(Cfg::kThreads), 0, st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dO, ws, ws + (int64_t)B * Hq * Np, (uint16_t*)dq, B, Hq, Hkv, N, Np,
-                       scale * kLog2e, scale, W, S, bptr, bidx, nnz, drop);
+                       scale * kLog2e, scale, W, S, bptr, bidx, nnz, drop, sp);
+    return hipGetLastError();
+}
+
+// Sum of a split block's float32 partials into a bf16 output (block-sparse
+// backward): merge m = merges[4m .. 4m+2] = (block r, first slot s0, slot
+// count ns); rows r * 256 .. of each of the nh heads (the query heads for dQ,
+// the K/V heads for dK and dV) get sum_s part[s0 + s][head][row].  One
+// workgroup per (merge, head); a thread per 8 columns of a row.
+template <int D>
+__global__ __launch_bounds__(256) void bsp_merge_sum_kernel(const int* __restrict__ merges, int nmerge,
+                                                            const float* __restrict__ part, int nslots,
+                                                            uint16_t* __restrict__ out, int nh, int N) {
+    constexpr int BR = 256, CPR = D / 8;
+    const int mi = blockIdx.x % nmerge, hd = blockIdx.x / nmerge;
+    const int nb = (N + BR - 1) / BR;
+    const int r = min(max(merges[4 * mi], 0), nb - 1);
+    const int s0 = min(max(merges[4 * mi + 1], 0), nslots);
+    const int ns = min(max(merges[4 * mi + 2], 0), nslots - s0);
+    for (int idx = threadIdx.x; idx < BR * CPR; idx += blockDim.x) {
+        const int row = idx / CPR, c8 = (idx % CPR) * 8;
+        const int i = r * BR + row;
+        if (i >= N) continue;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < ns; ++s) {
+            const float* p = part + (((int64_t)(s0 + s) * nh + hd) * BR + row) * D + c8;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(p), c = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[e] += a[e];
+                acc[4 + e] += c[e];
+            }
+        }
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+        *reinterpret_cast<u32x4*>(out + ((int64_t)hd * N + i) * D + c8) = w;
+    }
+}
+
+static hipError_t launch_merge_sum(int d, const int* merges, int nmerge, const float* part, int nslots, void* out,
+                                   int nh, int N, hipStream_t st) {
+    if (nmerge <= 0) return hipSuccess;
+    if (d == 64)
+        hipLaunchKernelGGL(bsp_merge_sum_kernel<64>, dim3((unsigned)(nmerge * nh)), dim3(256), 0, st, merges, nmerge,
+                           part, nslots, (uint16_t*)out, nh, N);
+    else
+        hipLaunchKernelGGL(bsp_merge_sum_kernel<128>, dim3((unsigned)(nmerge * nh)), dim3(256), 0, st, merges,
+                           nmerge, part, nslots, (uint16_t*)out, nh, N);
     return hipGetLastError();
 }
 
@@ -883,6 +1001,43 @@ hipError_t launch_bwd_bf16_bsparse(int d, int causal, const void* q, const void*
     if (e != hipSuccess) return e;
     if (d == 64) return causal ? launch_dq<64, true, false, true>(QA) : launch_dq<64, false, false, true>(QA);
     return causal ? launch_dq<128, true, false, true>(QA) : launch_dq<128, false, false, true>(QA);
+#undef KV
+#undef QA
+}
+
+hipError_t launch_bwd_bf16_bsparse_split(int d, int causal, const void* q, const void* k, const void* v,
+                                         const void* dO, const float* ws, void* dq, void* dk, void* dv, int B, int Hq,
+                                         int Hkv, int N, const int* col_idx, const int* row_idx, int nnz,
+                                         const int* row_chunks, int n_row_chunks, const int* row_merges,
+                                         int n_row_merges, int n_row_slots, const int* col_chunks, int n_col_chunks,
+                                         const int* col_merges, int n_col_merges, int n_col_slots, float* part,
+                                         float scale, hipStream_t st) {
+    // partials: dQ [n_row_slots][B Hq][256][d], then dK and dV [n_col_slots][B Hkv][256][d] each
+    float* pq = part;
+    float* pkv = part + (int64_t)n_row_slots * B * Hq * 256 * d;
+    const BspSplit sq{row_chunks, n_row_chunks, n_row_slots, pq}, skv{col_chunks, n_col_chunks, n_col_slots, pkv};
+    const DropArgs nd{0u, 0u, 0u, 1.f};
+#define KV q, k, v, dO, ws, dk, dv, B, Hq, Hkv, N, scale, st, 0, 0, nullptr, row_idx, nnz, nd, skv
+#define QA q, k, v, dO, ws, dq, B, Hq, Hkv, N, scale, st, 0, 0, nullptr, col_idx, nnz, nd, sq
+    hipError_t e = hipErrorInvalidValue;
+    if (d == 64)
+        e = causal ? launch_dkdv<64, true, false, true, false, true>(KV)
+                   : launch_dkdv<64, false, false, true, false, true>(KV);
+    if (d == 128)
+        e = causal ? launch_dkdv<128, true, false, true, false, true>(KV)
+                   : launch_dkdv<128, false, false, true, false, true>(KV);
+    if (e == hipSuccess) e = launch_merge_sum(d, col_merges, n_col_merges, pkv, n_col_slots, dk, B * Hkv, N, st);
+    if (e == hipSuccess)
+        e = launch_merge_sum(d, col_merges, n_col_merges, pkv + (int64_t)n_col_slots * B * Hkv * 256 * d, n_col_slots,
+                             dv, B * Hkv, N, st);
+    if (e != hipSuccess) return e;
+    if (d == 64)
+        e = causal ? launch_dq<64, true, false, true, false, true>(QA) : launch_dq<64, false, false, true, false, true>(QA);
+    else
+        e = causal ? launch_dq<128, true, false, true, false, true>(QA)
+                   : launch_dq<128, false, false, true, false, true>(QA);
+    if (e == hipSuccess) e = launch_merge_sum(d, row_merges, n_row_merges, pq, n_row_slots, dq, B * Hq, N, st);
+    return e;
 #undef KV
 #undef QA
 }

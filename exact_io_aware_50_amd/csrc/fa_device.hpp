@@ -516,6 +516,18 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[NC][4], uint32_t k0,
     }
 }
 
+// A work split of a block mask (block-sparse kernels): work item c covers the
+// entries e0 .. e1-1 of row (or column) block r of the compressed layout,
+// chunks[4c .. 4c+3] = (r, e0, e1, slot).  slot < 0: the item is the whole
+// row (column) and writes the outputs; slot >= 0: it writes a float32 partial
+// into that slot of `part`, and a merge pass combines a block's partials.
+// chunks == nullptr: one item per block row (column), the plain layout.
+struct BspSplit {
+    const int* chunks;
+    int nchunks, nslots;
+    float* part;
+};
+
 // Dropout parameters.  One Philox call serves a 4 x 4 block of the score
 // matrix, one byte per element: element (query i, key j) of (batch b, query
 // head h) takes byte 4 (i % 4) + j % 4 of Philox((j / 4, i / 4, b * Hq + h,

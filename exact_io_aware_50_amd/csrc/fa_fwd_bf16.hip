@@ -92,11 +92,11 @@ __device__ __forceinline__ void sched_gemm_phase() {
 // page of the self-hosted LLM glossary: dropout is one of the operations fused
 // into the kernel).  The normaliser and LSE are those of the undropped softmax;
 // kept probabilities are scaled by 1 / (1 - p), p = thr / 256 (DropArgs).
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false, bool SPLIT = false>
 __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int N, float c2, int W,
-    int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz, DropArgs drop) {
+    int S, const int* __restrict__ bptr, const int* __restrict__ bidx, int nnz, DropArgs drop, BspSplit sp) {
     static_assert(!(LOCAL && BSP), "one sparsity pattern at a time");
     using Cfg = FwdBf16Cfg<D>;
     using KT = typename Cfg::KT;
@@ -108,15 +108,30 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
     const int grp = wave >> 2;                                           // waves w and w+4 share a SIMD
 
     const int nmb = (N + BM - 1) / BM;
-    const PersistentSched sched(nmb * Hq * B);
+    constexpr bool split = BSP && SPLIT;               // work items from sp.chunks
+    const int nit = split ? sp.nchunks : nmb;            // work items per (batch, head)
+    const PersistentSched sched(nit * Hq * B);
     for (int r = 0; sched.more(r); ++r) {
         const int lin = sched.item(r);
         if (lin < 0) continue;
         const int lane = threadIdx.x & 63;
         const int l32 = lane & 31, hh = lane >> 5;
-        const int mbi = lin % nmb, bh = lin / nmb;
+        const int mbi = lin % nit, bh = lin / nit;
         const int h = bh % Hq, b = bh / Hq;
-        const int mb = CAUSAL ? nmb - 1 - mbi : mbi;      // longest causal rows first
+        int mb = CAUSAL ? nmb - 1 - mbi : mbi;            // longest causal rows first
+        // (block-sparse) the item's entries bbeg .. bbeg+bcnt-1
+        int bbeg = 0, bcnt = 0;
+        if constexpr (BSP) {
+            if (split) {
+                const int* c = sp.chunks + 4 * mbi;
+                mb = min(max(c[0], 0), nmb - 1);
+                bbeg = min(max(c[1], 0), nnz);
+                bcnt = min(max(c[2], bbeg), nnz) - bbeg;
+            } else {
+                bbeg = min(max(bptr[mb], 0), nnz);
+                bcnt = min(max(bptr[mb + 1], bbeg), nnz) - bbeg;
+            }
+        }
         const int g = h / (Hq / Hkv);
         const uint16_t* Qh = Q + ((int64_t)b * Hq + h) * N * D;
         const uint16_t* Kh = K + ((int64_t)b * Hkv + g) * N * D;
@@ -128,14 +143,8 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
         const int kend = CAUSAL ? min(N, q0 + BM) : N;
         const int ts = LOCAL ? max(0, q0 - W + 1) / BN : 0;   // first window tile of the workgroup
         const int ns = LOCAL ? min((S + BN - 1) / BN, ts) : 0;    // global-token tiles before it
-        // (block-sparse) the row block's entries bbeg .. bbeg+bcnt-1
         constexpr int TPB = BM / BN;                      // tiles per mask block
         const int ntk = (N + BN - 1) / BN;
-        int bbeg = 0, bcnt = 0;
-        if constexpr (BSP) {
-            bbeg = min(max(bptr[mb], 0), nnz);
-            bcnt = min(max(bptr[mb + 1], bbeg), nnz) - bbeg;
-        }
         auto bcol = [&](int e) __attribute__((always_inline)) { return min(max(bidx[bbeg + e], 0), nmb - 1); };
         // the workgroup's t-th tile: tiles 0 .. ns-1, then ts, ts+1, ... (local);
         // tile t % TPB of the (t / TPB)-th listed block (block-sparse)
@@ -376,7 +385,25 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
 
         // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
         const float ltot = pair_sum(lsum);
-        if (qrow < N) {
+        // (split row) the partial slot, read here rather than kept live
+        int slot = -1;
+        if (split) slot = sp.chunks[4 * mbi + 3] < sp.nslots ? sp.chunks[4 * mbi + 3] : -1;
+        if (BSP && slot >= 0 && qrow < N) {
+            // (split row) this item's O and base-2 log-sum-exp, float32, for the merge
+            const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+            const int64_t prow = ((int64_t)slot * B * Hq + bh) * BM + (qrow - q0);
+            float* Op = sp.part + prow * D;
+#pragma unroll
+            for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    f32x4 w;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = oacc[ct][4 * gq + e] * inv;
+                    *reinterpret_cast<f32x4*>(Op + 32 * ct + 8 * gq + 4 * hh) = w;
+                }
+            if (hh == 0) sp.part[(int64_t)sp.nslots * B * Hq * BM * D + prow] = ltot > 0.f ? m + log2f(ltot) : -INFINITY;
+        } else if (qrow < N) {
             float inv = BSP && !(ltot > 0.f) ? 0.f : 1.0f / ltot;   // (block-sparse) a row with no key: O = 0
             if constexpr (DROP) inv *= drop.rkeep;
             uint16_t* Orow = O + (((int64_t)b * Hq + h) * N + qrow) * D;
@@ -395,18 +422,78 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
     }
 }
 
-template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false>
+template <int D, bool CAUSAL, bool LOCAL = false, bool BSP = false, bool DROP = false, bool SPLIT = false>
 static hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                          int N, float scale, hipStream_t st, int W = 0, int S = 0, const int* bptr = nullptr,
-                         const int* bidx = nullptr, int nnz = 0, DropArgs drop = {0u, 0u, 0u, 1.f}) {
+                         const int* bidx = nullptr, int nnz = 0, DropArgs drop = {0u, 0u, 0u, 1.f},
+                         BspSplit sp = {nullptr, 0, 0, nullptr}) {
     using Cfg = FwdBf16Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
+    const int nit = BSP && SPLIT ? sp.nchunks : nmb;
     static PerDevice slots;
-    const int grid = persistent_grid((const void*)fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>, Cfg::kThreads,
-                                     nmb * Hq * B, slots);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0,
+    const int grid = persistent_grid((const void*)fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP, SPLIT>, Cfg::kThreads,
+                                     nit * Hq * B, slots);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, LOCAL, BSP, DROP, SPLIT>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0,
                        st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, B, Hq, Hkv,
-                       N, scale * kLog2e, W, S, bptr, bidx, nnz, drop);
+                       N, scale * kLog2e, W, S, bptr, bidx, nnz, drop, sp);
+    return hipGetLastError();
+}
+
+// Merge of a split row block's partials (block-sparse forward): merge m =
+// merges[4m .. 4m+2] = (row block r, first slot s0, slot count ns).  With
+// L_s the base-2 log-sum-exp and O_s the output of slot s over its keys:
+// L = log2 sum_s 2^L_s, O = sum_s 2^(L_s - L) O_s, LSE = L ln 2 (the online
+// softmax's rescale, applied once per slot).  A row no slot saw: O = 0,
+// LSE = -inf.  One workgroup per (merge, batch x head); a thread per 8
+// columns of a row.
+template <int D>
+__global__ __launch_bounds__(256) void bsp_merge_fwd_kernel(const int* __restrict__ merges, int nmerge,
+                                                            const float* __restrict__ part, int nslots,
+                                                            uint16_t* __restrict__ O, float* __restrict__ LSE, int BH,
+                                                            int N) {
+    constexpr int BM = FwdBf16Cfg<D>::BM, CPR = D / 8;
+    const int mi = blockIdx.x % nmerge, bh = blockIdx.x / nmerge;
+    const int nmb = (N + BM - 1) / BM;
+    const int r = min(max(merges[4 * mi], 0), nmb - 1);
+    const int s0 = min(max(merges[4 * mi + 1], 0), nslots);
+    const int ns = min(max(merges[4 * mi + 2], 0), nslots - s0);
+    const float* Lp = part + (int64_t)nslots * BH * BM * D;
+    for (int idx = threadIdx.x; idx < BM * CPR; idx += blockDim.x) {
+        const int row = idx / CPR, c8 = (idx % CPR) * 8;
+        const int i = r * BM + row;
+        if (i >= N) continue;
+        float lmax = -INFINITY;
+        for (int s = 0; s < ns; ++s) lmax = fmaxf(lmax, Lp[((int64_t)(s0 + s) * BH + bh) * BM + row]);
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
+        if (lmax > -INFINITY) {
+            for (int s = 0; s < ns; ++s) {
+                const int64_t prow = ((int64_t)(s0 + s) * BH + bh) * BM + row;
+                const float wgt = exp2f(Lp[prow] - lmax);
+                const f32x4 a = *reinterpret_cast<const f32x4*>(part + prow * D + c8);
+                const f32x4 c = *reinterpret_cast<const f32x4*>(part + prow * D + c8 + 4);
+                wsum += wgt;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[e] += wgt * a[e];
+                    acc[4 + e] += wgt * c[e];
+                }
+            }
+        }
+        const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+        *reinterpret_cast<u32x4*>(O + ((int64_t)bh * N + i) * D + c8) = w;
+        if (c8 == 0) LSE[(int64_t)bh * N + i] = wsum > 0.f ? (lmax + log2f(wsum)) * kLn2 : -INFINITY;
+    }
+}
+
+template <int D>
+static hipError_t launch_merge_fwd(const int* merges, int nmerge, const float* part, int nslots, void* o, float* lse,
+                                   int BH, int N, hipStream_t st) {
+    if (nmerge <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bsp_merge_fwd_kernel<D>, dim3((unsigned)(nmerge * BH)), dim3(256), 0, st, merges, nmerge,
+                       part, nslots, (uint16_t*)o, lse, BH, N);
     return hipGetLastError();
 }
 
@@ -434,6 +521,25 @@ hipError_t launch_fwd_bf16_bsparse(int d, int causal, const void* q, const void*
     if (d == 128) return causal ? launch<128, true, false, true>(ARGS) : launch<128, false, false, true>(ARGS);
 #undef ARGS
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_bf16_bsparse_split(int d, int causal, const void* q, const void* k, const void* v, void* o,
+                                         float* lse, int B, int Hq, int Hkv, int N, const int* col_idx, int nnz,
+                                         const int* chunks, int nchunks, const int* merges, int nmerge, int nslots,
+                                         float* part, float scale, hipStream_t st) {
+    const BspSplit sp{chunks, nchunks, nslots, part};
+    const DropArgs nd{0u, 0u, 0u, 1.f};
+    hipError_t e = hipErrorInvalidValue;
+#define ARGS q, k, v, o, lse, B, Hq, Hkv, N, scale, st, 0, 0, nullptr, col_idx, nnz, nd, sp
+    if (d == 64)
+        e = causal ? launch<64, true, false, true, false, true>(ARGS) : launch<64, false, false, true, false, true>(ARGS);
+    if (d == 128)
+        e = causal ? launch<128, true, false, true, false, true>(ARGS)
+                   : launch<128, false, false, true, false, true>(ARGS);
+#undef ARGS
+    if (e != hipSuccess) return e;
+    return d == 64 ? launch_merge_fwd<64>(merges, nmerge, part, nslots, o, lse, B * Hq, N, st)
+                   : launch_merge_fwd<128>(merges, nmerge, part, nslots, o, lse, B * Hq, N, st);
 }
 
 hipError_t launch_fwd_bf16_dropout(int d, int causal, const void* q, const void* k, const void* v, void* o,

@@ -122,6 +122,21 @@ hipError_t launch_fwd_bf16_dropout(int d, int causal, const void* q, const void*
 
 // Backward through that dropout (the same mask regenerated), bf16: dK/dV then
 // dQ, from a workspace written by launch_bwd_delta with keep = 1 - p.
+// Block-sparse with a work split (heavy block rows / columns cut into several
+// items): the attention kernels write float32 partials of split blocks into
+// `part`, merge passes combine them (the LSE merge forward, sums backward).
+hipError_t launch_fwd_bf16_bsparse_split(int d, int causal, const void* q, const void* k, const void* v, void* o,
+                                         float* lse, int B, int Hq, int Hkv, int N, const int* col_idx, int nnz,
+                                         const int* chunks, int nchunks, const int* merges, int nmerge, int nslots,
+                                         float* part, float scale, hipStream_t st);
+hipError_t launch_bwd_bf16_bsparse_split(int d, int causal, const void* q, const void* k, const void* v,
+                                         const void* dO, const float* ws, void* dq, void* dk, void* dv, int B, int Hq,
+                                         int Hkv, int N, const int* col_idx, const int* row_idx, int nnz,
+                                         const int* row_chunks, int n_row_chunks, const int* row_merges,
+                                         int n_row_merges, int n_row_slots, const int* col_chunks, int n_col_chunks,
+                                         const int* col_merges, int n_col_merges, int n_col_slots, float* part,
+                                         float scale, hipStream_t st);
+
 hipError_t launch_bwd_bf16_dropout(int d, int causal, const void* q, const void* k, const void* v, const void* dO,
                                    const float* ws, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
                                    uint32_t thr, uint64_t seed, float rkeep, float scale, hipStream_t st);

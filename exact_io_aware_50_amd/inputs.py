@@ -110,6 +110,13 @@ BSPARSE_WORKLOADS = {
         Workload("bsparse_bf16_n16384 (B=1 Hq=32 Hkv=8 N=16384 d=128, non-causal, 256-blocks: 3-block band "
                  "and 2 random permutations, bf16)", 8, 1, 32, 8, 16384, 128, False, "bf16"),
         dict(band=1, n_global=0, n_random=2, seed=8)),
+    # the same with one global block row and column (a row that sees every
+    # block and a key block every row sees): 64 blocks against about 6
+    "bsparse_global_bf16_n16384": (
+        Workload("bsparse_global_bf16_n16384 (B=1 Hq=32 Hkv=8 N=16384 d=128, non-causal, 256-blocks: 3-block "
+                 "band, 2 random permutations, 1 global block row and column, bf16)", 8, 1, 32, 8, 16384, 128, False,
+                 "bf16"),
+        dict(band=1, n_global=1, n_random=2, seed=8)),
 }
 
 

@@ -333,6 +333,63 @@ fa_status_t fa_bwd_bsparse(const void* q, const void* k, const void* v,
                            float softmax_scale, fa_dtype_t dtype, hipStream_t stream);
 
 /*
+ * Block-sparse attention with a work split, for masks whose block rows or
+ * columns differ widely in length (a global block row or column sees every
+ * block): the same results as fa_fwd_bsparse / fa_bwd_bsparse up to float32
+ * summation order (same pages; the split is the split-KV rescale of the
+ * "Online Softmax" section of "flash attention io aware" applied to key
+ * chunks).  A work item is a run of consecutive entries of one block row (for
+ * the forward and dQ) or one block column (for dK/dV); a long row or column
+ * is cut into several items, run in parallel, that write float32 partials,
+ * and a merge pass combines them: the log-sum-exp merge for O and LSE, sums
+ * for dQ, dK and dV.  Tables (device int32, 16-byte aligned, four ints per
+ * entry; the library neither copies nor frees them):
+ *   row_chunks[4c..4c+3] = (r, e0, e1, slot): entries e0 .. e1-1 of the
+ *       compressed rows (col_idx) of row block r; slot = -1 when the item is
+ *       all of row r, else the partial slot it writes (0 <= slot < n_row_slots).
+ *       Every row block needs at least one item (an empty row: e0 = e1).
+ *   row_merges[4m..4m+3] = (r, s0, ns, 0): row block r is the merge of slots
+ *       s0 .. s0+ns-1 (its split items).
+ *   col_chunks, col_merges: the same over the compressed columns (row_idx)
+ *       and the key blocks, with n_col_slots slots.
+ * 1 <= n_*_chunks <= nb + nnz, 0 <= n_*_merges <= nb, 0 <= n_*_slots <= nnz.
+ * part_ws (float, 16-byte aligned; NULL allowed when no slot is used) holds
+ * the partials: fa_fwd_bsparse_split_workspace_bytes() and
+ * fa_bwd_bsparse_split_workspace_bytes() bytes.  Table entries are clamped on
+ * the device, so malformed tables read and write nothing out of bounds, but
+ * then the results are unspecified.  Other arguments, layouts and errors as
+ * fa_fwd_bsparse / fa_bwd_bsparse (row_ptr and col_ptr are not needed: the
+ * items carry their ranges); delta_ws as fa_bwd.
+ */
+fa_status_t fa_fwd_bsparse_split(const void* q, const void* k, const void* v,
+                                 void* o, float* lse,
+                                 int B, int Hq, int Hkv, int N, int d, int causal,
+                                 const int* col_idx, int nnz,
+                                 const int* row_chunks, int n_row_chunks,
+                                 const int* row_merges, int n_row_merges, int n_row_slots,
+                                 float* part_ws,
+                                 float softmax_scale, fa_dtype_t dtype, hipStream_t stream);
+
+fa_status_t fa_bwd_bsparse_split(const void* q, const void* k, const void* v,
+                                 const void* o, const void* dO, const float* lse,
+                                 void* dq, void* dk, void* dv,
+                                 float* delta_ws,
+                                 int B, int Hq, int Hkv, int N, int d, int causal,
+                                 const int* col_idx, const int* row_idx, int nnz,
+                                 const int* row_chunks, int n_row_chunks,
+                                 const int* row_merges, int n_row_merges, int n_row_slots,
+                                 const int* col_chunks, int n_col_chunks,
+                                 const int* col_merges, int n_col_merges, int n_col_slots,
+                                 float* part_ws,
+                                 float softmax_scale, fa_dtype_t dtype, hipStream_t stream);
+
+/* Bytes of part_ws: n_row_slots * B * Hq * 256 * (d + 1) * 4 for the forward;
+ * (n_row_slots * B * Hq + 2 * n_col_slots * B * Hkv) * 256 * d * 4 for the
+ * backward (0 for invalid arguments). */
+size_t fa_fwd_bsparse_split_workspace_bytes(int B, int Hq, int d, int n_row_slots);
+size_t fa_bwd_bsparse_split_workspace_bytes(int B, int Hq, int Hkv, int d, int n_row_slots, int n_col_slots);
+
+/*
  * Decode: attention of Nq new query rows against a key/value cache of Nk
  * rows.  "Paper digest: FlashAttention", section "Limits" (decode-time
  * attention reads a large KV cache for few queries); self-hosted LLM

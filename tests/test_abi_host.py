@@ -30,7 +30,9 @@ def test_library_exports_every_declared_function():
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_delta", "fa_bwd_dkdv", "fa_bwd_dq",
                           "fa_bwd_workspace_bytes", "fa_quantize_fp8", "fa_fwd_local", "fa_bwd_local", "fa_decode",
-                          "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd_fp8",
+                          "fa_fwd_bsparse", "fa_bwd_bsparse", "fa_fwd_bsparse_split", "fa_bwd_bsparse_split",
+                          "fa_fwd_bsparse_split_workspace_bytes", "fa_bwd_bsparse_split_workspace_bytes",
+                          "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd_fp8",
                           "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
                           "fa_engine_clock_probe", "fa_status_string", "fa_abi_version"}
     for n in names:
@@ -238,6 +240,76 @@ def test_bsparse_validation():
     assert fa.fa_bwd_bsparse(**{**bw, "delta_ws": None}) == 1
     assert fa.fa_bwd_bsparse(**{**bw, "Hq": 3}) == 2
     assert fa.fa_bwd_bsparse(**{**bw, "B": 0}) == 0
+
+
+def test_bsparse_split_validation():
+    """The split entry points reject bad tables, counts and buffers on the host."""
+    from exact_io_aware_50_amd import fa
+    f = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, Hq=2, Hkv=2, N=600, d=128, causal=0, col_idx=A[5],
+             nnz=5, row_chunks=A[6], n_row_chunks=4, row_merges=A[7], n_row_merges=1, n_row_slots=2, part_ws=A[8],
+             softmax_scale=0.1, dtype=1, stream=None)
+    assert fa.fa_fwd_bsparse_split(**{**f, "n_row_chunks": 0}) == 2
+    assert fa.fa_fwd_bsparse_split(**{**f, "n_row_chunks": 9}) == 2          # more than nb + nnz = 8
+    assert fa.fa_fwd_bsparse_split(**{**f, "n_row_merges": 4}) == 2          # more than nb = 3
+    assert fa.fa_fwd_bsparse_split(**{**f, "n_row_slots": 6}) == 2           # more than nnz
+    assert fa.fa_fwd_bsparse_split(**{**f, "n_row_slots": -1}) == 2
+    assert fa.fa_fwd_bsparse_split(**{**f, "row_chunks": None}) == 1
+    assert fa.fa_fwd_bsparse_split(**{**f, "row_merges": None}) == 1
+    assert fa.fa_fwd_bsparse_split(**{**f, "part_ws": None}) == 1
+    assert fa.fa_fwd_bsparse_split(**{**f, "col_idx": None}) == 1
+    assert fa.fa_fwd_bsparse_split(**{**f, "row_chunks": A[6] + 4}) == 4
+    assert fa.fa_fwd_bsparse_split(**{**f, "part_ws": A[8] + 8}) == 4
+    assert fa.fa_fwd_bsparse_split(**{**f, "part_ws": A[3]}) == 6             # partials over O
+    assert fa.fa_fwd_bsparse_split(**{**f, "dtype": 0}) == 3
+    assert fa.fa_fwd_bsparse_split(**{**f, "N": 0}) == 0
+    bw = dict(q=A[0], k=A[1], v=A[2], o=A[3], dO=A[4], lse=A[5], dq=A[6], dk=A[7], dv=A[8], delta_ws=A[9],
+              B=1, Hq=2, Hkv=1, N=600, d=64, causal=1, col_idx=A[10], row_idx=A[11], nnz=5, row_chunks=A[12],
+              n_row_chunks=3, row_merges=A[13], n_row_merges=0, n_row_slots=0, col_chunks=A[14], n_col_chunks=4,
+              col_merges=A[15], n_col_merges=1, n_col_slots=2, part_ws=A[0] + 0x100000, softmax_scale=0.1,
+              dtype=1, stream=None)
+    assert fa.fa_bwd_bsparse_split(**{**bw, "col_chunks": None}) == 1
+    assert fa.fa_bwd_bsparse_split(**{**bw, "row_idx": None}) == 1
+    assert fa.fa_bwd_bsparse_split(**{**bw, "n_col_slots": 6}) == 2
+    assert fa.fa_bwd_bsparse_split(**{**bw, "part_ws": None}) == 1
+    assert fa.fa_bwd_bsparse_split(**{**bw, "part_ws": A[7]}) == 6            # partials over dK
+    assert fa.fa_bwd_bsparse_split(**{**bw, "delta_ws": None}) == 1
+    assert fa.fa_bwd_bsparse_split(**{**bw, "B": 0}) == 0
+    assert fa.fa_fwd_bsparse_split_workspace_bytes(1, 32, 128, 5) == 5 * 32 * 256 * 129 * 4
+    assert fa.fa_bwd_bsparse_split_workspace_bytes(1, 32, 8, 128, 5, 3) == (5 * 32 + 2 * 3 * 8) * 256 * 128 * 4
+    assert fa.fa_fwd_bsparse_split_workspace_bytes(1, 32, 96, 5) == 0
+
+
+def test_bsparse_split_plan():
+    """Work items of a skewed mask: every row's entries covered once, in order, by items of at most `split`
+    entries; split rows get consecutive slots and one merge entry; items listed longest first."""
+    import numpy as np
+    from exact_io_aware_50_amd import fa
+    from exact_io_aware_50_amd import inputs as I
+    m = I.block_pattern(64, band=1, n_global=1, n_random=2, seed=8)
+    L = fa.BlockSparseLayout(m)
+    assert L.split == -(-3 * L.nnz // 128)
+    for ptr, chunks, merges, slots, n in ((L.row_ptr, L.row_chunks, L.row_merges, L.n_row_slots, L.n_row_chunks),
+                                          (L.col_ptr, L.col_chunks, L.col_merges, L.n_col_slots, L.n_col_chunks)):
+        ptr, ch, mg = ptr.numpy(), chunks.numpy()[:n], merges.numpy()
+        lens = ch[:, 2] - ch[:, 1]
+        assert np.all(np.diff(lens) <= 0) and np.all(lens <= L.split)
+        seen_slots = []
+        for r in range(64):
+            mine = ch[ch[:, 0] == r]
+            mine = mine[np.argsort(mine[:, 1])]
+            assert mine[0, 1] == ptr[r] and mine[-1, 2] == ptr[r + 1]
+            assert np.all(mine[1:, 1] == mine[:-1, 2])
+            if len(mine) == 1:
+                assert mine[0, 3] == -1
+            else:
+                s = mine[:, 3]
+                assert np.all(np.diff(s) == 1)
+                assert [r, s[0], len(s), 0] in mg.tolist()
+                seen_slots += s.tolist()
+        assert sorted(seen_slots) == list(range(slots))
+    assert L.n_row_slots > 0 and L.n_col_slots > 0                          # the global row and column are split
+    U = fa.BlockSparseLayout(I.block_pattern(64, band=1, n_global=0, n_random=2, seed=8))
+    assert U.n_row_slots == 0 and U.n_col_slots == 0                        # an even mask is not
 
 
 def test_dropout_validation():
