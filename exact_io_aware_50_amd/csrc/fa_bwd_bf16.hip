@@ -918,21 +918,22 @@ static hipError_t launch_dq(const void* q, const void* k, const void* v, const v
 // backward): merge m = merges[4m .. 4m+2] = (block r, first slot s0, slot
 // count ns); rows r * 256 .. of each of the nh heads (the query heads for dQ,
 // the K/V heads for dK and dV) get sum_s part[s0 + s][head][row].  One
-// workgroup per (merge, head); a thread per 8 columns of a row.
+// workgroup per (merge, head, run of 256 / (D/8) rows); a thread per 8
+// columns of a row.
 template <int D>
 __global__ __launch_bounds__(256) void bsp_merge_sum_kernel(const int* __restrict__ merges, int nmerge,
                                                             const float* __restrict__ part, int nslots,
                                                             uint16_t* __restrict__ out, int nh, int N) {
-    constexpr int BR = 256, CPR = D / 8;
-    const int mi = blockIdx.x % nmerge, hd = blockIdx.x / nmerge;
+    constexpr int BR = 256, CPR = D / 8, RB = 256 / CPR;
+    const int mi = blockIdx.x % nmerge, hd = (blockIdx.x / nmerge) % nh, rb = blockIdx.x / nmerge / nh;
     const int nb = (N + BR - 1) / BR;
     const int r = min(max(merges[4 * mi], 0), nb - 1);
     const int s0 = min(max(merges[4 * mi + 1], 0), nslots);
     const int ns = min(max(merges[4 * mi + 2], 0), nslots - s0);
-    for (int idx = threadIdx.x; idx < BR * CPR; idx += blockDim.x) {
-        const int row = idx / CPR, c8 = (idx % CPR) * 8;
+    {
+        const int row = rb * RB + threadIdx.x / CPR, c8 = (threadIdx.x % CPR) * 8;
         const int i = r * BR + row;
-        if (i >= N) continue;
+        if (i >= N) return;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < ns; ++s) {
             const float* p = part + (((int64_t)(s0 + s) * nh + hd) * BR + row) * D + c8;
@@ -953,11 +954,12 @@ __global__ __launch_bounds__(256) void bsp_merge_sum_kernel(const int* __restric
 static hipError_t launch_merge_sum(int d, const int* merges, int nmerge, const float* part, int nslots, void* out,
                                    int nh, int N, hipStream_t st) {
     if (nmerge <= 0) return hipSuccess;
+    // 256 rows per block, 256 / (d/8) rows per workgroup
     if (d == 64)
-        hipLaunchKernelGGL(bsp_merge_sum_kernel<64>, dim3((unsigned)(nmerge * nh)), dim3(256), 0, st, merges, nmerge,
-                           part, nslots, (uint16_t*)out, nh, N);
+        hipLaunchKernelGGL(bsp_merge_sum_kernel<64>, dim3((unsigned)(nmerge * nh * 8)), dim3(256), 0, st, merges,
+                           nmerge, part, nslots, (uint16_t*)out, nh, N);
     else
-        hipLaunchKernelGGL(bsp_merge_sum_kernel<128>, dim3((unsigned)(nmerge * nh)), dim3(256), 0, st, merges,
+        hipLaunchKernelGGL(bsp_merge_sum_kernel<128>, dim3((unsigned)(nmerge * nh * 16)), dim3(256), 0, st, merges,
                            nmerge, part, nslots, (uint16_t*)out, nh, N);
     return hipGetLastError();
 }

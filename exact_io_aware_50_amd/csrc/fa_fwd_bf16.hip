@@ -444,24 +444,25 @@ static hipError_t launch(const void* q, const void* k, const void* v, void* o, f
 // L_s the base-2 log-sum-exp and O_s the output of slot s over its keys:
 // L = log2 sum_s 2^L_s, O = sum_s 2^(L_s - L) O_s, LSE = L ln 2 (the online
 // softmax's rescale, applied once per slot).  A row no slot saw: O = 0,
-// LSE = -inf.  One workgroup per (merge, batch x head); a thread per 8
-// columns of a row.
+// LSE = -inf.  One workgroup per (merge, batch x head, run of 256 / (D/8)
+// rows); a thread per 8 columns of a row.
 template <int D>
 __global__ __launch_bounds__(256) void bsp_merge_fwd_kernel(const int* __restrict__ merges, int nmerge,
                                                             const float* __restrict__ part, int nslots,
                                                             uint16_t* __restrict__ O, float* __restrict__ LSE, int BH,
                                                             int N) {
-    constexpr int BM = FwdBf16Cfg<D>::BM, CPR = D / 8;
-    const int mi = blockIdx.x % nmerge, bh = blockIdx.x / nmerge;
+    constexpr int BM = FwdBf16Cfg<D>::BM, CPR = D / 8, RB = 256 / CPR, NRB = BM / RB;
+    const int mi = blockIdx.x % nmerge, bh = (blockIdx.x / nmerge) % BH, rb = blockIdx.x / nmerge / BH;
     const int nmb = (N + BM - 1) / BM;
     const int r = min(max(merges[4 * mi], 0), nmb - 1);
     const int s0 = min(max(merges[4 * mi + 1], 0), nslots);
     const int ns = min(max(merges[4 * mi + 2], 0), nslots - s0);
     const float* Lp = part + (int64_t)nslots * BH * BM * D;
-    for (int idx = threadIdx.x; idx < BM * CPR; idx += blockDim.x) {
-        const int row = idx / CPR, c8 = (idx % CPR) * 8;
+    static_assert(NRB * RB == BM, "rows split evenly over the workgroups");
+    {
+        const int row = rb * RB + threadIdx.x / CPR, c8 = (threadIdx.x % CPR) * 8;
         const int i = r * BM + row;
-        if (i >= N) continue;
+        if (i >= N) return;
         float lmax = -INFINITY;
         for (int s = 0; s < ns; ++s) lmax = fmaxf(lmax, Lp[((int64_t)(s0 + s) * BH + bh) * BM + row]);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
@@ -492,8 +493,9 @@ template <int D>
 static hipError_t launch_merge_fwd(const int* merges, int nmerge, const float* part, int nslots, void* o, float* lse,
                                    int BH, int N, hipStream_t st) {
     if (nmerge <= 0) return hipSuccess;
-    hipLaunchKernelGGL(bsp_merge_fwd_kernel<D>, dim3((unsigned)(nmerge * BH)), dim3(256), 0, st, merges, nmerge,
-                       part, nslots, (uint16_t*)o, lse, BH, N);
+    constexpr int NRB = FwdBf16Cfg<D>::BM / (256 / (D / 8));
+    hipLaunchKernelGGL(bsp_merge_fwd_kernel<D>, dim3((unsigned)(nmerge * BH * NRB)), dim3(256), 0, st, merges,
+                       nmerge, part, nslots, (uint16_t*)o, lse, BH, N);
     return hipGetLastError();
 }
 
