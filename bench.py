@@ -39,25 +39,64 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def probe_clocks(torch, fa, calls, per, check, dev, span=0.02):
-    """Engine clock (GHz) under each kernel: fa_engine_clock_probe (eight one-wave
-    workgroups, one per XCD, counting shader-clock ticks against the 100 MHz
-    real-time counter for `span` seconds) runs on a second stream while the
-    kernel runs back to back on the current one.  Outside the timed region."""
-    side = torch.cuda.Stream(device=dev)
-    buf = torch.zeros(16, dtype=torch.int64, device=dev)
+def sclk_path(torch):
+    """The sysfs file of the GPU's engine-clock levels (the current one starred), or None."""
+    import glob
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if len(paths) <= 1:
+        return paths[0] if paths else None
+    p = torch.cuda.get_device_properties(0)
+    want = f"{getattr(p, 'pci_bus_id', -1):02x}:{getattr(p, 'pci_device_id', -1):02x}."
+    for path in paths:
+        try:
+            slot = [l for l in open(os.path.join(os.path.dirname(path), "uevent")) if l.startswith("PCI_SLOT_NAME=")]
+            if slot and want in slot[0]:
+                return path
+        except OSError:
+            pass
+    return None
+
+
+def read_sclk(path):
+    """Current engine clock in MHz from pp_dpm_sclk (the starred level), or None."""
+    try:
+        for line in open(path):
+            if "*" in line:
+                return float(line.split(":")[1].lower().split("mhz")[0])
+    except (OSError, ValueError, IndexError):
+        pass
+    return None
+
+
+def measure_clocks(torch, calls, per, check, seconds=0.4, skip=0.1):
+    """Engine clock (GHz) under each kernel, outside the timed region: the kernel runs back to back for `seconds`
+    while a host thread reads the current engine clock from sysfs (pp_dpm_sclk) about every 2 ms; the mean of the
+    readings after the first `skip` seconds (the clock settling)."""
+    import threading
+    path = sclk_path(torch)
+    if path is None or read_sclk(path) is None:
+        log("engine clock unavailable (no readable pp_dpm_sclk)")
+        return {}
     clocks = {}
     for name, fn in calls:
-        reps = int(1.5 * span * 1e3 / max(per[name], 1e-3)) + 5
+        samples, run = [], [True]
+
+        def poll():
+            t0 = time.perf_counter()
+            while run[0]:
+                c = read_sclk(path)
+                if c is not None and time.perf_counter() - t0 > skip:
+                    samples.append(c)
+                time.sleep(0.002)
         torch.cuda.synchronize()
-        check(fa.fa_engine_clock_probe(buf.data_ptr(), 8, span, side.cuda_stream), "fa_engine_clock_probe")
-        time.sleep(0.001)                       # the probe's waves are resident before the kernels
-        for _ in range(reps):
+        th = threading.Thread(target=poll, daemon=True)
+        th.start()
+        for _ in range(int(seconds * 1e3 / max(per[name], 1e-3)) + 1):
             check(fn(), name)
         torch.cuda.synchronize()
-        t = buf.cpu().tolist()
-        ghz = [0.1 * t[2 * w] / t[2 * w + 1] for w in range(8) if t[2 * w + 1] > 0]
-        clocks[name] = round(sum(ghz) / len(ghz), 3) if ghz else None
+        run[0] = False
+        th.join()
+        clocks[name] = round(sum(samples) / len(samples) / 1e3, 3) if samples else None
     return clocks
 
 
@@ -532,9 +571,9 @@ def main():
             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
             "traffic": stored_traffic(dom, args.workload)}
 
-    # engine clock under each kernel (outside the timed region, probe_clocks);
+    # engine clock under each kernel (outside the timed region, measure_clocks);
     # the peak scales with it, 2516.6 TFLOP/s being quoted at 2.4 GHz
-    clocks = {} if args.no_clock else probe_clocks(torch, fa, calls, per, check, dev)
+    clocks = {} if args.no_clock else measure_clocks(torch, calls, per, check)
     if clocks:
         log("engine clock under load: " + ", ".join(f"{n} {c} GHz" for n, c in clocks.items()))
     for n, c in clocks.items():
@@ -565,9 +604,9 @@ def main():
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
         "kernels": kern,
-        "clock": {"source": "fa_engine_clock_probe: shader-clock ticks over 20 ms of the 100 MHz real-time "
-                            "counter, one wave per XCD, beside each kernel run back to back outside the timed "
-                            "region; peak taken as 2516.6 x clock / 2.4 GHz",
+        "clock": {"source": "sysfs pp_dpm_sclk (current engine clock) read about every 2 ms while each kernel "
+                            "runs back to back for 0.4 s outside the timed region, mean after the first 0.1 s; "
+                            "peak taken as 2516.6 x clock / 2.4 GHz",
                   "ghz": clocks or None},
         "fwd_frac_at_clock": (round(fwd_tf / (PEAK_BF16_TFLOPS * clocks["fwd"] / 2.4), 4)
                               if clocks.get("fwd") else None),

@@ -516,13 +516,6 @@ fa_status_t fa_quantize_fp8(const void* x_bf16, size_t n, void* x_e4m3, float* d
     return launch_status(fa::launch_quantize_fp8(x_bf16, n, x_e4m3, descale, stream));
 }
 
-fa_status_t fa_engine_clock_probe(unsigned long long* out, int n_wg, double seconds, hipStream_t stream) {
-    if (!out) return FA_ERR_NULL;
-    if (n_wg < 1 || n_wg > 64 || !(seconds > 0.0 && seconds <= 10.0)) return FA_ERR_SHAPE;
-    if (!aligned(out, 8)) return FA_ERR_ALIGN;
-    return launch_status(fa::launch_clock_probe(out, n_wg, seconds, stream));
-}
-
 const char* fa_status_string(fa_status_t s) {
     switch (s) {
         case FA_OK: return "ok";

@@ -148,10 +148,6 @@ hipError_t launch_bwd_fp8(int causal, const void* q, const void* k, const void* 
 
 hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descale, hipStream_t st);
 
-// Engine-clock probe: n_wg one-wave workgroups, each writing (shader-clock
-// ticks, 100 MHz real-time ticks) over `seconds` of real time.
-hipError_t launch_clock_probe(unsigned long long* out, int n_wg, double seconds, hipStream_t st);
-
 // Decode split over the keys: nrb blocks of 32 packed query rows per K/V head,
 // nsplit chunks of `chunk` keys (a multiple of 32).
 struct DecodePlan {

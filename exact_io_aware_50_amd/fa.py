@@ -77,8 +77,6 @@ _lib.fa_decode_paged.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p] + [_i] * 9 + [_
 _lib.fa_decode_paged.restype = _i
 _lib.fa_decode_paged_workspace_bytes.argtypes = [_i] * 7
 _lib.fa_decode_paged_workspace_bytes.restype = ctypes.c_size_t
-_lib.fa_engine_clock_probe.argtypes = [_p, _i, _d, _p]
-_lib.fa_engine_clock_probe.restype = _i
 _lib.fa_status_string.argtypes = [_i]
 _lib.fa_status_string.restype = ctypes.c_char_p
 _lib.fa_abi_version.argtypes = []
@@ -90,7 +88,7 @@ EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_delta", "fa_bwd_dkdv", 
            "fa_fwd_bsparse_split", "fa_bwd_bsparse_split", "fa_fwd_bsparse_split_workspace_bytes",
            "fa_bwd_bsparse_split_workspace_bytes", "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd_fp8", "fa_decode",
            "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
-           "fa_engine_clock_probe", "fa_status_string", "fa_abi_version")
+           "fa_status_string", "fa_abi_version")
 
 
 class FAError(RuntimeError):
@@ -530,10 +528,6 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, causal: bool, scale
                            maxb, bs, nblk, d, causal, scale, _dtype_code(q), _stream_handle(stream)),
            "fa_decode_paged")
     return o, lse
-
-
-def fa_engine_clock_probe(out, n_wg, seconds, stream) -> int:
-    return _lib.fa_engine_clock_probe(out, int(n_wg), float(seconds), stream)
 
 
 def fa_bwd_fp8(q8, k8, v8, o, dO8, lse, descale, dq, dk, dv, delta_ws, B, Hq, Hkv, N, d, causal, softmax_scale,

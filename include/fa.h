@@ -454,21 +454,6 @@ fa_status_t fa_decode_paged(const void* q, const void* k_cache, const void* v_ca
 size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int Nq,
                                        int max_blocks, int block_size, int d);
 
-/*
- * Measurement helper (not part of attention): the engine clock under load.
- * The matrix-core peak is quoted at the 2.4 GHz engine clock; the chip lowers
- * the clock under heavy matrix work, so a fraction of peak is also judged
- * against the clock it held.  Launches n_wg one-wave workgroups on `stream`
- * (1 <= n_wg <= 64, workgroup w on XCD w % 8); each counts shader-clock ticks
- * against the 100 MHz real-time counter for `seconds` (0 < seconds <= 10) of
- * real time and writes out[2w] = shader ticks, out[2w + 1] = real-time ticks
- * (device memory, 2 n_wg unsigned 64-bit words, 8-byte aligned).  The clock
- * in GHz is 0.1 * out[2w] / out[2w + 1].  Run it on a second stream beside the
- * work to be measured.  FA_ERR_SHAPE for n_wg or seconds out of range,
- * FA_ERR_NULL, FA_ERR_ALIGN.
- */
-fa_status_t fa_engine_clock_probe(unsigned long long* out, int n_wg, double seconds, hipStream_t stream);
-
 /* Static text for a status code ("unknown status" for other values). */
 const char* fa_status_string(fa_status_t s);
 

@@ -34,22 +34,11 @@ def test_library_exports_every_declared_function():
                           "fa_fwd_bsparse_split_workspace_bytes", "fa_bwd_bsparse_split_workspace_bytes",
                           "fa_fwd_dropout", "fa_bwd_dropout", "fa_bwd_fp8",
                           "fa_decode_workspace_bytes", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
-                          "fa_engine_clock_probe", "fa_status_string", "fa_abi_version"}
+                          "fa_status_string", "fa_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(fa.EXPORTS) == set(names)
     assert fa.fa_abi_version() == 2
-
-
-def test_clock_probe_validation():
-    """Rejected on the host, before any launch."""
-    from exact_io_aware_50_amd import fa
-    assert fa.fa_engine_clock_probe(None, 8, 0.01, None) == fa.FA_ERR_NULL
-    assert fa.fa_engine_clock_probe(A[0], 0, 0.01, None) == fa.FA_ERR_SHAPE
-    assert fa.fa_engine_clock_probe(A[0], 65, 0.01, None) == fa.FA_ERR_SHAPE
-    assert fa.fa_engine_clock_probe(A[0], 8, 0.0, None) == fa.FA_ERR_SHAPE
-    assert fa.fa_engine_clock_probe(A[0], 8, 11.0, None) == fa.FA_ERR_SHAPE
-    assert fa.fa_engine_clock_probe(A[0] + 4, 8, 0.01, None) == fa.FA_ERR_ALIGN
 
 
 def test_status_strings():
