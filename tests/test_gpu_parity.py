@@ -112,6 +112,35 @@ def test_small_shapes_full(fa, dev, shape):
     check(dt, f64(o), f64(lse), O, L, [f64(x) for x in (dq, dk, dv)], [dQ, dK, dV], tag=str(shape))
 
 
+def _random_shapes(n, seed=20261203):
+    """n shapes drawn from a fixed seed: batch 1..3, query heads 1..8 in groups
+    of 1, 2, 4 or 8 per K/V head, sequence length 1..700 (tiles and query
+    blocks of every raggedness), both head sizes, causal or not, bf16 or fp32."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.integers(1, 3)) if G < 8 else 1
+        out.append((int(rng.integers(1, 4)), G * Hkv, Hkv, int(rng.integers(1, 701)), int(rng.choice([64, 128])),
+                    bool(rng.integers(0, 2)), "f32" if rng.random() < 0.25 else "bf16"))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(20),
+                         ids=lambda s: "B{}H{}x{}N{}d{}{}{}".format(*s[:5], "c" if s[5] else "", s[6]))
+def test_random_shapes_full(fa, dev, shape):
+    """Forward and backward on seeded random shapes, every element against the oracle."""
+    test_small_shapes_full(fa, dev, shape)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_many_items_full(fa, dev, causal):
+    """More work items than resident workgroups (B=4, Hq=32, Hkv=8, N=520, d=128:
+    384 query blocks and 96 key blocks of 256 rows, ragged last blocks), so the
+    persistent schedule runs several rounds per workgroup; every element checked."""
+    test_small_shapes_full(fa, dev, (4, 32, 8, 520, 128, causal, "bf16"))
+
+
 def test_tiny_f32_workload(fa, dev):
     w = I.WORKLOADS["tiny_f32"]
     q, k, v, do = (I.full_tensor(w, t) for t in range(4))
