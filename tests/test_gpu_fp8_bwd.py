@@ -5,7 +5,7 @@ quantiser (bit-exact with fa_quantize_fp8, pinned elsewhere); the GPU runs
 the FP8 forward and then the FP8 backward on those codes.  Two references:
 
 - the exact gradients at the unquantised bf16 inputs (the budget the recipe
-  is judged by): relative L2 <= 1e-1 on dQ, dK, dV.  A float64 simulation of
+  is measured against): relative L2 <= 1e-1 on dQ, dK, dV.  A float64 simulation of
   the recipe gives about 6.5% (dQ), 6% (dK) and 4.5% (dV), nearly all of it
   the E4M3 rounding of the inputs;
   (With a single key the exact dQ and dK are zero; there the bound is the
