@@ -106,6 +106,10 @@ __device__ __forceinline__ int fp8_vpos(int key) {
     return 32 * ((key >> 2) & 1) + 16 * ((key >> 5) & 1) + 4 * ((key >> 3) & 3) + (key & 3);
 }
 
+__device__ __forceinline__ f32x16 mma_fp8s(const u32x8& a, const u32x8& b, f32x16 c, int scale_b) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b),
+                                                           c, 0, 0, 0, 127, 0, scale_b);
+}
 __device__ __forceinline__ f32x16 mma_fp8(const u32x8& a, const u32x8& b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a),
                                                            __builtin_bit_cast(i32x8, b), c,
@@ -315,13 +319,18 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
 //    i, byte j is byte i % 8 of what source lane 2j + i/8 read).  Source lanes
 //    2j and 2j + 1 read 8 columns each of the same key, so every lane receives
 //    one column over eight keys, in the order its P bytes hold the keys.
-//  - P is scaled by 2^7 before its E4M3 rounding (exp2(c s - m + 7)), and the
-//    running max is moved when a row grows by more than a factor 2, so the
-//    scaled P stays at most 256, below the largest E4M3 value 448.
-//  - l is the sum of the rounded scaled P that the P V product weighs V with,
-//    formed on the matrix cores: one more fp8 product per tile, of a ones
-//    operand with P (every output row is the key sum of its query column),
-//    instead of 32 vector additions per lane.  The scale leaves with l.
+//  - P is scaled before its E4M3 rounding, per query row and tile, by the
+//    power of two 2^e that puts the tile's largest P of the row just below
+//    2^8.5 (below the largest E4M3 value 448, with all of the format's binades
+//    under it), and the P V and row-sum products divide it back out with the
+//    instruction's B-operand block scale 2^-e (free).  The scaled P never
+//    overflows however stale the running max is, so the max is moved only past
+//    2^8 growth, as in the bf16 kernel (float32 range), not past 2^1 growth:
+//    6-8% faster at the 4096-token causal workload.
+//  - l is the sum of the rounded P that the P V product weighs V with, formed
+//    on the matrix cores: one more fp8 product per tile, of a ones operand
+//    with P under the same block scale (every output row is the key sum of its
+//    query column), instead of 32 vector additions per lane.
 template <int D>
 struct FwdFp8Cfg {
     static constexpr int kWaves = 8;                  // two groups of four, one wave of each per SIMD
@@ -331,8 +340,8 @@ struct FwdFp8Cfg {
     static constexpr int kStages = 4;
     using KT = LdsTile<BN, D / 2, kWaves>;            // byte rows, in 16-bit units
     static constexpr int kStage = 2 * KT::kElems;     // 16-bit units per stage (K then V)
-    static constexpr float kTau = 1.0f;               // log2 slack before the max is moved
-    static constexpr float kPLog2 = 7.0f;             // log2 of the P scale
+    static constexpr float kTau = 8.0f;               // log2 slack before the max is moved
+    static constexpr float kPTop = 8.5f;              // log2 of the largest scaled P of a tile, at most
 };
 
 // G phase order: the K fragments (two reads) of the score products, then the
@@ -442,7 +451,7 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
         float m = kNegBig;
-        f32x16 lacc = zero16();                           // row sums of the rounded scaled P (all rows alike)
+        f32x16 lacc = zero16();                           // row sums of the rounded P (all rows alike)
         u32x8 ones;
 #pragma unroll
         for (int i = 0; i < 8; ++i) ones[i] = 0x38383838u;   // E4M3 1.0 in every byte
@@ -470,6 +479,7 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
         // keys 32(p/2) + 16(p%2) + 8(j/4) + 4hh + j%4, j = 0..7: key of byte
         // e = 8p + j of P.
         const int g16 = lane >> 4, s16 = lane & 15, jj = s16 >> 1, qq = s16 & 1;
+        int pscale = 127;                                 // E8M0 block scale of pf: 2^-e
         auto do_pv = [&](int t) __attribute__((always_inline)) {
             const char* Vb = (const char*)(stage(t) + KT::kElems);
 #pragma unroll
@@ -485,10 +495,10 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
                     a[2 * pq] = (uint32_t)w[0];
                     a[2 * pq + 1] = (uint32_t)w[1];
                 }
-                oacc[ct] = mma_fp8(a, pf, oacc[ct]);
+                oacc[ct] = mma_fp8s(a, pf, oacc[ct], pscale);
             }
         };
-        auto do_rowsum = [&]() __attribute__((always_inline)) { lacc = mma_fp8(ones, pf, lacc); };
+        auto do_rowsum = [&]() __attribute__((always_inline)) { lacc = mma_fp8s(ones, pf, lacc, pscale); };
         // The scaled fp8 products are not held in their phase by the ordering
         // hints alone: consuming their results at the end of the phase keeps
         // them (and their completion) before the barrier.  The matrix phase is
@@ -539,9 +549,13 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
 #pragma unroll
                 for (int ct = 0; ct < D / 32; ++ct) oacc[ct] *= alpha;
             }
-            // P * 2^7 = exp2(c2 s - m + 7), packed to E4M3: byte e of pf is
-            // register e % 16 of key block e / 16
-            const float base = Cfg::kPLog2 - m;
+            // P 2^e = exp2(c2 s - m + e), packed to E4M3 (byte e of pf is register
+            // e % 16 of key block e / 16), with e = floor(kPTop - (c2 x - m)) the
+            // exponent that puts the tile's largest P of this row just below
+            // 2^kPTop (x = -inf, a row with no key in the tile: e = 126, P = 0)
+            const int e = (int)fminf(fmaf(-x, c2, Cfg::kPTop + m), 126.0f);
+            pscale = 127 - e;
+            const float base = (float)e - m;
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
                 float p[4];
@@ -602,7 +616,7 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
             }
         }
 
-        // ---- epilogue: O = s_V O_acc / l, LSE = ln2 (m + log2(l / 2^7))
+        // ---- epilogue: O = s_V O_acc / l, LSE = ln2 (m + log2 l)
         // (G(t) adds the row sums of P_{t-1}, so G(ntiles) added the last tile's)
         const float ltot = lacc[0];
         if (qrow < N) {
@@ -619,7 +633,7 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
                     w[1] = pack_bf16x2(oacc[ct][4 * gq + 2] * f, oacc[ct][4 * gq + 3] * f);
                     *reinterpret_cast<u32x2*>(Orow + 32 * ct + 8 * gq) = w;
                 }
-            if (hh == 0) LSE[((int64_t)b * Hq + h) * N + qrow] = (m + log2f(ltot) - Cfg::kPLog2) * kLn2;
+            if (hh == 0) LSE[((int64_t)b * Hq + h) * N + qrow] = (m + log2f(ltot)) * kLn2;
         }
     }
 }
