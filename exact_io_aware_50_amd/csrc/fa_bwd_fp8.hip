@@ -598,7 +598,9 @@ __global__ __launch_bounds__(QFp8Cfg::kThreads, 2) void bwd_dq_fp8_kernel(
             for (int w = 0; w < 8; ++w) {
                 const f32x16& v = dpacc[w >> 2];
                 const int o = 4 * (w & 3);
-                s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, v[o], v[o + 1], psc[w >> 2], false);
+                s16x2 lo;
+                asm("" : "=v"(lo) : "v"(v[o]));               // any value: both halves are written
+                lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, v[o], v[o + 1], psc[w >> 2], false);
                 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, v[o + 2], v[o + 3], psc[w >> 2], true);
                 dsf[w] = __builtin_bit_cast(uint32_t, lo);
             }

@@ -590,7 +590,9 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         p[i] = fast_exp2(fmaf(sacc[2 * sb + (w >> 2)][4 * (w & 3) + i], c2, base));
-                    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                    int pk;
+                    asm("" : "=v"(pk) : "v"(p[0]));       // any value: both halves are written
+                    pk = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pk, false);
                     pk = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], pk, true);
                     pf[sb][w] = (uint32_t)pk;
                 }
