@@ -14,7 +14,12 @@ on (torch's current stream, which the binding passes to the C ABI); the
 dominant kernel's average duration gives the roofline figure.  The CPU leg
 times the float64 oracle on a bounded sample of the same workload's heads.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Every leg (the headline step and each leg beside it) first runs untimed and
+back to back for --settle-ms (200 ms), then its W warmup calls, then the K
+timed ones: a load that follows idle time runs 10-25% slow for its first
+~50 ms on this GPU, and the timed region is meant to see the steady state.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
 """
 from __future__ import annotations
 
@@ -37,6 +42,30 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def settle(torch, stream, fn, ms, batch=4):
+    """Run fn back to back, untimed, for at least ms milliseconds of wall time.
+
+    After the GPU has been idle for as little as 50 ms, the first ~50 ms of load run 10-25% slower
+    than steady state (the power manager's response to the load step, measured per call with HIP
+    events).  A leg's warmup calls alone (a few ms) end inside that transient; this puts every timed
+    region in the steady state a continuously running job sees.  One batch of calls always stays
+    queued, so the GPU never idles while the host checks the time."""
+    if ms <= 0:
+        return
+    t_end = time.perf_counter() + ms * 1e-3
+    prev = None
+    while True:
+        for _ in range(batch):
+            fn()
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        if prev is not None:
+            prev.synchronize()
+        prev = ev
+        if time.perf_counter() >= t_end:
+            break
 
 
 def sclk_path(torch):
@@ -189,6 +218,7 @@ def local_leg(torch, fa, I, dev, stream, args):
         if st != fa.FA_OK:
             raise fa.FAError(st, "fa_bwd_local")
 
+    settle(torch, stream, lambda: (fwd(), bwd()), args.settle_ms, batch=1)
     for _ in range(args.warmup):
         fwd()
         bwd()
@@ -275,6 +305,7 @@ def bsparse_leg(torch, fa, I, dev, stream, args, name=None):
         if st != fa.FA_OK:
             raise fa.FAError(st, "fa_bwd_bsparse")
 
+    settle(torch, stream, lambda: (fwd(), bwd()), args.settle_ms, batch=1)
     for _ in range(args.warmup):
         fwd()
         bwd()
@@ -326,6 +357,7 @@ def decode_leg(torch, fa, I, dev, stream, args):
         if st != fa.FA_OK:
             raise fa.FAError(st, "fa_decode")
 
+    settle(torch, stream, run, args.settle_ms, batch=16)
     for _ in range(args.warmup):
         run()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -365,6 +397,7 @@ def decode_leg(torch, fa, I, dev, stream, args):
         if st != fa.FA_OK:
             raise fa.FAError(st, "fa_decode_paged")
 
+    settle(torch, stream, run_paged, args.settle_ms, batch=16)
     for _ in range(args.warmup):
         run_paged()
     e0.record(stream)
@@ -427,7 +460,7 @@ def _cpu_baseline_run(w, seconds, threads, affinity):
                       f"{threads} BLAS threads ({affinity} cores in the affinity mask)"}
 
 
-def gemm_reference(torch, dev, stream, kern, n=8192, iters=15):
+def gemm_reference(torch, dev, stream, kern, settle_ms, n=8192, iters=15):
     """Context for the TFLOP/s figures: the vendor library's bf16 GEMM (torch.matmul) on one
     n x n x n product, with seeded N(0,1) operands and with all-zero operands.  The matrix cores
     draw less power on zeros and the chip then holds a higher clock, so the gap between the two
@@ -443,6 +476,7 @@ def gemm_reference(torch, dev, stream, kern, n=8192, iters=15):
             a = torch.zeros(n, n, device=dev, dtype=torch.bfloat16)
             b = torch.zeros(n, n, device=dev, dtype=torch.bfloat16)
         c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        settle(torch, stream, lambda: torch.matmul(a, b, out=c), settle_ms, batch=2)
         for _ in range(3):
             torch.matmul(a, b, out=c)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -465,6 +499,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="causal_bf16_n4096")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed back-to-back calls before each leg's warmup, in ms (the GPU's clock settles "
+                         "about 50 ms into a load that follows idle time)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
@@ -528,10 +565,11 @@ def main():
         if events is not None:
             events[len(calls)].record(stream)
 
+    settle(torch, stream, step, args.settle_ms, batch=1)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
+    log(f"warmup done ({args.settle_ms:.0f} ms settle, then {args.warmup} steps)")
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -591,6 +629,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -624,6 +663,7 @@ def main():
         run8 = lambda: check(fa.fa_fwd(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o8.data_ptr(), lse.data_ptr(),
                                        B, Hq, Hkv, N, d, w.causal, w.scale, fa.FA_DTYPE_FP8_E4M3, ds.data_ptr(),
                                        sh), "fa_fwd fp8")
+        settle(torch, stream, run8, args.settle_ms)
         for _ in range(args.warmup):
             run8()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -647,6 +687,7 @@ def main():
                                                 do8.data_ptr(), lse.data_ptr(), ds4.data_ptr(), g8[0].data_ptr(),
                                                 g8[1].data_ptr(), g8[2].data_ptr(), ws.data_ptr(), B, Hq, Hkv, N, d,
                                                 w.causal, w.scale, sh), "fa_bwd_fp8")
+            settle(torch, stream, run8b, args.settle_ms, batch=2)
             for _ in range(args.warmup):
                 run8b()
             e0.record(stream)
@@ -676,6 +717,7 @@ def main():
                                                 seed, w.scale, fa.FA_DTYPE_BF16, sh), "fa_bwd_dropout")
         times = []
         for fn in (rund, rundb):
+            settle(torch, stream, fn, args.settle_ms, batch=2)
             for _ in range(args.warmup):
                 fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -714,7 +756,7 @@ def main():
             result["decode"]["frac_hbm"]))
 
     if not args.no_gemm_reference and w.dtype == "bf16":
-        result["gemm_reference"] = gemm_reference(torch, dev, stream, kern)
+        result["gemm_reference"] = gemm_reference(torch, dev, stream, kern, args.settle_ms)
         log("vendor bf16 GEMM 8192^3: {} TFLOP/s on N(0,1) data, {} on zeros".format(
             result["gemm_reference"]["tflops_randn"], result["gemm_reference"]["tflops_zeros"]))
 
