@@ -444,6 +444,35 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
             issue_half(t, 0);
             issue_half(t, 1);
         };
+        // the same half tile for this wave's row groups and its partner's (the
+        // other wave on this SIMD, four waves away: four row groups further)
+        auto issue_half_pair = [&](int t, const int half) __attribute__((always_inline)) {
+            const uint32_t st = lds_addr(stage(t)) + half * KT::kBytes;
+            const uint8_t* src = (half ? Vh : Kh) + (int64_t)t * BN * D;
+            const int rows_valid = N - t * BN;
+            const int w0 = wave & 3;
+            if (rows_valid >= BN) {
+#pragma unroll
+                for (int i = 0; i < PW; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int w = w0 + 4 * j;
+                        dma16s(src, voff[i] + (uint32_t)((w - wave) * KT::RG * D), st + (i * NW + w) * KT::RGS);
+                    }
+            } else {
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+#pragma unroll
+                for (int i = 0; i < PW; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int w = w0 + 4 * j;
+                        const int row = (i * NW + w) * KT::RG + ln % KT::RG;
+                        const int grow = row < rows_valid ? row : rows_valid - 1;
+                        dma16s(src, (uint32_t)(grow * D + (ln / KT::RG) * 16), st + (i * NW + w) * KT::RGS);
+                    }
+            }
+        };
 #pragma unroll
         for (int t = 0; t < NS; ++t)
             if (t < ntiles) issue(t);
@@ -601,16 +630,29 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
         };
 
         // ---- phases: as in the bf16 forward (K rows of tile u >= NS at the
-        // start of slot 2u - 4, V rows at the start of slot 2u - 3)
+        // start of slot 2u - 4, V rows at the start of slot 2u - 3), except
+        // that the loads of a slot are issued by the group that starts its
+        // matrix phase there (the first group the K rows, the second the V
+        // rows), each wave for its partner too: here the vector phase is the
+        // longer one (3% faster at the causal 4096 workload than every wave
+        // issuing in both phases, 1.5% faster than the vector-phase group
+        // issuing).  Before the barrier ending odd slot 2tv - 1 the first group
+        // has its K_tv (K_tv+1 may be in flight), the second its V_tv-1 (V_tv
+        // and V_tv+1 may be).
         auto head = [&](int s2) __attribute__((always_inline)) {
             const int u = (s2 >> 1) + 2;
-            if (s2 >= 4 && u < ntiles) issue_half(u, s2 & 1);
+            if (s2 >= 4 && u < ntiles && grp == (s2 & 1)) issue_half_pair(u, s2 & 1);
         };
         auto tail_odd = [&](int s2) __attribute__((always_inline)) {
             const int tv = (s2 + 1) / 2;
             if (tv >= NS && tv < ntiles) {
-                if (tv + 1 < ntiles) wait_vm<3 * PW>();
-                else wait_vm<PW>();
+                if (grp == 0) {
+                    if (tv + 1 < ntiles) wait_vm<2 * PW>();
+                    else wait_vm<0>();
+                } else {
+                    if (tv + 1 < ntiles) wait_vm<4 * PW>();
+                    else wait_vm<2 * PW>();
+                }
             } else if (tv == ntiles && ntiles > NS) {
                 wait_vm<0>();                         // V of the last tile
             }
