@@ -795,8 +795,9 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
 
         // ---- phases (slot s ends with a barrier).  In loop round t both groups
         // refill the stage of tile t+2 (its previous tile, t-2, was last read in
-        // slot 2t-1) during their vector phase (slot 2t+1 for the first group,
-        // 2t for the second); before the barrier ending odd slot s, tile (s+1)/2
+        // slot 2t-1) at the start of their vector phase (slot 2t+1 for the first
+        // group, 2t for the second; at its end, or in the matrix phase, is 0.5-2%
+        // and 3-6% slower); before the barrier ending odd slot s, tile (s+1)/2
         // has landed (one later tile may still be in flight).
         auto refill = [&](int t) __attribute__((always_inline)) {
             if (t + 2 >= NS && t + 2 < ntiles) issue(t + 2);
@@ -819,8 +820,8 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
             for (int t = 1; t <= ntiles; ++t) {
                 gemm(t);
                 lds_barrier();
-                softmax(t);
                 refill(t);
+                softmax(t);
                 tail_odd(2 * t + 1);
             }
         } else {
@@ -829,8 +830,8 @@ __global__ __launch_bounds__(QBf16Cfg<D>::kThreads, 2) void bwd_dq_bf16_kernel(
             do_sdp(0);
             tail_odd(1);
             for (int t = 1; t <= ntiles; ++t) {
-                softmax(t - 1);
                 refill(t);
+                softmax(t - 1);
                 lds_barrier();
                 gemm(t);
                 tail_odd(2 * t + 1);
