@@ -608,6 +608,12 @@ __global__ __launch_bounds__(QFp8Cfg::kThreads, 2) void bwd_dq_fp8_kernel(
             asm volatile("" : : "v"(dsf));
         };
 
+        // In loop round t each group refills the stage of tile t+2 (its previous
+        // tile, t-2, was last read in slot 2t-1) at the start of its matrix
+        // phase (slot 2t for the first group, 2t+1 for the second): with fp8
+        // products that phase is the shorter one (2-3% faster for the whole
+        // backward than refilling in the vector phase, as the bf16 kernel
+        // does).  Before the barrier ending odd slot s, tile (s+1)/2 has landed.
         auto refill = [&](int t) __attribute__((always_inline)) {
             if (t + 2 >= NS && t + 2 < ntiles) issue(t + 2);
         };
@@ -626,10 +632,10 @@ __global__ __launch_bounds__(QFp8Cfg::kThreads, 2) void bwd_dq_fp8_kernel(
             softmax(0);
             tail_odd(1);
             for (int t = 1; t <= ntiles; ++t) {
+                refill(t);
                 gemm(t);
                 lds_barrier();
                 softmax(t);
-                refill(t);
                 tail_odd(2 * t + 1);
             }
         } else {
@@ -638,8 +644,8 @@ __global__ __launch_bounds__(QFp8Cfg::kThreads, 2) void bwd_dq_fp8_kernel(
             tail_odd(1);
             for (int t = 1; t <= ntiles; ++t) {
                 softmax(t - 1);
-                refill(t);
                 lds_barrier();
+                refill(t);
                 gemm(t);
                 tail_odd(2 * t + 1);
             }
