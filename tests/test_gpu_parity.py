@@ -244,7 +244,8 @@ def fp8_forward_check(fa, dev, q, k, v, causal, scale, rows_by_head, tag):
     assert e <= 6e-2, (tag, e)
 
 
-@pytest.mark.parametrize("N,d,causal", [(200, 64, True), (257, 128, False), (1024, 128, True)])
+@pytest.mark.parametrize("N,d,causal", [(200, 64, True), (257, 128, False), (1024, 128, True), (1000, 128, False),
+                                           (777, 128, True)])
 def test_fp8_forward_small(fa, dev, N, d, causal):
     B, Hq, Hkv = 1, 4, 2
     q = I.random_tensor(7, (B, Hq, N, d), "bf16", tensor_id=0)
