@@ -428,7 +428,7 @@ __global__ __launch_bounds__(QFp8Cfg::kThreads, 2) void bwd_dq_fp8_kernel(
     float scale) {
     using Cfg = QFp8Cfg;
     using KT = Cfg::KT;
-    constexpr int D = Cfg::D, NW = Cfg::kWaves, BM = Cfg::BM, BNK = Cfg::BNK, NS = Cfg::kStages, KB = BNK / 32;
+    constexpr int D = Cfg::D, BM = Cfg::BM, BNK = Cfg::BNK, NS = Cfg::kStages, KB = BNK / 32;
     constexpr int kStage = Cfg::kStage, kLoads = Cfg::kLoads;
     static_assert(KT::kPerWave == 1, "one row group per wave per tile");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * kStage];

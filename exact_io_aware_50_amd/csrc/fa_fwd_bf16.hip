@@ -101,7 +101,7 @@ __global__ __launch_bounds__(FwdBf16Cfg<D>::kThreads, 2) void fwd_bf16_kernel(
     using Cfg = FwdBf16Cfg<D>;
     using KT = typename Cfg::KT;
     constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::kStages, KB = BN / 32;
-    constexpr int kStage = Cfg::kStage, kLoads = Cfg::kLoads;
+    constexpr int kStage = Cfg::kStage;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * kStage];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: phase branches stay scalar
