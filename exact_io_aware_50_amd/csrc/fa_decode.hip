@@ -167,13 +167,23 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     uint16_t* ring = smem + wave * Cfg::kStages * kStage;
     const uint16_t* Kg = K + ((int64_t)b * Hkv + g) * Nk * D;
     const uint16_t* Vg = V + ((int64_t)b * Hkv + g) * Nk * D;
+    // (paged) the unit's block ids, one per lane: table entries kbeg / bs .. + 63,
+    // read once before the ring starts.  Read per tile inside the loop, the
+    // entry is a vector load whose wait also drains the ring's tile loads.
+    int tab = 0, tab0 = 0;
+    if constexpr (PAGED) {
+        tab0 = kbeg / pg.bs;
+        if (tab0 + lane < pg.maxb) tab = pg.table[(int64_t)b * pg.maxb + tab0 + lane];
+    }
     // K and V rows of tile t into stage t % NS (rows past the chunk re-read its last row)
     auto issue = [&](int t) __attribute__((always_inline)) {
         const uint16_t* st = ring + (t % NS) * kStage;
         const int k0 = kbeg + t * BN;
         const uint16_t *ks = Kg + (int64_t)k0 * D, *vs = Vg + (int64_t)k0 * D;
         if constexpr (PAGED) {
-            const int blk = min(max(pg.table[(int64_t)b * pg.maxb + k0 / pg.bs], 0), pg.nblk - 1);
+            const int jb = k0 / pg.bs - tab0;           // uniform
+            const int raw = jb < 64 ? __builtin_amdgcn_readlane(tab, jb) : pg.table[(int64_t)b * pg.maxb + k0 / pg.bs];
+            const int blk = min(max(raw, 0), pg.nblk - 1);
             const int64_t off = (((int64_t)blk * Hkv + g) * pg.bs + k0 % pg.bs) * D;
             ks = K + off;
             vs = V + off;
