@@ -44,14 +44,13 @@ struct DecCfg {
     static constexpr float kTau = 8.0f;               // log2 slack before the running max is moved
 };
 
-// Paged cache: the pool [nblk][Hkv][bs][D], the block table [B][maxb], and the
-// chunk plan written on the device by decode_plan_kernel from the lengths:
-// seq[b] = (first chunk, chunk count, chunk size, length), unit[c] = (batch,
-// first key, end key) of chunk c < T, batch -1 for an unused chunk.
+// Paged cache: the pool [nblk][Hkv][bs][D], the block table [B][maxb] and the
+// lengths [B]; `seq` receives the chunk plan for the merge: seq[b] = (first
+// chunk, chunk count) of sequence b.
 struct PagedArgs {
     const int* table;
-    const int* seq;
-    const int* unit;
+    const int* lens;
+    int* seq;
     int maxb, bs, nblk, T;
 };
 
@@ -59,59 +58,66 @@ struct PagedArgs {
 // of n keys (clamped to [0, maxb * bs]) gets 1 + floor(n (T - B) / L) chunks
 // of equal size rounded up to 32 keys, L being the total length, so that
 // every chunk slot holds about the same number of keys whatever the lengths
-// (T >= 2B makes the counts add up to at most T).  One workgroup.
-__global__ __launch_bounds__(256) void decode_plan_kernel(const int* __restrict__ lens, int B, int maxb, int bs,
-                                                          int T, int* __restrict__ seq, int* __restrict__ unit) {
-    __shared__ long long red[256];
-    __shared__ int scan[256];
-    const int tid = threadIdx.x;
-    const int cap = maxb * bs;
-    long long sum = 0;
-    for (int b = tid; b < B; b += 256) sum += min(max(lens[b], 0), cap);
-    red[tid] = sum;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
-        __syncthreads();
+// (T >= 2B makes the counts add up to at most T); the chunks are numbered
+// sequence by sequence.  Every wave works this out for its own chunk slot `cid`
+// (the lengths read once per 64 sequences, a wave-wide sum and prefix sum of
+// the counts): sequence, first and end key, and length of the chunk, or
+// b = -1 for an unused slot.  With `write`, the wave also stores every
+// sequence's (first chunk, count) in pg.seq.
+__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    const long long L = red[0] > 0 ? red[0] : 1;
+    return x;
+}
+__device__ __forceinline__ int paged_plan(const PagedArgs& pg, int B, int cid, int lane, bool write, int& kbeg,
+                                          int& kend, int& nlen) {
+    const int cap = pg.maxb * pg.bs;
+    int64_t part = 0;
+    for (int b0 = 0; b0 < B; b0 += 64)
+        if (b0 + lane < B) part += min(max(pg.lens[b0 + lane], 0), cap);
+    int64_t L = wave_sum64(part);
+    if (L <= 0) L = 1;
+    int found = -1;
     int base = 0;                                     // chunks of the sequences before this pass
-    for (int b0 = 0; b0 < B; b0 += 256) {
-        const int b = b0 + tid;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int bb = b0 + lane;
         int n = 0, c = 0, cs = 0;
-        if (b < B) {
-            n = min(max(lens[b], 0), cap);
+        if (bb < B) {
+            n = min(max(pg.lens[bb], 0), cap);
             if (n > 0) {
-                c = 1 + (int)((long long)n * (T - B) / L);
+                c = 1 + (int)((int64_t)n * (pg.T - B) / L);
                 cs = ((n + c - 1) / c + 31) / 32 * 32;
                 c = (n + cs - 1) / cs;
             }
         }
-        // inclusive scan of the counts over this pass
-        scan[tid] = c;
-        __syncthreads();
-        for (int w = 1; w < 256; w <<= 1) {
-            const int x = tid >= w ? scan[tid - w] : 0;
-            __syncthreads();
-            scan[tid] += x;
-            __syncthreads();
+        const int incl = wave_incl_scan(c, lane);
+        const int off = base + incl - c;
+        if (write && bb < B) {
+            pg.seq[2 * bb] = off;
+            pg.seq[2 * bb + 1] = c;
         }
-        const int off = base + scan[tid] - c;
-        if (b < B) {
-            seq[4 * b] = off;
-            seq[4 * b + 1] = c;
-            seq[4 * b + 2] = cs;
-            seq[4 * b + 3] = n;
-            for (int j = 0; j < c; ++j) {
-                unit[3 * (off + j)] = b;
-                unit[3 * (off + j) + 1] = j * cs;
-                unit[3 * (off + j) + 2] = min(n, (j + 1) * cs);
-            }
+        const uint64_t hit = __ballot(c > 0 && cid >= off && cid < off + c);
+        if (found < 0 && hit) {
+            const int l = __ffsll((unsigned long long)hit) - 1;
+            found = b0 + l;
+            const int j = cid - __shfl(off, l);
+            const int csl = __shfl(cs, l);
+            nlen = __shfl(n, l);
+            kbeg = j * csl;
+            kend = min(nlen, (j + 1) * csl);
+            if (!write) break;
         }
-        base += scan[255];
-        __syncthreads();
+        base += __shfl(incl, 63);
     }
-    for (int cid = base + tid; cid < T; cid += 256) unit[3 * cid] = -1;
+    return found;
 }
 
 // PAGED: the cache is a pool of blocks [nblk][Hkv][bs][D] and sequence b's
@@ -137,12 +143,14 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     const int G = Hq / Hkv, R = G * Nq, nrb = (R + 31) / 32;
     const int64_t u = (int64_t)blockIdx.x * Cfg::kWaves + wave;    // this wave's unit
     int s, rb, g, b, cid = 0;
+    int pkbeg = 0, pkend = 0, pnb = 0;                // (paged) this chunk's keys and its sequence's length
     if constexpr (PAGED) {
         if (u >= (int64_t)pg.T * Hkv * nrb) return;                 // wave-uniform; no barriers below
         rb = (int)(u % nrb);
         g = (int)((u / nrb) % Hkv);
         cid = (int)(u / nrb / Hkv);
-        b = pg.unit[3 * cid];
+        const int lane0 = threadIdx.x & 63;
+        b = paged_plan(pg, B, cid, lane0, u == 0, pkbeg, pkend, pnb);
         if (b < 0) return;                                           // an unused chunk slot
         s = 0;
     } else {
@@ -158,10 +166,10 @@ __global__ __launch_bounds__(DecCfg<D>::kThreads) void decode_split_kernel(
     const int r = rb * 32 + l32;                      // this lane's packed query row
     const bool rv = r < R;
     const int hq = g * G + (rv ? r / Nq : 0), qi = rv ? r % Nq : 0;
-    const int Nb = PAGED ? pg.seq[4 * b + 3] : Nk;    // this sequence's keys
+    const int Nb = PAGED ? pnb : Nk;                  // this sequence's keys
     const int lim = CAUSAL ? Nb - Nq + qi : Nb - 1;   // last key the row sees
-    const int kbeg = PAGED ? pg.unit[3 * cid + 1] : s * chunk;
-    const int kend = PAGED ? pg.unit[3 * cid + 2] : min(Nb, kbeg + chunk);
+    const int kbeg = PAGED ? pkbeg : s * chunk;
+    const int kend = PAGED ? pkend : min(Nb, kbeg + chunk);
     const int nt = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
 
     uint16_t* ring = smem + wave * Cfg::kStages * kStage;
@@ -303,9 +311,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
     int cnt = nsplit;
     if (seq) {
         const int b = (int)(row / HqNq);
-        first = (int64_t)seq[4 * b] * HqNq + row % HqNq;
+        first = (int64_t)seq[2 * b] * HqNq + row % HqNq;
         stride = HqNq;
-        cnt = seq[4 * b + 1];
+        cnt = seq[2 * b + 1];
     }
     float L = -INFINITY;
     for (int s = lane; s < cnt; s += 64) L = fmaxf(L, Wl[first + s * stride]);
@@ -402,21 +410,18 @@ static hipError_t launch_paged(const void* q, const void* kc, const void* vc, co
     using Cfg = DecCfg<D>;
     const int T = paged_chunks(B, Hq, Hkv, Nq, D, device_cus());
     const int nrb = (Hq / Hkv * Nq + 31) / 32;
+    // (first chunk, count) per sequence, written by the split kernel for the merge
     int* seq = reinterpret_cast<int*>(ws);
-    int* unit = seq + 4 * (int64_t)B;
     const int64_t ints = ((4 * (int64_t)B + 3 * (int64_t)T) * 4 + 15) / 16 * 16;
     float* wo = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ints);
     float* wl = wo + (int64_t)T * Hq * Nq * D;
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(256), 0, st, lens, B, maxb, bs, T, seq, unit);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const PagedArgs pg{table, seq, unit, maxb, bs, nblk, T};
+    const PagedArgs pg{table, lens, seq, maxb, bs, nblk, T};
     const int64_t units = (int64_t)T * Hkv * nrb;
     const unsigned g1 = (unsigned)((units + Cfg::kWaves - 1) / Cfg::kWaves);
     hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, true>), dim3(g1), dim3(Cfg::kThreads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)kc, (const uint16_t*)vc, wo, wl, B, Hq, Hkv, Nq,
                        maxb * bs, 0, 0, scale * kLog2e, pg);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = (int64_t)B * Hq * Nq;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, wo, wl,

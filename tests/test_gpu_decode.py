@@ -129,7 +129,7 @@ PAGED = [
     (4, 8, 8, 1, [33, 0, 500, 2048], 64, 256, False),
     (2, 64, 8, 2, [3000, 1], 128, 128, True),
     (2, 4, 2, 5, [3, 70], 64, 32, True),            # causal rows before sequence 0's first key
-    # more sequences than the plan kernel's 256 threads: its scan runs in two passes
+    # more sequences than a wave has lanes: the chunk plan is worked out in five passes of 64
     (300, 2, 1, 1, [int(x) for x in np.random.Generator(np.random.PCG64(31)).integers(0, 200, 300)], 64, 32, False),
     # 128 K/V heads leave 8 chunk slots on a 256-CU device: chunks of 2528 keys span 79 blocks of 32, past the
     # 64 block ids a wave holds in registers (the rest are read from the table)
