@@ -14,6 +14,10 @@ on (torch's current stream, which the binding passes to the C ABI); the
 dominant kernel's average duration gives the roofline figure.  The CPU leg
 times the float64 oracle on a bounded sample of the same workload's heads.
 
+The same four calls are also recorded once into a HIP graph (torch's CUDAGraph)
+and replayed K times (`graph` in the JSON line: no launch gaps between the
+kernels); `value` stays the eager figure.
+
 Every leg (the headline step and each leg beside it) first runs untimed and
 back to back for --settle-ms (200 ms), then its W warmup calls, then the K
 timed ones: a load that follows idle time runs 10-25% slow for its first
@@ -42,6 +46,39 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_graph(torch, make_calls, check, steps, warmup, settle_ms):
+    """ms per step of the step's calls recorded once into a HIP graph (torch's CUDAGraph) and replayed.
+
+    make_calls(stream_handle) gives the (name, fn) calls launching on that stream.  They run once
+    eagerly on the capture stream first, so that nothing the launchers query and keep (CU count,
+    occupancy) is first asked for during the capture."""
+    cur = torch.cuda.current_stream()
+    gs = torch.cuda.Stream()
+    gcalls = make_calls(gs.cuda_stream)
+    gs.wait_stream(cur)
+    with torch.cuda.stream(gs):
+        for name, fn in gcalls:
+            check(fn(), name)
+    cur.wait_stream(gs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        for name, fn in gcalls:
+            check(fn(), name)
+    torch.cuda.synchronize()
+    settle(torch, cur, g.replay, settle_ms, batch=1)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del g
+    return ms
 
 
 def settle(torch, stream, fn, ms, batch=4):
@@ -507,6 +544,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-dropout", action="store_true", help="skip the attention-dropout leg")
     ap.add_argument("--no-clock", action="store_true", help="skip the engine-clock sampling")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing of the step")
     ap.add_argument("--no-gemm-reference", action="store_true",
                     help="skip the vendor bf16 GEMM timed for context (practical MFMA rate on this data)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode (KV cache) leg")
@@ -545,17 +583,20 @@ def main():
         if st != fa.FA_OK:
             raise fa.FAError(st, name)
 
-    calls = [
-        ("fwd", lambda: fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq,
-                                  Hkv, N, d, w.causal, w.scale, code, None, sh)),
-        ("bwd_delta", lambda: fa.fa_bwd_delta(o.data_ptr(), do.data_ptr(), lse.data_ptr(), ws.data_ptr(), B, Hq,
-                                              N, d, code, sh)),
-        ("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), ws.data_ptr(),
-                                            dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d, w.causal, w.scale,
-                                            code, sh)),
-        ("bwd_dq", lambda: fa.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), ws.data_ptr(),
-                                        dq.data_ptr(), B, Hq, Hkv, N, d, w.causal, w.scale, code, sh)),
-    ]
+    def make_calls(sh):
+        return [
+            ("fwd", lambda: fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq,
+                                      Hkv, N, d, w.causal, w.scale, code, None, sh)),
+            ("bwd_delta", lambda: fa.fa_bwd_delta(o.data_ptr(), do.data_ptr(), lse.data_ptr(), ws.data_ptr(), B, Hq,
+                                                  N, d, code, sh)),
+            ("bwd_dkdv", lambda: fa.fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                                                ws.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d,
+                                                w.causal, w.scale, code, sh)),
+            ("bwd_dq", lambda: fa.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), ws.data_ptr(),
+                                            dq.data_ptr(), B, Hq, Hkv, N, d, w.causal, w.scale, code, sh)),
+        ]
+
+    calls = make_calls(sh)
 
     def step(events=None):
         for i, (name, fn) in enumerate(calls):
@@ -609,6 +650,15 @@ def main():
             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
             "traffic": stored_traffic(dom, args.workload)}
 
+    # the same step recorded once into a HIP graph and replayed (launch gaps
+    # between the four kernels removed); reported beside the eager figure
+    graph = None
+    if not args.no_graph:
+        g_ms = time_graph(torch, make_calls, check, args.steps, args.warmup, args.settle_ms)
+        graph = {"ms_per_step": round(g_ms, 4),
+                 "value": round((fwd_fl + bwd_fl) / (g_ms * 1e-3) / 1e12, 2)}
+        log(f"graph replay: {g_ms:.4f} ms/step, {graph['value']} TFLOP/s")
+
     # engine clock under each kernel (outside the timed region, measure_clocks);
     # the peak scales with it, 2516.6 TFLOP/s being quoted at 2.4 GHz
     clocks = {} if args.no_clock else measure_clocks(torch, calls, per, check)
@@ -643,6 +693,7 @@ def main():
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
         "kernels": kern,
+        "graph": graph,
         "clock": {"source": "sysfs pp_dpm_sclk (current engine clock) read about every 2 ms while each kernel "
                             "runs back to back for 0.4 s outside the timed region, mean after the first 0.1 s; "
                             "peak taken as 2516.6 x clock / 2.4 GHz",

@@ -37,6 +37,11 @@
  *    failed launch returns FA_ERR_LAUNCH.  Device faults surface at the
  *    caller's next synchronisation of `stream`.
  *  - No atomics in attention: results are bitwise reproducible run to run.
+ *  - Graph capture: a call enqueues kernel launches only (no memset, copy,
+ *    allocation or wait), so it can be recorded into a HIP graph by stream
+ *    capture and replayed; a replay reads the buffers' contents at replay
+ *    time.  The first call on a device should run outside a capture, so that
+ *    the per-device cache above is filled by then.
  *  - Calls on different streams are independent and thread-safe.
  */
 #ifndef FA_H
