@@ -431,6 +431,8 @@ __device__ __forceinline__ void pipe_wait(int j, int total) {
 //  - a transposed read touches, per 16 lanes, 4 rows of 2 neighbouring chunks:
 //    128 contiguous bytes;
 //  - every fragment address is one per-lane base plus a compile-time offset.
+// RG is 4 rows of 256 bytes (bf16, d = 128), 8 rows of 128 bytes (bf16 d = 64,
+// or E4M3 codes at d = 128) or 16 rows of 64 bytes (E4M3 codes at d = 64).
 template <int ROWS, int COLS, int NW>
 struct LdsTile {
     static constexpr int CPR = COLS / 8;                 // 16-byte chunks per row
@@ -440,7 +442,7 @@ struct LdsTile {
     static constexpr int kBytes = kGroups * RGS;
     static constexpr int kElems = kBytes / 2;
     static constexpr int kPerWave = kGroups / NW;
-    static_assert(CPR == 8 || CPR == 16, "64 or 128 columns");
+    static_assert(CPR == 4 || CPR == 8 || CPR == 16, "32, 64 or 128 columns");
     static_assert(kGroups % NW == 0, "the waves cover the tile in whole groups");
 
     // Direct global -> LDS copy of rows [0, ROWS) of `src` (row stride COLS).

@@ -94,18 +94,11 @@ hipError_t launch_quantize_fp8(const void* x, size_t n, void* out, float* descal
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------ fp8 forward
+// ------------------------------------------------------------ fp8 products
 //
 // Operands are 32 bytes per lane: lane l supplies row (A) or column (B) l % 32
-// and 32 contraction slots.  S^T = K Q^T uses d-slots 64*s + 32*hh + e.  For
-// O^T += V^T P^T the B operand is this lane's P: byte e is accumulator
-// register e % 16 of key block e / 16, i.e. key 32*(e/16) + row(e%16, hh).  The
-// transposed V tile stores key kappa at the position this lane reads it from:
-//   pos(kappa) = 32*hh + 16*kb + 4*a + b  for kappa = 32*kb + 8*a + 4*hh + b.
-__device__ __forceinline__ int fp8_vpos(int key) {
-    return 32 * ((key >> 2) & 1) + 16 * ((key >> 5) & 1) + 4 * ((key >> 3) & 3) + (key & 3);
-}
-
+// and 32 contraction slots (half hh = l / 32 of the 64).  The block scales are
+// E8M0 exponents (127 = 2^0).
 __device__ __forceinline__ f32x16 mma_fp8s(const u32x8& a, const u32x8& b, f32x16 c, int scale_b) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b),
                                                            c, 0, 0, 0, 127, 0, scale_b);
@@ -118,195 +111,7 @@ __device__ __forceinline__ f32x16 mma_fp8(const u32x8& a, const u32x8& b, f32x16
                                                            0, 127);     // B block scale 2^0
 }
 
-template <int D>
-struct Fp8Cfg {
-    static constexpr int kThreads = 256;
-    static constexpr int BM = 128;
-    static constexpr int BN = 64;
-    static constexpr int KS = D + 16;                      // bytes per K row in LDS
-    static constexpr int VS = BN + 16;                     // bytes per V^T row in LDS
-    static constexpr int kKBytes = BN * KS;
-    static constexpr int kVBytes = D * VS;
-    static constexpr int kStage = kKBytes + kVBytes;
-    static constexpr int kKChunks = BN * D / 16;           // 16-byte chunks of a K tile
-    static constexpr int kKPer = kKChunks / kThreads;
-    static constexpr int kVTasks = (BN / 4) * (D / 16);    // 4 keys x 16 columns per task
-    static_assert(kKChunks % kThreads == 0, "K tile chunks cover the threads evenly");
-    static_assert(kVTasks <= kThreads, "one V task per thread at most");
-};
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
-                                                      const uint8_t* __restrict__ V, uint16_t* __restrict__ O,
-                                                      float* __restrict__ LSE, const float* __restrict__ descale,
-                                                      int Hq, int Hkv, int N, float scale) {
-    using Cfg = Fp8Cfg<D>;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, KS = Cfg::KS, VS = Cfg::VS;
-    __shared__ __attribute__((aligned(64))) uint8_t smem[2 * Cfg::kStage];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hh = lane >> 5;
-
-    const int nmb = (N + BM - 1) / BM;
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
-    const int mbi = lin % nmb, bh = lin / nmb;
-    const int h = bh % Hq, b = bh / Hq;
-    const int mb = CAUSAL ? nmb - 1 - mbi : mbi;
-    const int g = h / (Hq / Hkv);
-    const uint8_t* Qh = Q + ((int64_t)b * Hq + h) * N * D;
-    const uint8_t* Kh = K + ((int64_t)b * Hkv + g) * N * D;
-    const uint8_t* Vh = V + ((int64_t)b * Hkv + g) * N * D;
-
-    const float c2 = scale * kLog2e * descale[0] * descale[1];
-    const float sv = descale[2];
-
-    const int q0 = mb * BM;
-    const int qw = q0 + 32 * wave;
-    const int qrow = qw + l32;
-
-    u32x8 qf[D / 64];
-#pragma unroll
-    for (int s = 0; s < D / 64; ++s) {
-        u32x8 v = {};
-        if (qrow < N) v = *reinterpret_cast<const u32x8*>(Qh + (int64_t)qrow * D + 64 * s + 32 * hh);
-        qf[s] = v;
-    }
-
-    const int kend = CAUSAL ? min(N, q0 + BM) : N;
-    const int ntiles = (kend + BN - 1) / BN;
-
-    f32x16 oacc[D / 32];
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] = zero16();
-    float m = kNegBig, lsum = 0.f;
-
-    u32x4 kreg[Cfg::kKPer];
-    u32x4 vreg[4];
-    auto fetch = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < Cfg::kKPer; ++i) {
-            const int c = tid + i * Cfg::kThreads;
-            const int row = c / (D / 16), seg = c % (D / 16);
-            u32x4 v = {};
-            if (k0 + row < N) v = *reinterpret_cast<const u32x4*>(Kh + (int64_t)(k0 + row) * D + 16 * seg);
-            kreg[i] = v;
-        }
-        if (tid < Cfg::kVTasks) {
-            const int rg = tid % (BN / 4), seg = tid / (BN / 4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                u32x4 v = {};
-                const int row = k0 + 4 * rg + j;
-                if (row < N) v = *reinterpret_cast<const u32x4*>(Vh + (int64_t)row * D + 16 * seg);
-                vreg[j] = v;
-            }
-        }
-    };
-    auto put = [&](uint8_t* st) {
-#pragma unroll
-        for (int i = 0; i < Cfg::kKPer; ++i) {
-            const int c = tid + i * Cfg::kThreads;
-            const int row = c / (D / 16), seg = c % (D / 16);
-            *reinterpret_cast<u32x4*>(st + row * KS + 16 * seg) = kreg[i];
-        }
-        if (tid < Cfg::kVTasks) {
-            const int rg = tid % (BN / 4), seg = tid / (BN / 4);
-            uint8_t* vt = st + Cfg::kKBytes;
-            const int pos = fp8_vpos(4 * rg);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int w = e >> 2, sh = 8 * (e & 3);
-                const uint32_t b0 = (vreg[0][w] >> sh) & 0xffu, b1 = (vreg[1][w] >> sh) & 0xffu;
-                const uint32_t b2 = (vreg[2][w] >> sh) & 0xffu, b3 = (vreg[3][w] >> sh) & 0xffu;
-                *reinterpret_cast<uint32_t*>(vt + (16 * seg + e) * VS + pos) = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-            }
-        }
-    };
-
-    fetch(0);
-    put(smem);
-    __syncthreads();
-
-    for (int j = 0; j < ntiles; ++j) {
-        const int k0 = j * BN;
-        const bool more = j + 1 < ntiles;
-        if (more) fetch(k0 + BN);
-        const uint8_t* Ks = smem + (j & 1) * Cfg::kStage;
-        const uint8_t* Vt = Ks + Cfg::kKBytes;
-
-        if (!(CAUSAL && k0 > qw + 31)) {
-            f32x16 sacc[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                f32x16 acc = zero16();
-#pragma unroll
-                for (int s = 0; s < D / 64; ++s)
-                    acc = mma_fp8(*reinterpret_cast<const u32x8*>(Ks + (32 * kb + l32) * KS + 64 * s + 32 * hh),
-                                  qf[s], acc);
-                sacc[kb] = acc;
-            }
-            const bool need_mask = (CAUSAL && k0 + BN - 1 > qw) || (k0 + BN > N);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + acc_row(r, hh);
-                        if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r] = -INFINITY;
-                    }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = fmaxf(mx, other_half(mx));
-            const float mnew = fmaxf(m, mx * c2);
-            const float alpha = fast_exp2(m - mnew);
-            float rs = 0.f;
-            u32x8 pf;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    float p[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        p[i] = fast_exp2(fmaf(sacc[kb][4 * r4 + i], c2, -mnew));
-                        rs += p[i];
-                    }
-                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * 256.f, p[1] * 256.f, 0, false);
-                    w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * 256.f, p[3] * 256.f, w, true);
-                    pf[4 * kb + r4] = (uint32_t)w;
-                }
-            lsum = fmaf(lsum, alpha, rs);
-            m = mnew;
-#pragma unroll
-            for (int ct = 0; ct < D / 32; ++ct) {
-                oacc[ct] *= alpha;
-                oacc[ct] = mma_fp8(*reinterpret_cast<const u32x8*>(Vt + (32 * ct + l32) * VS + 32 * hh), pf, oacc[ct]);
-            }
-        }
-        if (more) put(smem + ((j + 1) & 1) * Cfg::kStage);
-        __syncthreads();
-    }
-
-    const float ltot = lsum + other_half(lsum);
-    if (qrow < N) {
-        const float f = sv / (256.0f * ltot);
-        uint16_t* Orow = O + (((int64_t)b * Hq + h) * N + qrow) * D;
-#pragma unroll
-        for (int ct = 0; ct < D / 32; ++ct)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq)
-                st4<BF16>(Orow + 32 * ct + 8 * gq + 4 * hh,
-                          BF16::pack4(oacc[ct][4 * gq] * f, oacc[ct][4 * gq + 1] * f,
-                                      oacc[ct][4 * gq + 2] * f, oacc[ct][4 * gq + 3] * f));
-        if (hh == 0) LSE[((int64_t)b * Hq + h) * N + qrow] = (m + log2f(ltot)) * kLn2;
-    }
-}
-
-// ------------------------------------------------------------ fp8 forward, d = 128
+// ------------------------------------------------------------ fp8 forward (d = 64 and 128)
 //
 // The schedule of the bf16 forward (two wave groups one phase apart, K and V
 // tiles loaded straight into a ring of four LDS stages in their row-major
@@ -314,6 +119,8 @@ __global__ __launch_bounds__(256) void fwd_fp8_kernel(const uint8_t* __restrict_
 // the bf16 kernel's: an E4M3 tile is half the bytes, and the per-phase costs
 // that do not grow with the tile -- the row max exchange, the scale exponent,
 // the barrier -- are paid half as often; 2.5-7% faster than 64-key tiles):
+//  - a 128-key tile of E4M3 codes is 16 row groups of 8 rows at d = 128 (two
+//    per wave) and 8 groups of 16 rows at d = 64 (one per wave);
 //  - S^T = K_t Q^T: per 32-key block, d/64 fp8 products whose K fragment is
 //    two 16-byte row reads;
 //  - O^T += V_t^T P^T: one fp8 product per 32 d-columns and 64 keys.
@@ -380,7 +187,6 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
     using KT = typename Cfg::KT;
     constexpr int NW = Cfg::kWaves, BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::kStages, KB = BN / 32;
     constexpr int kStage = Cfg::kStage, SUB = Cfg::kSub, PW = KT::kPerWave;
-    static_assert(D == 128, "the ping-pong fp8 kernel is for d = 128");
     static_assert((NS & (NS - 1)) == 0, "stage index by mask");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * kStage];
 
@@ -712,14 +518,14 @@ __global__ __launch_bounds__(FwdFp8Cfg<D>::kThreads, 2) void fwd_fp8_pp_kernel(
     }
 }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 static hipError_t launch_fp8_pp(const void* q, const void* k, const void* v, void* o, float* lse,
                                 const float* descale, int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
-    using Cfg = FwdFp8Cfg<128>;
+    using Cfg = FwdFp8Cfg<D>;
     const int nmb = (N + Cfg::BM - 1) / Cfg::BM;
     static PerDevice slots;
-    const int grid = persistent_grid((const void*)fwd_fp8_pp_kernel<128, CAUSAL>, Cfg::kThreads, nmb * Hq * B, slots);
-    hipLaunchKernelGGL((fwd_fp8_pp_kernel<128, CAUSAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
+    const int grid = persistent_grid((const void*)fwd_fp8_pp_kernel<D, CAUSAL>, Cfg::kThreads, nmb * Hq * B, slots);
+    hipLaunchKernelGGL((fwd_fp8_pp_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(Cfg::kThreads), 0, st,
                        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, (uint16_t*)o, lse, descale, B, Hq,
                        Hkv, N, scale);
     return hipGetLastError();
@@ -727,25 +533,10 @@ static hipError_t launch_fp8_pp(const void* q, const void* k, const void* v, voi
 
 hipError_t launch_fwd_fp8(int d, int causal, const void* q, const void* k, const void* v, void* o, float* lse,
                           const float* descale, int B, int Hq, int Hkv, int N, float scale, hipStream_t st) {
-    if (d == 128) return causal ? launch_fp8_pp<true>(q, k, v, o, lse, descale, B, Hq, Hkv, N, scale, st)
-                                : launch_fp8_pp<false>(q, k, v, o, lse, descale, B, Hq, Hkv, N, scale, st);
-    // d = 64: a row group of a 64-key tile is 16 rows of 64 bytes, fewer
-    // groups than the eight waves of the ping-pong kernel; the four-wave
-    // kernel above handles it
-    const int nmb = (N + 127) / 128;
-    const dim3 grid((unsigned)((int64_t)nmb * Hq * B)), block(256);
-#define FA_FP8_CASE(DD)                                                                                 \
-    if (d == DD) {                                                                                      \
-        if (causal)                                                                                     \
-            hipLaunchKernelGGL((fwd_fp8_kernel<DD, true>), grid, block, 0, st, (const uint8_t*)q,        \
-                               (const uint8_t*)k, (const uint8_t*)v, (uint16_t*)o, lse, descale, Hq, Hkv, N, scale); \
-        else                                                                                            \
-            hipLaunchKernelGGL((fwd_fp8_kernel<DD, false>), grid, block, 0, st, (const uint8_t*)q,       \
-                               (const uint8_t*)k, (const uint8_t*)v, (uint16_t*)o, lse, descale, Hq, Hkv, N, scale); \
-        return hipGetLastError();                                                                       \
-    }
-    FA_FP8_CASE(64)
-#undef FA_FP8_CASE
+    if (d == 128) return causal ? launch_fp8_pp<128, true>(q, k, v, o, lse, descale, B, Hq, Hkv, N, scale, st)
+                                : launch_fp8_pp<128, false>(q, k, v, o, lse, descale, B, Hq, Hkv, N, scale, st);
+    if (d == 64) return causal ? launch_fp8_pp<64, true>(q, k, v, o, lse, descale, B, Hq, Hkv, N, scale, st)
+                               : launch_fp8_pp<64, false>(q, k, v, o, lse, descale, B, Hq, Hkv, N, scale, st);
     return hipErrorInvalidValue;
 }
 

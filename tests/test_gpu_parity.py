@@ -245,7 +245,7 @@ def fp8_forward_check(fa, dev, q, k, v, causal, scale, rows_by_head, tag):
 
 
 @pytest.mark.parametrize("N,d,causal", [(200, 64, True), (257, 128, False), (1024, 128, True), (1000, 128, False),
-                                           (777, 128, True)])
+                                           (777, 128, True), (1000, 64, False), (333, 64, True), (50, 64, False)])
 def test_fp8_forward_small(fa, dev, N, d, causal):
     B, Hq, Hkv = 1, 4, 2
     q = I.random_tensor(7, (B, Hq, N, d), "bf16", tensor_id=0)
