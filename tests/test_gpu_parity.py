@@ -263,6 +263,15 @@ def test_fp8_forward_gqa_n16384_workload(fa, dev):
     fp8_forward_check(fa, dev, q, k, v, w.causal, w.scale, [(bh, rows) for bh in I.sample_heads(w)], w.name)
 
 
+@pytest.mark.timeout(300)
+def test_fp8_forward_mha_n1024_workload(fa, dev):
+    """The d = 64 fp8 forward at the 1024-token workload's shape: every row of the sampled heads."""
+    w = I.WORKLOADS["mha_bf16_n1024"]
+    q, k, v = (I.full_tensor(w, t) for t in range(3))
+    rows = np.arange(w.N)
+    fp8_forward_check(fa, dev, q, k, v, w.causal, w.scale, [(bh, rows) for bh in I.sample_heads(w)], w.name)
+
+
 # ---------------------------------------------------------------- properties at full size
 
 def test_identical_keys_closed_form_full_size(fa, dev):
